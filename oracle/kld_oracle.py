@@ -1,0 +1,313 @@
+"""Plain f64 CPU oracle for full-vocabulary KL scoring.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import this
+module: only the test suite, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the
+HIP library (no kernels, headers, helpers or constants) and it imports
+nothing from the ``full_vocab_kl_amd`` package.
+
+Every function is the plain definition of one quantity, written in numpy
+float64 with no blocking, fusion or reordering beyond what the definition
+states.  Sources are cited by page title and section:
+
+* [QC]  "Qwen3.8-27B Quantization Challenge" (dataset card):
+        sections "How the references were made", "Golden distributions",
+        "The score", "Scoring an entry yourself".
+* [FS]  "Qwen3.8-27B fidelity suite v5 -- evaluation inputs, the BF16
+        reference, and every per-shard report": opening paragraphs (the
+        metric definition through one shared BF16 LM head) and "What is in
+        here" (hidden-state shapes).
+* [QE]  "Qwopus3.8-27B-Coder-Flash: quality-eval reference": sections
+        "Files" (top-64 export layout) and "Method" (top-64 + tail bucket
+        KLD, top-1, perplexity).
+* [IQ]  "Qwen3.8-27B IQ8R (GPTQ int8, Hadamard-rotated)": section
+        "Quality" (mean / 99 % / 99.9 % KLD, top-1).
+
+Readings where the pages are silent (each also listed in the design notes):
+
+* R1  ties in argmax and top-k are broken toward the lower vocabulary id.
+* R2  percentiles use linear interpolation between order statistics
+      (Hyndman-Fan type 7).
+* R3  in the top-64 + tail rule the candidate's tail cell is the complement
+      1 - sum over the reference ids of the candidate's per-id estimates.
+* R4  the reference tail mass p_T comes from the exported fp16 top-64
+      log-probs (the export stores no tail mass).
+* R5  fused-path logits are not rounded to bf16: products of the bf16
+      operands are summed exactly (f64 here) and the softmax is taken on
+      those sums.
+* R6  a finite reference logit against a -inf candidate logit makes KL
+      +inf; a reference logit of -inf contributes nothing; a row whose
+      reference or candidate logits are all -inf, or that holds a NaN or
+      +inf, has KL = NaN.
+* R7  NLL of a target id outside [0, V) is NaN.
+
+Parity is pinned for every function here by the ``-m "not gpu"`` tests
+(tests/test_oracle_pins.py); no function is "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+TOPK = 64
+
+# --------------------------------------------------------------------------
+# exact decoding of the storage formats
+# --------------------------------------------------------------------------
+
+
+def bf16_bits_to_f64(u16: np.ndarray) -> np.ndarray:
+    """Decode bfloat16 bit patterns exactly: a bf16 value is the upper half of
+    an IEEE binary32, so shifting its 16 bits left by 16 gives that binary32,
+    which widens to binary64 without rounding."""
+    u16 = np.asarray(u16, dtype=np.uint16)
+    return (u16.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def fp16_bits_to_f64(u16: np.ndarray) -> np.ndarray:
+    """Decode IEEE binary16 bit patterns exactly (binary16 widens exactly)."""
+    return np.asarray(u16, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def f64_to_fp16_bits(x: np.ndarray) -> np.ndarray:
+    """Round binary64 to binary16, round-to-nearest-even, and return the bits.
+
+    numpy converts double to half directly (one rounding, ties to even),
+    which the pins check on hand-built halfway cases."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+# --------------------------------------------------------------------------
+# per-row definitions
+# --------------------------------------------------------------------------
+
+
+def _row_is_bad(x: np.ndarray) -> bool:
+    return bool(np.isnan(x).any() or np.isposinf(x).any() or not np.isfinite(x).any())
+
+
+def logsumexp(x: np.ndarray) -> float:
+    """O1: lse(x) = m + ln sum_j exp(x_j - m), m = max_j x_j.
+
+    [QC] "How the references were made": each position's distribution over
+    the full vocabulary, in natural-log units; the log-softmax of a row is
+    x - lse(x) ([QC] "Scoring an entry yourself")."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.isnan(x).any() or np.isposinf(x).any():
+        return float("nan")
+    m = x.max()
+    if m == -np.inf:
+        return -math.inf
+    return float(m + np.log(np.sum(np.exp(x - m))))
+
+
+def kl_row(a: np.ndarray, b: np.ndarray) -> float:
+    """O2: KL(p || q) = sum_j p_j (ln p_j - ln q_j), p = softmax(a) (reference),
+    q = softmax(b) (candidate), summed over every vocabulary id.
+
+    [FS] opening paragraph: the metric is KL(BF16 || candidate); [QC] "The
+    score": the sum over cells of p_i (log p_i - log q_i), here with every
+    vocabulary id as its own cell; [QE] "Method": KL(BF16 || quant) per
+    position.  Edge cases follow reading R6."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    if _row_is_bad(a) or _row_is_bad(b):
+        return float("nan")
+    lse_a = logsumexp(a)
+    lse_b = logsumexp(b)
+    support = a > -np.inf                      # p_j > 0 exactly where a_j is finite
+    if np.any(support & (b == -np.inf)):       # p_j > 0 and q_j = 0
+        return math.inf
+    la = a[support] - lse_a
+    lb = b[support] - lse_b
+    p = np.exp(la)
+    return float(np.sum(p * (la - lb)))
+
+
+def argmax_row(x: np.ndarray) -> int:
+    """O3: the smallest id j with x_j equal to the row maximum (reading R1).
+
+    [QE] "Method": top-1 agreement is an exact argmax match; [QC] "The
+    score": the leaderboard's top-1 agreement (argmax match)."""
+    x = np.asarray(x, dtype=np.float64)
+    m = x.max()
+    return int(np.flatnonzero(x == m)[0])
+
+
+def nll_row(x: np.ndarray, target: int) -> float:
+    """O4: NLL of the true next token = lse(x) - x_target (reading R7 for ids
+    outside the vocabulary).
+
+    [QE] "Method": perplexity is exp(mean NLL) of the true next token;
+    [QE] "Files": the stored target log-prob of the true next token;
+    [QC] "Golden distributions": the reference's NLL of the true next token."""
+    x = np.asarray(x, dtype=np.float64)
+    if target < 0 or target >= x.shape[0]:
+        return float("nan")
+    return float(logsumexp(x) - x[target])
+
+
+def topk_row(x: np.ndarray, k: int = TOPK):
+    """O6: the k most likely ids, most likely first, ties to the lower id
+    (reading R1), with log-probs x_j - lse(x) rounded to fp16 (nearest-even).
+
+    [QE] "Files": top-64 ids int32 and log-probs float16, sorted; [QC]
+    "Golden distributions": the most likely tokens, most likely first.
+    Returns (ids int32 [k], lp fp16 bits uint16 [k], lp f64 [k] unrounded)."""
+    x = np.asarray(x, dtype=np.float64)
+    ids = np.arange(x.shape[0])
+    order = np.lexsort((ids, -x))              # primary key -x, then id ascending
+    top = order[:k]
+    lp = x[top] - logsumexp(x)
+    return top.astype(np.int32), f64_to_fp16_bits(lp), lp
+
+
+def tail_kld_probs(ids_p, p, ids_q, q, v: int) -> float:
+    """O7: top-K + one-tail-bucket KLD of the quality-eval reference, on
+    probabilities.
+
+    [QE] "Method": the divergence is taken over 65 cells -- the reference's
+    64 listed ids and one cell for all other ids.  When a reference id is
+    absent from the candidate's list, its candidate probability is an equal
+    share of the mass the candidate's list leaves over, divided among the
+    ids that list does not name.  With K = len(ids_q) (the candidate list
+    length):
+
+      1. p_i for i in P; p_T = max(0, 1 - sum_P p_i)                  (R4)
+      2. r = max(0, 1 - sum_{j in Q} q_j); u = r / (V - K)
+      3. qhat_i = q_i if i in Q else u
+      4. qhat_T = max(0, 1 - sum_{i in P} qhat_i)                     (R3)
+      5. KL = sum_{i in P} p_i ln(p_i/qhat_i) + p_T ln(p_T/qhat_T),
+         with 0 ln(0/x) = 0 and p ln(p/0) = +inf for p > 0.
+    """
+    ids_p = np.asarray(ids_p, dtype=np.int64)
+    ids_q = np.asarray(ids_q, dtype=np.int64)
+    p = np.asarray(p, dtype=np.float64)
+    qv = np.asarray(q, dtype=np.float64)
+    k = ids_q.shape[0]
+    p_tail = max(0.0, 1.0 - float(np.sum(p)))
+    r = max(0.0, 1.0 - float(np.sum(qv)))
+    u = r / (v - k) if v > k else 0.0
+    q_of = {int(j): float(qj) for j, qj in zip(ids_q, qv)}
+    qhat = np.array([q_of.get(int(i), u) for i in ids_p], dtype=np.float64)
+    q_tail = max(0.0, 1.0 - float(np.sum(qhat)))
+    total = 0.0
+    for pi, qi in zip(np.append(p, p_tail), np.append(qhat, q_tail)):
+        if pi == 0.0:
+            continue
+        if qi == 0.0:
+            return math.inf
+        total += pi * math.log(pi / qi)
+    return total
+
+
+def tail_kld_row(ids_p, lp_p_bits, ids_q, lp_q_bits, v: int) -> float:
+    """O7 on the export format: fp16 log-prob bits are decoded exactly and
+    exponentiated in f64 ([QE] "Files": top-64 ids int32 and log-probs
+    float16), then :func:`tail_kld_probs`."""
+    p = np.exp(fp16_bits_to_f64(lp_p_bits))
+    q = np.exp(fp16_bits_to_f64(lp_q_bits))
+    return tail_kld_probs(ids_p, p, ids_q, q, v)
+
+
+# --------------------------------------------------------------------------
+# fused head: logits from hidden states through one shared head
+# --------------------------------------------------------------------------
+
+
+def head_logits(w_bits: np.ndarray, h_bits: np.ndarray, v_chunk: int = 8192) -> np.ndarray:
+    """O8: z[i, j] = sum_k W[j, k] h[i, k] in f64 from bf16-decoded operands.
+
+    [FS] opening paragraph: both sides' logits are produced by applying one
+    and the same bf16 output head to each side's final hidden states; "What
+    is in here": hidden states are [positions, 5120] bf16.  Reading R5: the sums are
+    not rounded to bf16.  Each product of two bf16 values is exact in f64;
+    the matmul routine sums them in f64.  Returns f64 [n, V]; the head is
+    decoded ``v_chunk`` rows at a time only to bound memory."""
+    w_bits = np.asarray(w_bits, dtype=np.uint16)
+    h = bf16_bits_to_f64(h_bits)
+    n, v = h.shape[0], w_bits.shape[0]
+    out = np.empty((n, v), dtype=np.float64)
+    for j0 in range(0, v, v_chunk):
+        wj = bf16_bits_to_f64(w_bits[j0:j0 + v_chunk])
+        out[:, j0:j0 + v_chunk] = h @ wj.T
+    return out
+
+
+# --------------------------------------------------------------------------
+# whole-row scoring and aggregation
+# --------------------------------------------------------------------------
+
+
+def score_rows(a: np.ndarray, b: np.ndarray, target=None, k: int | None = None) -> dict:
+    """Per-position scores for logit rows a (reference) and b (candidate),
+    each [n, V] (any float dtype; promoted to f64).
+
+    Returns kl, lse_ref, lse_cand, argmax_ref, argmax_cand, nll_ref,
+    nll_cand (NaN where no target is given), and with k: top-k ids / fp16
+    lp bits per side."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    n = a.shape[0]
+    out = {
+        "kl": np.empty(n), "lse_ref": np.empty(n), "lse_cand": np.empty(n),
+        "argmax_ref": np.empty(n, np.int64), "argmax_cand": np.empty(n, np.int64),
+        "nll_ref": np.full(n, np.nan), "nll_cand": np.full(n, np.nan),
+    }
+    if k is not None:
+        for s in ("ref", "cand"):
+            out[f"ids_{s}"] = np.empty((n, k), np.int32)
+            out[f"lp_{s}"] = np.empty((n, k), np.uint16)
+    for i in range(n):
+        out["kl"][i] = kl_row(a[i], b[i])
+        out["lse_ref"][i] = logsumexp(a[i])
+        out["lse_cand"][i] = logsumexp(b[i])
+        out["argmax_ref"][i] = argmax_row(a[i])
+        out["argmax_cand"][i] = argmax_row(b[i])
+        if target is not None:
+            out["nll_ref"][i] = nll_row(a[i], int(target[i]))
+            out["nll_cand"][i] = nll_row(b[i], int(target[i]))
+        if k is not None:
+            for s, x in (("ref", a[i]), ("cand", b[i])):
+                ids, lp, _ = topk_row(x, k)
+                out[f"ids_{s}"][i] = ids
+                out[f"lp_{s}"][i] = lp
+    return out
+
+
+def percentile(x: np.ndarray, q: float) -> float:
+    """O5 percentile by reading R2 (linear interpolation, type 7): sort
+    ascending, h = q (N - 1), value = x_(floor h) + (h - floor h) *
+    (x_(floor h + 1) - x_(floor h)).
+
+    [QC] "The score": the leaderboard shows the median, p99 and p99.9 KL;
+    [IQ] "Quality": KLD 99 % and 99.9 %; [QE] "v1.0 at a glance": median
+    and p99."""
+    xs = np.sort(np.asarray(x, dtype=np.float64))
+    n = xs.shape[0]
+    h = q * (n - 1)
+    lo = int(math.floor(h))
+    hi = min(lo + 1, n - 1)
+    return float(xs[lo] + (h - lo) * (xs[hi] - xs[lo]))
+
+
+def summarize(kl, argmax_ref=None, argmax_cand=None, nll_ref=None, nll_cand=None,
+              quantiles=(0.5, 0.99, 0.999)) -> dict:
+    """Aggregate per-position scores, every position weighted equally.
+
+    [QC] "The score": mean KL over all positions ranks entries, with median,
+    p99, p99.9, top-1 agreement and the perplexity ratio; [QE] "Method":
+    perplexity = exp(mean NLL) of the true next token."""
+    kl = np.asarray(kl, dtype=np.float64)
+    n = kl.shape[0]
+    res = {"n": n, "mean_kl": float(np.sum(kl) / n)}
+    if argmax_ref is not None and argmax_cand is not None:
+        res["top1"] = float(np.sum(np.asarray(argmax_ref) == np.asarray(argmax_cand)) / n)
+    if nll_ref is not None and nll_cand is not None:
+        mr = float(np.sum(np.asarray(nll_ref, np.float64)) / n)
+        mc = float(np.sum(np.asarray(nll_cand, np.float64)) / n)
+        res.update(mean_nll_ref=mr, mean_nll_cand=mc, ppl_ref=math.exp(mr),
+                   ppl_cand=math.exp(mc), ppl_ratio=math.exp(mc) / math.exp(mr))
+    res["quantiles"] = {float(q): percentile(kl, q) for q in quantiles}
+    return res

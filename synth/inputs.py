@@ -1,0 +1,157 @@
+"""Seeded, row-addressable synthetic inputs.
+
+Every row r of stream k for workload c is drawn from
+``numpy.random.default_rng(SeedSequence([BASE_SEED, c, k, r]))`` so any
+subset of rows can be regenerated on its own.  The head weight is drawn in
+blocks of ``HEAD_BLOCK`` vocabulary rows (block b uses index b).  Rounding
+to bf16 is round-to-nearest-even from float32.
+
+The shapes follow the pages' workloads: a 248,320-id vocabulary, hidden
+width 5120, windows of 2048 tokens with 2047 scored positions, a 2.54 GB
+bf16 head.  The value recipes (logit scale, boosted id, noise widths) are
+this project's synthetic stand-ins for the models and corpora, which are
+not available.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+BASE_SEED = 20261203
+VOCAB = 248_320
+HIDDEN = 5120
+WINDOW_POSITIONS = 2047
+
+STREAM_BASE, STREAM_NOISE, STREAM_BOOST, STREAM_TARGET, STREAM_HEAD, STREAM_SUBSET = range(6)
+HEAD_BLOCK = 2048
+
+# workload ids used as the second seed word
+LOGITS_F32, FUSED_WINDOW, LOGITS_BF16_TOPK, FUSED_BATCH, LONG_TRACE = range(5)
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def rng(workload: int, stream: int, index: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([BASE_SEED, workload, stream, index]))
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.reshape(-1).view(np.uint32)
+    hi = u.view(np.uint16)[1::2]                  # upper halves (little-endian)
+    bias = (hi & np.uint16(1)).astype(np.uint32) + np.uint32(0x7FFF)
+    r = u + bias                                  # finite inputs: no wrap-around
+    return r.view(np.uint16)[1::2].reshape(x.shape).copy()
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _pmap(fn, items):
+    items = list(items)
+    if len(items) <= 1:
+        return [fn(i) for i in items]
+    with ThreadPoolExecutor(_threads()) as ex:
+        return list(ex.map(fn, items))
+
+
+# --------------------------------------------------------------------------
+# logits rows
+# --------------------------------------------------------------------------
+
+def logit_row_pair(workload: int, r: int, v: int, scale: float = 3.0, boost: float = 12.0,
+                   noise: float = 0.03):
+    """Reference row a = scale * N(0,1) with +boost on one uniformly drawn id;
+    candidate row b = a + N(0, noise^2); both float32."""
+    a = rng(workload, STREAM_BASE, r).standard_normal(v, dtype=np.float32)
+    a *= np.float32(scale)
+    j = int(rng(workload, STREAM_BOOST, r).integers(0, v))
+    a[j] += np.float32(boost)
+    b = a + np.float32(noise) * rng(workload, STREAM_NOISE, r).standard_normal(v, dtype=np.float32)
+    return a, b.astype(np.float32)
+
+
+def logit_rows(workload: int, rows, v: int, dtype: str = "f32", **kw):
+    """Rows ``rows`` of the logits workload.  dtype 'f32' returns float32
+    arrays; 'bf16' returns uint16 bit arrays (a and b rounded separately)."""
+    rows = list(rows)
+    a = np.empty((len(rows), v), np.float32 if dtype == "f32" else np.uint16)
+    b = np.empty_like(a)
+
+    def one(i):
+        ra, rb = logit_row_pair(workload, rows[i], v, **kw)
+        if dtype == "f32":
+            a[i], b[i] = ra, rb
+        else:
+            a[i], b[i] = f32_to_bf16_bits(ra), f32_to_bf16_bits(rb)
+    _pmap(one, range(len(rows)))
+    return a, b
+
+
+def targets(workload: int, rows, v: int) -> np.ndarray:
+    """True next-token ids, uniform over [0, v), one seeded draw per row."""
+    return np.array([int(rng(workload, STREAM_TARGET, r).integers(0, v)) for r in rows], np.int32)
+
+
+# --------------------------------------------------------------------------
+# fused head inputs
+# --------------------------------------------------------------------------
+
+def head_weight(workload: int, v: int, d: int, std: float = 0.02) -> np.ndarray:
+    """Shared head W [v, d] as bf16 bits, W ~ N(0, std^2)."""
+    w = np.empty((v, d), np.uint16)
+
+    def one(blk):
+        j0 = blk * HEAD_BLOCK
+        j1 = min(v, j0 + HEAD_BLOCK)
+        z = rng(workload, STREAM_HEAD, blk).standard_normal((j1 - j0, d), dtype=np.float32)
+        z *= np.float32(std)
+        w[j0:j1] = f32_to_bf16_bits(z)
+    _pmap(one, range((v + HEAD_BLOCK - 1) // HEAD_BLOCK))
+    return w
+
+
+def hidden_row_pair(workload: int, r: int, d: int, noise: float):
+    """h = N(0,1) row scaled to unit RMS (float32); reference = bf16(h),
+    candidate = bf16(h + N(0, noise^2))."""
+    z = rng(workload, STREAM_BASE, r).standard_normal(d, dtype=np.float32)
+    rms = np.float32(np.sqrt(np.mean(z.astype(np.float64) ** 2)))
+    h = (z / rms).astype(np.float32)
+    hc = h + np.float32(noise) * rng(workload, STREAM_NOISE, r).standard_normal(d, dtype=np.float32)
+    return f32_to_bf16_bits(h), f32_to_bf16_bits(hc.astype(np.float32))
+
+
+def hidden_rows(workload: int, rows, d: int, noise) -> tuple:
+    """Hidden-state rows; ``noise`` is a float or a callable row -> std."""
+    rows = list(rows)
+    hr = np.empty((len(rows), d), np.uint16)
+    hc = np.empty_like(hr)
+
+    def one(i):
+        s = noise(rows[i]) if callable(noise) else noise
+        hr[i], hc[i] = hidden_row_pair(workload, rows[i], d, s)
+    _pmap(one, range(len(rows)))
+    return hr, hc
+
+
+def long_trace_noise(row: int, chunk_rows: int = 8192, n_chunks: int = 32) -> float:
+    """Candidate noise for the long-trace workload: linear sweep over chunks,
+    0.005 for the first chunk up to 0.05 for the last."""
+    c = min(row // chunk_rows, n_chunks - 1)
+    return 0.005 + c * (0.045 / (n_chunks - 1))
+
+
+def subset(workload: int, n: int, m: int) -> np.ndarray:
+    """A seeded sorted subset of m distinct row indices out of n."""
+    g = rng(workload, STREAM_SUBSET, 0)
+    return np.sort(g.choice(n, size=min(m, n), replace=False)).astype(np.int64)
