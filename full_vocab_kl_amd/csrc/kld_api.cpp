@@ -1,0 +1,165 @@
+// C ABI of libkld: argument validation (fail-closed, before any launch),
+// workspace layout and kernel dispatch.  See include/kld.h for the contract.
+#include "kld.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+
+#include "kld_device.hpp"
+#include "kld_launch.hpp"
+
+using namespace kld;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Workspace carving: a bump allocator over the caller's buffer.
+struct Carver {
+  char *base;
+  size_t used = 0;
+  explicit Carver(void *b) : base((char *)b) {}
+  template <typename T> T *take(size_t count) {
+    used = round_up(used, kAlign);
+    T *p = base ? (T *)(base + used) : nullptr;
+    used += count * sizeof(T);
+    return p;
+  }
+};
+
+// ---- logits path geometry --------------------------------------------------
+// Splits per row so that the grid holds about 4096 blocks (16 per CU), each
+// streaming at least 4096 ids; chunk is a multiple of 8 ids so that 16-byte
+// vectors never straddle a split for either dtype.
+struct LogitsGeom {
+  int splits;
+  int64_t chunk;
+};
+
+LogitsGeom logits_geom(int64_t n, int64_t v) {
+  int64_t want = n > 0 ? (4096 + n - 1) / n : 1;
+  int64_t max_splits = (v + 4095) / 4096;
+  if (max_splits < 1) max_splits = 1;
+  if (want > max_splits) want = max_splits;
+  if (want < 1) want = 1;
+  int64_t chunk = (v + want - 1) / want;
+  chunk = (chunk + 7) / 8 * 8;
+  LogitsGeom g;
+  g.chunk = chunk;
+  g.splits = (int)((v + chunk - 1) / chunk);
+  return g;
+}
+
+size_t logits_workspace(int64_t n, int64_t v, int flags, Carver *c) {
+  (void)flags;
+  LogitsGeom g = logits_geom(n, v);
+  c->take<RowState>((size_t)n * g.splits);
+  return round_up(c->used, kAlign);
+}
+
+inline hipStream_t as_stream(void *s) { return (hipStream_t)s; }
+
+}  // namespace
+
+extern "C" {
+
+const char *kld_status_str(int s) {
+  switch (s) {
+    case KLD_OK: return "KLD_OK";
+    case KLD_EINVAL: return "KLD_EINVAL: null pointer or negative count";
+    case KLD_ESHAPE: return "KLD_ESHAPE: inconsistent sizes";
+    case KLD_EDTYPE: return "KLD_EDTYPE: unknown dtype";
+    case KLD_EWORKSPACE: return "KLD_EWORKSPACE: workspace missing or too small";
+    case KLD_EUNSUPPORTED: return "KLD_EUNSUPPORTED: request not served by this build";
+    case KLD_EHIP: return "KLD_EHIP: HIP runtime error";
+    default: return "KLD_UNKNOWN";
+  }
+}
+
+int kld_abi_version(void) { return KLD_ABI_VERSION; }
+
+size_t kld_workspace_size(int op, int64_t n, int64_t v, int64_t d, int flags) {
+  if (n < 0 || v < 0 || d < 0) return 0;
+  Carver c(nullptr);
+  switch (op) {
+    case KLD_OP_FROM_LOGITS: return logits_workspace(n, v, flags, &c);
+    default: return 0;
+  }
+}
+
+kld_status kld_from_logits(const void *ref, const void *cand, int dtype, int64_t n, int64_t v,
+                           int64_t ld_ref, int64_t ld_cand, const int32_t *target,
+                           const kld_rows *out, const kld_topk *topk, void *ws, size_t ws_bytes,
+                           void *stream) {
+  if (dtype != KLD_F32 && dtype != KLD_BF16) return KLD_EDTYPE;
+  if (n < 0 || v < 0) return KLD_EINVAL;
+  if (!out) return KLD_EINVAL;
+  if (n == 0) return KLD_OK;
+  if (v < 1 || v > 0x7fffffffLL) return KLD_ESHAPE;
+  if (!ref || !cand || !out->kl) return KLD_EINVAL;
+  if (ld_ref < v || ld_cand < v) return KLD_ESHAPE;
+  if ((out->nll_ref || out->nll_cand) && !target) return KLD_EINVAL;
+  if (topk) {
+    if (v < KLD_TOPK) return KLD_ESHAPE;
+    return KLD_EUNSUPPORTED;
+  }
+  const size_t need = kld_workspace_size(KLD_OP_FROM_LOGITS, n, v, 0, topk ? KLD_FLAG_TOPK : 0);
+  if (!ws || ws_bytes < need) return KLD_EWORKSPACE;
+
+  const size_t esize = dtype == KLD_F32 ? 4 : 2;
+  LogitsGeom g = logits_geom(n, v);
+  LogitsArgs a;
+  a.ref = ref; a.cand = cand; a.dtype = dtype; a.n = n; a.v = v;
+  a.ld_ref = ld_ref; a.ld_cand = ld_cand; a.chunk = g.chunk; a.splits = g.splits;
+  a.aligned = aligned16(ref) && aligned16(cand) && (ld_ref * esize) % 16 == 0 &&
+              (ld_cand * esize) % 16 == 0;
+  a.target = target;
+  a.out = RowsOut{out->kl, out->nll_ref, out->nll_cand, out->lse_ref, out->lse_cand,
+                  out->argmax_ref, out->argmax_cand};
+  a.stream = as_stream(stream);
+
+  Carver c(ws);
+  RowState *part = c.take<RowState>((size_t)n * g.splits);
+  if (launch_logits_state(a, part) != hipSuccess) return KLD_EHIP;
+  if (launch_logits_finalize(a, part) != hipSuccess) return KLD_EHIP;
+  return KLD_OK;
+}
+
+kld_status kld_fused_head(const uint16_t *W, int64_t v, int64_t d, const uint16_t *h_ref,
+                          const uint16_t *h_cand, int64_t n, const int32_t *target,
+                          const kld_rows *out, const kld_topk *topk, void *ws, size_t ws_bytes,
+                          void *stream) {
+  (void)W; (void)v; (void)d; (void)h_ref; (void)h_cand; (void)n; (void)target; (void)out;
+  (void)topk; (void)ws; (void)ws_bytes; (void)stream;
+  return KLD_EUNSUPPORTED;
+}
+
+kld_status topk_export(const void *logits, int dtype, int64_t n, int64_t v, int64_t ld, int k,
+                       int32_t *ids, uint16_t *lp, const int32_t *target, float *target_lp,
+                       void *ws, size_t ws_bytes, void *stream) {
+  (void)logits; (void)dtype; (void)n; (void)v; (void)ld; (void)k; (void)ids; (void)lp;
+  (void)target; (void)target_lp; (void)ws; (void)ws_bytes; (void)stream;
+  return KLD_EUNSUPPORTED;
+}
+
+kld_status kld_topk_tail(const int32_t *ids_p, const uint16_t *lp_p, const int32_t *ids_q,
+                         const uint16_t *lp_q, int64_t n, int k, int64_t v, float *kl_tail,
+                         void *stream) {
+  (void)ids_p; (void)lp_p; (void)ids_q; (void)lp_q; (void)n; (void)k; (void)v; (void)kl_tail;
+  (void)stream;
+  return KLD_EUNSUPPORTED;
+}
+
+kld_status kld_summary(const float *kl, const int32_t *argmax_ref, const int32_t *argmax_cand,
+                       const float *nll_ref, const float *nll_cand, int64_t n,
+                       const double *quantiles, int nq, double *out, void *ws, size_t ws_bytes,
+                       void *stream) {
+  (void)kl; (void)argmax_ref; (void)argmax_cand; (void)nll_ref; (void)nll_cand; (void)n;
+  (void)quantiles; (void)nq; (void)out; (void)ws; (void)ws_bytes; (void)stream;
+  return KLD_EUNSUPPORTED;
+}
+
+}  // extern "C"

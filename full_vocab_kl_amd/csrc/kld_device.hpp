@@ -1,0 +1,150 @@
+// Device-side building blocks shared by the libkld kernels (gfx950, wave64).
+//
+// Online per-row state for KL(p || q) over a vocabulary ("Qwen3.8-27B
+// fidelity suite v5", opening paragraphs: the metric KL(BF16 || candidate);
+// "Qwen3.8-27B Quantization Challenge", "How the references were made":
+// f32 distributions over the full vocabulary).
+//
+// For a reference row a and candidate row b the state keeps, over the ids
+// seen so far, the maxima ma, mb and, with offsets ra = ref(ma), rb = ref(mb)
+// (ref(m) = m, or 0 while the side has seen only -inf):
+//   sa = sum_j 2^((a_j - ra) L2E),  sb = sum_j 2^((b_j - rb) L2E),
+//   t  = sum_j 2^((a_j - ra) L2E) ((a_j - ra) - (b_j - rb)).
+// Then lse_a = ra + ln sa, lse_b = rb + ln sb and, exactly,
+//   KL = t/sa + ln(sb/sa)
+// (sum_j p_j (a_j - b_j) = t/sa + ra - rb, and the offsets cancel).  Taking
+// every difference against the running maxima keeps t exact to f32 rounding
+// of O(1) numbers even when the two rows carry large opposite offsets.  When
+// a maximum moves by D the sums are rescaled by 2^(-D L2E) and t is rebased
+// by sa * D (reference side: t -= sa D before the rescale; candidate side:
+// t += sa D).  The argmax of each side is the running maximum plus its lowest
+// id.  Partial states over disjoint id ranges merge associatively; merging in
+// a fixed order keeps results bitwise reproducible.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kld {
+
+constexpr float kL2E = 1.4426950408889634f;   // log2(e) rounded to f32
+constexpr double kLn2 = 0.69314718055994530942;
+constexpr int kNoId = 0x7fffffff;
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kFltMax = 3.402823466e38f;
+
+struct RowState {
+  float ma, sa, t, mb, sb;
+  int ia, ib;
+};
+
+__host__ __device__ inline RowState empty_state() {
+  RowState s;
+  s.ma = kNegInf; s.sa = 0.f; s.t = 0.f; s.mb = kNegInf; s.sb = 0.f;
+  s.ia = kNoId; s.ib = kNoId;
+  return s;
+}
+
+// Offset a side's differences are taken against: its maximum, or 0 while it
+// has seen only -inf (so that -inf elements give 2^-inf = 0, never NaN).
+__device__ __forceinline__ float ref_of(float m) { return m == kNegInf ? 0.f : m; }
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Factor that moves a sum taken against offset ref(m_old) to ref(m_new).
+__device__ __forceinline__ float rescale(float m_old, float m_new) {
+  return m_old == kNegInf ? 0.f : exp2_fast((m_old - ref_of(m_new)) * kL2E);
+}
+
+__device__ __forceinline__ bool beats(float v1, int i1, float v2, int i2) {
+  return v1 > v2 || (v1 == v2 && i1 < i2);
+}
+
+// Bring state x to the offsets of maxima (ma, mb) >= x's own.
+__device__ __forceinline__ void rebase(const RowState &x, float ma, float mb, float &sa, float &t,
+                                       float &sb) {
+  const float fa = rescale(x.ma, ma), fb = rescale(x.mb, mb);
+  const float da = ref_of(ma) - ref_of(x.ma), db = ref_of(mb) - ref_of(x.mb);
+  // x.sa == 0 means x saw no finite reference id: nothing to rebase
+  const float tt = x.sa == 0.f ? x.t : fmaf(x.sa, db - da, x.t);
+  sa = x.sa * fa;
+  t = tt * fa;
+  sb = x.sb * fb;
+}
+
+// Associative merge of two partial states over disjoint id ranges.
+__device__ inline RowState merge(const RowState &x, const RowState &y) {
+  RowState r;
+  r.ma = fmaxf(x.ma, y.ma);
+  r.mb = fmaxf(x.mb, y.mb);
+  float xs, xt, xb, ys, yt, yb;
+  rebase(x, r.ma, r.mb, xs, xt, xb);
+  rebase(y, r.ma, r.mb, ys, yt, yb);
+  r.sa = xs + ys;
+  r.t = xt + yt;
+  r.sb = xb + yb;
+  r.ia = beats(x.ma, x.ia, y.ma, y.ia) ? x.ia : y.ia;
+  r.ib = beats(x.mb, x.ib, y.mb, y.ib) ? x.ib : y.ib;
+  return r;
+}
+
+__device__ __forceinline__ RowState shfl_xor_state(const RowState &s, int mask) {
+  RowState o;
+  o.ma = __shfl_xor(s.ma, mask); o.sa = __shfl_xor(s.sa, mask); o.t = __shfl_xor(s.t, mask);
+  o.mb = __shfl_xor(s.mb, mask); o.sb = __shfl_xor(s.sb, mask);
+  o.ia = __shfl_xor(s.ia, mask); o.ib = __shfl_xor(s.ib, mask);
+  return o;
+}
+
+// Butterfly over the 64 lanes of a wave: every lane ends with the merge of
+// all 64 states.  The pairing order is fixed, so the result is reproducible.
+__device__ inline RowState wave_merge(RowState s) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    RowState o = shfl_xor_state(s, m);
+    // merge in lane order so both partners compute the identical value
+    const bool lower = (threadIdx.x & m) == 0;
+    s = lower ? merge(s, o) : merge(o, s);
+  }
+  return s;
+}
+
+// Per-position results from a complete state (f64 arithmetic on the f32 sums).
+struct RowResult {
+  float kl, lse_a, lse_b;
+  int ia, ib;
+};
+
+__device__ inline RowResult finish(const RowState &s) {
+  RowResult r;
+  const double sa = (double)s.sa, sb = (double)s.sb, t = (double)s.t;
+  double kl;
+  if (isnan(sa) || isnan(sb) || !(sa > 0.0) || !(sb > 0.0)) {
+    kl = __builtin_nan("");
+  } else if (isnan(t)) {
+    // t turns NaN only through 0 * inf: a finite reference logit whose
+    // weight underflowed met a -inf candidate logit, so q = 0 where p > 0.
+    kl = __builtin_inf();
+  } else {
+    kl = t / sa + log(sb / sa);
+    if (kl < 0.0) kl = 0.0;   // rounding below the true value (KL >= 0)
+  }
+  r.kl = kl == 0.0 ? 0.0f : (float)kl;   // canonical +0
+  r.lse_a = (float)((double)ref_of(s.ma) + log(sa));
+  r.lse_b = (float)((double)ref_of(s.mb) + log(sb));
+  r.ia = s.ia == kNoId ? 0 : s.ia;   // all ids -inf: every id ties, the lowest is 0
+  r.ib = s.ib == kNoId ? 0 : s.ib;
+  return r;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) {
+  return __uint_as_float(((uint32_t)u) << 16);
+}
+
+// Round f32 to fp16 bits, nearest-even (hardware conversion).
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+  _Float16 h = (_Float16)x;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+}  // namespace kld

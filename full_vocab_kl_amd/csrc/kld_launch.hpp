@@ -1,0 +1,40 @@
+// Host-side launch interface between the C ABI (kld_api.cpp) and the kernel
+// translation units.  Internal to libkld.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kld {
+
+struct RowState;
+
+struct RowsOut {
+  float *kl, *nll_ref, *nll_cand, *lse_ref, *lse_cand;
+  int32_t *argmax_ref, *argmax_cand;
+};
+
+struct TopkOut {
+  int32_t *ids_ref;
+  uint16_t *lp_ref;
+  int32_t *ids_cand;
+  uint16_t *lp_cand;
+};
+
+// ---- logits path ---------------------------------------------------------
+struct LogitsArgs {
+  const void *ref, *cand;
+  int dtype;              // 0 f32, 1 bf16
+  int64_t n, v, ld_ref, ld_cand;
+  int64_t chunk;          // ids per split (multiple of the vector width)
+  int splits;
+  bool aligned;           // both row sets 16-byte aligned
+  const int32_t *target;
+  RowsOut out;
+  hipStream_t stream;
+};
+int logits_vec_elems(int dtype);
+hipError_t launch_logits_state(const LogitsArgs &a, RowState *part);
+hipError_t launch_logits_finalize(const LogitsArgs &a, const RowState *part);
+
+}  // namespace kld

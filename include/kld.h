@@ -1,0 +1,205 @@
+/*
+ * libkld -- full-vocabulary KL scoring of a candidate model against a bf16
+ * reference, on one AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (sources are cited by page title and section):
+ *
+ *  - Per position, KL(p || q) over every vocabulary id, p = softmax of the
+ *    reference logits, q = softmax of the candidate logits, natural log,
+ *    f32 softmax.  ("Qwen3.8-27B fidelity suite v5": opening paragraphs,
+ *    the metric KL(BF16 || candidate); "Qwen3.8-27B Quantization Challenge":
+ *    "How the references were made" -- the full 248,320-id distribution in
+ *    f32 -- and "The score".)
+ *  - Top-1 agreement (exact argmax match, ties to the lower id), the NLL of
+ *    the true next token on both sides, the log-sum-exp of both rows.
+ *    ("Qwopus3.8-27B-Coder-Flash: quality-eval reference": "Method".)
+ *  - Logits either given, or produced in-kernel from final hidden states
+ *    through one shared bf16 head W[V, d] that is never written out as
+ *    logits.  (fidelity suite v5: opening paragraphs; "What is in here".)
+ *  - Top-64 export: ids int32 and fp16 log-probs, most likely first, and the
+ *    top-64 + one-tail-bucket approximate KLD.  (quality-eval reference:
+ *    "Files", "Method".)
+ *  - Mean / median / p99 / p99.9 KLD, top-1 rate and perplexities.
+ *    ("The score"; "Qwen3.8-27B IQ8R": "Quality".)
+ *
+ * Conventions shared by every entry point:
+ *
+ *  - Every tensor argument is DEVICE memory owned by the caller; the library
+ *    never allocates or frees memory.  Scratch space comes from the caller's
+ *    workspace (`ws`, `ws_bytes`), sized by kld_workspace_size().  Device
+ *    pointers must be 16-byte aligned unless stated otherwise.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream).  Outputs are valid once that stream has completed the work.
+ *  - Fail-closed: every argument is checked before anything is launched; on
+ *    an error nothing is launched and nothing is written.  n == 0 is a valid
+ *    no-op.  A failed launch returns KLD_EHIP.
+ *  - No global mutable state: calls are thread-safe.  Results are bitwise
+ *    deterministic (fixed-order merges, no floating-point atomics).
+ *  - Non-finite inputs: a -inf logit is a zero-probability id; a finite
+ *    reference logit against a -inf candidate logit makes KL +inf; a row with
+ *    a NaN or +inf logit, or whose reference or candidate row is all -inf,
+ *    gets KL = NaN.  A target id outside [0, V) gives NLL = NaN.
+ */
+#ifndef LIBKLD_KLD_H
+#define LIBKLD_KLD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KLD_ABI_VERSION 1
+#define KLD_TOPK 64           /* the export width the quality-eval reference uses */
+#define KLD_MAX_QUANTILES 16
+
+typedef enum kld_status {
+  KLD_OK = 0,
+  KLD_EINVAL = 1,       /* a required pointer is NULL or a count is negative */
+  KLD_ESHAPE = 2,       /* inconsistent sizes (ld < v, v < 64 with top-k, k != 64, ...) */
+  KLD_EDTYPE = 3,       /* unknown dtype code */
+  KLD_EWORKSPACE = 4,   /* workspace missing or smaller than kld_workspace_size() */
+  KLD_EUNSUPPORTED = 5, /* valid request this build does not serve (alignment, d % 8) */
+  KLD_EHIP = 6          /* the HIP runtime reported an error at launch */
+} kld_status;
+
+typedef enum kld_dtype {
+  KLD_F32 = 0,          /* IEEE binary32 logits */
+  KLD_BF16 = 1          /* bfloat16 logits, passed as uint16 bit patterns */
+} kld_dtype;
+
+/* Operation codes for kld_workspace_size(). */
+enum {
+  KLD_OP_FROM_LOGITS = 0,
+  KLD_OP_FUSED_HEAD = 1,
+  KLD_OP_TOPK_EXPORT = 2,
+  KLD_OP_SUMMARY = 3
+};
+#define KLD_FLAG_TOPK 1       /* the call will also export top-64 lists */
+
+/* Per-position outputs, each [n] device arrays.  `kl` is required; any other
+ * member may be NULL to skip it.  nll_* need a target array. */
+typedef struct kld_rows {
+  float *kl;            /* KL(ref || cand) in nats, >= +0 (never -0) or NaN/+inf */
+  float *nll_ref;       /* lse_ref - ref[target] */
+  float *nll_cand;      /* lse_cand - cand[target] */
+  float *lse_ref;       /* log-sum-exp of the reference row */
+  float *lse_cand;
+  int32_t *argmax_ref;  /* lowest id among the row's maxima */
+  int32_t *argmax_cand;
+} kld_rows;
+
+/* Optional top-64 export, [n, 64] device arrays, most likely first (value
+ * descending, then id ascending); lp is log-prob rounded to fp16 (nearest
+ * even), given as uint16 bit patterns.  Members may be NULL per side. */
+typedef struct kld_topk {
+  int32_t *ids_ref;
+  uint16_t *lp_ref;
+  int32_t *ids_cand;
+  uint16_t *lp_cand;
+} kld_topk;
+
+/* Bytes of workspace an operation needs.  op is a KLD_OP_* code; flags may
+ * hold KLD_FLAG_TOPK.  d is used by KLD_OP_FUSED_HEAD only; for
+ * KLD_OP_SUMMARY, n is the number of positions.  Returns 0 for an unknown op
+ * or negative sizes. */
+size_t kld_workspace_size(int op, int64_t n, int64_t v, int64_t d, int flags);
+
+/*
+ * kld_from_logits -- score n positions given both logit tensors.
+ *
+ * ref, cand : [n, v] row-major logits (dtype f32 or bf16 bits), leading
+ *             dimensions ld_ref, ld_cand >= v (in elements).  Any alignment is
+ *             accepted; 16-byte-aligned rows take the vector path.
+ * target    : [n] int32 true next-token ids, or NULL (then nll_* must be NULL).
+ * out       : per-position outputs (see kld_rows).
+ * topk      : NULL, or top-64 export of both sides (needs v >= 64).
+ * Definition: KL over all v ids per row ("Qwen3.8-27B fidelity suite v5",
+ * opening paragraphs; "Qwen3.8-27B Quantization Challenge", "The score").
+ */
+kld_status kld_from_logits(const void *ref, const void *cand, int dtype, int64_t n, int64_t v,
+                           int64_t ld_ref, int64_t ld_cand, const int32_t *target,
+                           const kld_rows *out, const kld_topk *topk, void *ws, size_t ws_bytes,
+                           void *stream);
+
+/*
+ * kld_fused_head -- score n positions from final hidden states through one
+ * shared bf16 head, without writing logits to memory ("Qwen3.8-27B fidelity
+ * suite v5": opening paragraphs, one shared BF16 head for both sides;
+ * "What is in here": hidden states [2047, 5120] bf16).
+ *
+ * W             : [v, d] bf16 head, row-major, contiguous.
+ * h_ref, h_cand : [n, d] bf16 hidden states, row-major, contiguous.
+ * Logits z = W h are accumulated in f32 from exact bf16 products and are not
+ * rounded to bf16; the softmax is taken in f32.  d must be a multiple of 8.
+ * target, out, topk as for kld_from_logits.
+ */
+kld_status kld_fused_head(const uint16_t *W, int64_t v, int64_t d, const uint16_t *h_ref,
+                          const uint16_t *h_cand, int64_t n, const int32_t *target,
+                          const kld_rows *out, const kld_topk *topk, void *ws, size_t ws_bytes,
+                          void *stream);
+
+/*
+ * topk_export -- top-k ids and fp16 log-probs of one logit tensor, and the
+ * log-prob of the true next token ("Qwopus3.8-27B-Coder-Flash: quality-eval
+ * reference", "Files": <set>.ids int32, <set>.lp float16, <set>.target f32).
+ *
+ * logits    : [n, v] (dtype f32 or bf16 bits), leading dimension ld >= v.
+ * k         : must be 64.  v >= 64.
+ * ids, lp   : [n, 64] outputs (int32, fp16 bits).
+ * target, target_lp : NULL, or [n] ids and [n] f32 log-prob outputs.
+ */
+kld_status topk_export(const void *logits, int dtype, int64_t n, int64_t v, int64_t ld, int k,
+                       int32_t *ids, uint16_t *lp, const int32_t *target, float *target_lp,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * kld_topk_tail -- the top-64 + one-tail-bucket approximate KLD of the
+ * quality-eval reference ("Method"), per position, from two exported lists.
+ *
+ * ids_p, lp_p : reference list [n, k] (int32 ids, fp16 log-prob bits).
+ * ids_q, lp_q : candidate list [n, k].
+ * k = 64; v > k is the vocabulary size.  kl_tail: [n] f32 output.
+ * Cells: the reference's k ids plus one tail cell.  A reference id absent
+ * from the candidate list gets r / (v - k), r = max(0, 1 - candidate list
+ * mass); the candidate tail cell is max(0, 1 - sum of its cell estimates);
+ * the reference tail is max(0, 1 - reference list mass).  0 ln(0/x) = 0,
+ * p ln(p/0) = +inf.  Needs no workspace.  Pointers need 4-byte alignment.
+ */
+kld_status kld_topk_tail(const int32_t *ids_p, const uint16_t *lp_p, const int32_t *ids_q,
+                         const uint16_t *lp_q, int64_t n, int k, int64_t v, float *kl_tail,
+                         void *stream);
+
+/*
+ * kld_summary -- aggregate per-position scores, every position weighted
+ * equally ("Qwen3.8-27B Quantization Challenge", "The score": mean KL ranks,
+ * with median, p99, p99.9, top-1 and the perplexity ratio).
+ *
+ * kl          : [n] per-position KL (required, values >= +0 or NaN/+inf).
+ * argmax_ref/argmax_cand : [n] or both NULL.   nll_ref/nll_cand : [n] or both NULL.
+ * quantiles   : HOST array of nq values in [0, 1], nq <= 16.
+ * out         : DEVICE double[8 + nq]:
+ *   [0] mean KL  [1] top-1 rate  [2] mean NLL ref  [3] mean NLL cand
+ *   [4] ppl ref = exp(mean NLL ref)  [5] ppl cand  [6] ppl cand / ppl ref
+ *   [7] count of non-finite KL values
+ *   [8 + i] quantile i of KL: linear interpolation between exact order
+ *           statistics (h = q (n - 1)); NaN values sort above +inf.
+ * Entries whose inputs are NULL are written as NaN.
+ */
+kld_status kld_summary(const float *kl, const int32_t *argmax_ref, const int32_t *argmax_cand,
+                       const float *nll_ref, const float *nll_cand, int64_t n,
+                       const double *quantiles, int nq, double *out, void *ws, size_t ws_bytes,
+                       void *stream);
+
+/* Human-readable name of a status code (static string). */
+const char *kld_status_str(int status);
+
+/* KLD_ABI_VERSION of the built library. */
+int kld_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBKLD_KLD_H */

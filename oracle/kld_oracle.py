@@ -40,6 +40,7 @@ Readings where the pages are silent (each also listed in the design notes):
       reference or candidate logits are all -inf, or that holds a NaN or
       +inf, has KL = NaN.
 * R7  NLL of a target id outside [0, V) is NaN.
+* R8  argmax ignores NaN entries; a row of only NaN reports id 0.
 
 Parity is pinned for every function here by the ``-m "not gpu"`` tests
 (tests/test_oracle_pins.py); no function is "parity unpinned".
@@ -131,7 +132,10 @@ def argmax_row(x: np.ndarray) -> int:
     [QE] "Method": top-1 agreement is an exact argmax match; [QC] "The
     score": the leaderboard's top-1 agreement (argmax match)."""
     x = np.asarray(x, dtype=np.float64)
-    m = x.max()
+    ok = ~np.isnan(x)                          # reading R8: NaN ids never win
+    if not ok.any():
+        return 0
+    m = x[ok].max()
     return int(np.flatnonzero(x == m)[0])
 
 

@@ -1,0 +1,73 @@
+"""CPU-only checks of the C-ABI library: it loads, exports every symbol that
+include/kld.h declares, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import full_vocab_kl_amd as kld
+from full_vocab_kl_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "kld.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kld_\w+|topk_export)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert {"kld_from_logits", "kld_fused_head", "topk_export", "kld_topk_tail", "kld_summary",
+            "kld_workspace_size", "kld_status_str", "kld_abi_version"} <= set(names)
+    lib = kld.lib()
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(binding.EXPORTED)
+
+
+def test_abi_version_and_status_strings():
+    assert kld.kld_abi_version() == 1
+    assert kld.kld_status_str(0) == "KLD_OK"
+    for c in range(1, 7):
+        assert kld.kld_status_str(c).startswith("KLD_E")
+
+
+def test_workspace_sizes():
+    assert kld.kld_workspace_size(0, 512, 248_320) > 0
+    assert kld.kld_workspace_size(0, -1, 10) == 0
+    assert kld.kld_workspace_size(99, 1, 10) == 0
+    assert kld.kld_workspace_size(0, 0, 10) == 0
+
+
+def _rows(kl=1):
+    return binding._Rows(kl, None, None, None, None, None, None)
+
+
+def _call_from_logits(ref=16, cand=16, dtype=0, n=4, v=100, ld_ref=100, ld_cand=100, target=None,
+                      rows=None, topk=None, ws=16, ws_bytes=1 << 30):
+    rows = rows if rows is not None else _rows()
+    return kld.lib().kld_from_logits(ref, cand, dtype, n, v, ld_ref, ld_cand, target,
+                                     ctypes.byref(rows), topk, ws, ws_bytes, None)
+
+
+def test_from_logits_validation_fails_closed():
+    # every case fails validation, so nothing reaches the GPU (fake pointers are never touched)
+    assert _call_from_logits(dtype=7) == 3
+    assert _call_from_logits(n=-1) == 1
+    assert _call_from_logits(ref=None) == 1
+    assert _call_from_logits(cand=None) == 1
+    assert _call_from_logits(rows=_rows(kl=None)) == 1
+    assert _call_from_logits(ld_ref=99) == 2
+    assert _call_from_logits(ld_cand=50) == 2
+    assert _call_from_logits(v=0) == 2
+    nll_rows = binding._Rows(16, 16, None, None, None, None, None)
+    assert _call_from_logits(rows=nll_rows, target=None) == 1
+    assert _call_from_logits(ws=None) == 4
+    assert _call_from_logits(ws_bytes=3) == 4
+    tk = binding._Topk(16, 16, 16, 16)
+    assert _call_from_logits(v=63, ld_ref=63, ld_cand=63, topk=ctypes.byref(tk)) == 2
+    # n == 0 is a valid no-op
+    assert _call_from_logits(n=0) == 0

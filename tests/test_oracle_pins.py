@@ -167,6 +167,8 @@ def test_argmax_lowest_id_on_ties():
     assert oracle.argmax_row(np.array([1.0, 3.0, 2.0, 3.0])) == 1
     assert oracle.argmax_row(np.array([-math.inf, -math.inf])) == 0
     assert oracle.argmax_row(np.array([5.0, 5.0, 5.0])) == 0
+    assert oracle.argmax_row(np.array([1.0, math.nan, 7.0, 7.0])) == 2
+    assert oracle.argmax_row(np.array([math.nan, math.nan])) == 0
 
 
 def _brute_topk(x, k):
