@@ -60,6 +60,14 @@ size_t logits_workspace(int64_t n, int64_t v, int flags, Carver *c) {
   return round_up(c->used, kAlign);
 }
 
+size_t fused_workspace(int64_t n, int64_t v, int flags, Carver *c) {
+  (void)flags;
+  const FusedGeom g = fused_geom(n, v);
+  c->take<float>((size_t)7 * g.nvt * g.npad);
+  c->take<float>((size_t)2 * n);
+  return round_up(c->used, kAlign);
+}
+
 inline hipStream_t as_stream(void *s) { return (hipStream_t)s; }
 
 }  // namespace
@@ -86,6 +94,7 @@ size_t kld_workspace_size(int op, int64_t n, int64_t v, int64_t d, int flags) {
   Carver c(nullptr);
   switch (op) {
     case KLD_OP_FROM_LOGITS: return logits_workspace(n, v, flags, &c);
+    case KLD_OP_FUSED_HEAD: return fused_workspace(n, v, flags, &c);
     default: return 0;
   }
 }
@@ -132,9 +141,32 @@ kld_status kld_fused_head(const uint16_t *W, int64_t v, int64_t d, const uint16_
                           const uint16_t *h_cand, int64_t n, const int32_t *target,
                           const kld_rows *out, const kld_topk *topk, void *ws, size_t ws_bytes,
                           void *stream) {
-  (void)W; (void)v; (void)d; (void)h_ref; (void)h_cand; (void)n; (void)target; (void)out;
-  (void)topk; (void)ws; (void)ws_bytes; (void)stream;
-  return KLD_EUNSUPPORTED;
+  if (n < 0 || v < 0 || d < 0) return KLD_EINVAL;
+  if (!out) return KLD_EINVAL;
+  if (n == 0) return KLD_OK;
+  if (v < 1 || v > 0x7fffffffLL || d < 1) return KLD_ESHAPE;
+  if (!W || !h_ref || !h_cand || !out->kl) return KLD_EINVAL;
+  if ((out->nll_ref || out->nll_cand) && !target) return KLD_EINVAL;
+  if (d % 8 != 0 || !aligned16(W) || !aligned16(h_ref) || !aligned16(h_cand))
+    return KLD_EUNSUPPORTED;
+  if (topk) {
+    if (v < KLD_TOPK) return KLD_ESHAPE;
+    return KLD_EUNSUPPORTED;
+  }
+  const size_t need = kld_workspace_size(KLD_OP_FUSED_HEAD, n, v, d, topk ? KLD_FLAG_TOPK : 0);
+  if (!ws || ws_bytes < need) return KLD_EWORKSPACE;
+
+  const FusedGeom g = fused_geom(n, v);
+  Carver c(ws);
+  float *part = c.take<float>((size_t)7 * g.nvt * g.npad);
+  float *zt = c.take<float>((size_t)2 * n);
+  FusedArgs a;
+  a.W = W; a.h_ref = h_ref; a.h_cand = h_cand; a.v = v; a.d = d; a.n = n; a.target = target;
+  a.out = RowsOut{out->kl, out->nll_ref, out->nll_cand, out->lse_ref, out->lse_cand,
+                  out->argmax_ref, out->argmax_cand};
+  a.stream = as_stream(stream);
+  if (launch_fused(a, part, zt) != hipSuccess) return KLD_EHIP;
+  return KLD_OK;
 }
 
 kld_status topk_export(const void *logits, int dtype, int64_t n, int64_t v, int64_t ld, int k,

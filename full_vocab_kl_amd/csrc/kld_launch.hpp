@@ -37,4 +37,19 @@ int logits_vec_elems(int dtype);
 hipError_t launch_logits_state(const LogitsArgs &a, RowState *part);
 hipError_t launch_logits_finalize(const LogitsArgs &a, const RowState *part);
 
+// ---- fused head path ------------------------------------------------------
+struct FusedArgs {
+  const uint16_t *W, *h_ref, *h_cand;
+  int64_t v, d, n;
+  const int32_t *target;
+  RowsOut out;
+  hipStream_t stream;
+};
+struct FusedGeom {
+  int64_t nvt, npt, npad;   // vocabulary tiles, position tiles, padded positions
+};
+FusedGeom fused_geom(int64_t n, int64_t v);
+// part: 7 * nvt * npad floats; zt: 2 * n floats (used when a target is given)
+hipError_t launch_fused(const FusedArgs &a, float *part, float *zt);
+
 }  // namespace kld

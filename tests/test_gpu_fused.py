@@ -1,0 +1,92 @@
+"""GPU parity of kld_fused_head against the f64 oracle (through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import full_vocab_kl_amd as kld
+from gpu_util import gpu, need_gpu, to_dev, assert_kl_close, assert_mean_rel, assert_nll_close
+
+pytestmark = gpu
+
+GAP = 1e-3   # fused-path argmax exemption: oracle top-2 gap below this on that side
+
+
+def _inputs(workload, n, v, d, noise, rows=None):
+    w = synth.head_weight(workload, v, d)
+    hr, hc = synth.hidden_rows(workload, range(n), d, noise)
+    t = synth.targets(workload, range(n), v)
+    return w, hr, hc, t
+
+
+def _gpu(w, hr, hc, t):
+    out = kld.kld_fused_head(to_dev(w, True), to_dev(hr, True), to_dev(hc, True),
+                             to_dev(t) if t is not None else None)
+    torch.cuda.synchronize()
+    return {k: x.cpu().numpy() for k, x in out.items()}
+
+
+def _oracle(w, hr, hc, t):
+    a = oracle.head_logits(w, hr)
+    b = oracle.head_logits(w, hc)
+    res = oracle.score_rows(a, b, t)
+    for s, z in (("ref", a), ("cand", b)):
+        top2 = -np.sort(-z, axis=1)[:, :2]
+        res[f"gap_{s}"] = top2[:, 0] - top2[:, 1]
+    return res
+
+
+def _compare(got, want, where, strict_mean=False):
+    assert_kl_close(got["kl"], want["kl"], where)
+    g = np.asarray(got["kl"], np.float64); w = want["kl"]
+    if strict_mean:
+        assert_mean_rel(g, w, where=where)
+    else:
+        assert abs(g.mean() - w.mean()) <= np.mean(1e-6 + 1e-3 * w), where
+    for s in ("ref", "cand"):
+        ok = want[f"gap_{s}"] >= GAP
+        assert np.array_equal(got[f"argmax_{s}"][ok], want[f"argmax_{s}"][ok]), f"{where}: argmax {s}"
+        lw = want[f"lse_{s}"]
+        assert np.all(np.abs(got[f"lse_{s}"] - lw) <= 1e-5 * np.maximum(1, np.abs(lw))), where
+        if "nll_ref" in got:
+            assert_nll_close(got[f"nll_{s}"], want[f"nll_{s}"], where)
+
+
+@pytest.mark.parametrize("n,v,d", [(5, 300, 64), (130, 1000, 128), (37, 5003, 200), (129, 513, 520),
+                                   (300, 2048, 64), (1, 257, 8)])
+def test_fused_small_shapes(n, v, d):
+    need_gpu()
+    print(f"case n={n} v={v} d={d}", flush=True)
+    w, hr, hc, t = _inputs(synth.FUSED_WINDOW, n, v, d, 0.01)
+    _compare(_gpu(w, hr, hc, t), _oracle(w, hr, hc, t), f"n={n} v={v} d={d}")
+
+
+def test_fused_identical_hidden_gives_exact_zero():
+    need_gpu()
+    w, hr, _, t = _inputs(synth.FUSED_WINDOW, 70, 3000, 256, 0.01)
+    got = _gpu(w, hr, hr.copy(), t)
+    assert np.all(got["kl"] == 0.0) and not np.any(np.signbit(got["kl"]))
+    assert np.array_equal(got["argmax_ref"], got["argmax_cand"])
+
+
+def test_fused_deterministic():
+    need_gpu()
+    w, hr, hc, t = _inputs(synth.FUSED_WINDOW, 200, 4000, 512, 0.02)
+    r1 = _gpu(w, hr, hc, t)
+    r2 = _gpu(w, hr, hc, t)
+    for k in r1:
+        assert np.array_equal(r1[k].view(np.uint8), r2[k].view(np.uint8)), k
+
+
+def test_fused_full_window_sampled():
+    """One 2047-position window at d = 5120, V = 248,320 (the launch the bench
+    times); the oracle checks 48 seeded positions."""
+    need_gpu()
+    n, v, d = synth.WINDOW_POSITIONS, synth.VOCAB, synth.HIDDEN
+    w, hr, hc, t = _inputs(synth.FUSED_WINDOW, n, v, d, 0.01)
+    got = _gpu(w, hr, hc, t)
+    rows = synth.subset(synth.FUSED_WINDOW, n, 48)
+    want = _oracle(w, hr[rows], hc[rows], t[rows])
+    _compare({k: x[rows] for k, x in got.items()}, want, "full window", strict_mean=True)
+    assert np.all(np.isfinite(got["kl"])) and np.all(got["kl"] >= 0)
