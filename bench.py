@@ -1,0 +1,254 @@
+"""Throughput of the libkld hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload fused_window]
+
+Default workload: one 2047-position window through the shared head
+(d = 5120, V = 248,320, bf16 head and hidden states, f32 softmax).  One step
+is the whole path over that window: kld_fused_head (logits, KL, argmax, NLL
+and lse of every position, both sides) followed by kld_summary (mean KL,
+top-1, perplexities, median / p99 / p99.9 KL).  Inputs are seeded synthetic
+data already resident in HBM when the timed region starts.
+
+Prints one JSON line: positions/s over K timed steps, the roofline of the
+dominant kernel (its average duration from HIP events recorded around it on
+the launch stream during the timed steps), and the f64 CPU oracle timed on a
+bounded sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "scored positions/sec at V=248,320 (fused head d=5120) + % of MFMA/HBM peak"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+QUANTILES = (0.5, 0.99, 0.999)
+
+
+def _args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="fused_window", choices=["fused_window", "logits_f32"])
+    p.add_argument("--cpu-sample", type=int, default=None,
+                   help="positions the CPU oracle scores for the baseline (0 = skip)")
+    p.add_argument("--no-secondary", action="store_true",
+                   help="skip the secondary logits-path measurement")
+    return p.parse_args()
+
+
+def _traffic(kernel_key):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, or None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            return json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+
+
+# --------------------------------------------------------------------------
+# workloads
+# --------------------------------------------------------------------------
+
+def fused_window(steps, warmup, cpu_sample):
+    import numpy as np
+    import torch
+
+    import full_vocab_kl_amd as kld
+    import synth
+
+    n, v, d = synth.WINDOW_POSITIONS, synth.VOCAB, synth.HIDDEN
+    wl = synth.FUSED_WINDOW
+    w_np = synth.head_weight(wl, v, d)
+    hr_np, hc_np = synth.hidden_rows(wl, range(n), d, 0.01)
+    t_np = synth.targets(wl, range(n), v)
+    dev = torch.device("cuda:0")
+    bf = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    W, hr, hc = bf(w_np), bf(hr_np), bf(hc_np)
+    tg = torch.from_numpy(t_np).to(dev)
+    ws = torch.empty(kld.kld_workspace_size(1, n, v, d), dtype=torch.uint8, device=dev)
+    ws_s = torch.empty(kld.kld_workspace_size(3, n, 0), dtype=torch.uint8, device=dev)
+    summ = torch.empty(8 + len(QUANTILES), dtype=torch.float64, device=dev)
+    out = None
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+
+    def step(ev=None):
+        nonlocal out
+        out = kld.kld_fused_head(W, hr, hc, tg, ws=ws, out=out, events=ev)
+        kld.kld_summary(out["kl"], out["argmax_ref"], out["argmax_cand"], out["nll_ref"],
+                        out["nll_cand"], quantiles=QUANTILES, ws=ws_s, out=summ)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kms = [a.elapsed_time(b) for a, b in evs]
+    kernel_ms = sum(kms) / len(kms)
+    flops = 4.0 * n * d * v
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    summary = kld.summary_dict(summ, QUANTILES)
+
+    res = {
+        "value": n * steps / elapsed, "unit": "positions/s", "ms_per_step": elapsed * 1e3 / steps,
+        "dtype": "bf16",
+        "config": {"workload": "kld_fused_head + kld_summary: one window, N=2047 positions, "
+                               "d=5120, V=248,320, bf16 head W~N(0,0.02^2), hidden RMS-normalised, "
+                               "cand noise 0.01, f32 accumulate and softmax",
+                   "positions": n, "d": d, "V": v},
+        "roofline": {"bound": "mfma", "kernel": "fused_head_kernel",
+                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": _traffic("fused_head_kernel"),
+                     "kernel_ms": round(kernel_ms, 4),
+                     "algorithmic": f"4*N*d*V = {flops:.4e} flop per launch"},
+        "result": {"mean_kl": summary["mean_kl"], "top1": summary["top1"],
+                   "ppl_ref": summary["ppl_ref"], "ppl_cand": summary["ppl_cand"],
+                   "p99": summary["quantiles"][0.99], "p999": summary["quantiles"][0.999]},
+    }
+    if cpu_sample:
+        res["cpu_baseline"] = cpu_fused(w_np, hr_np, hc_np, t_np, cpu_sample)
+    return res
+
+
+def cpu_fused(w_np, hr_np, hc_np, t_np, m):
+    """The f64 oracle on m seeded positions of the same window (logits through
+    the head, then KL / argmax / NLL), timed on the host cores."""
+    import oracle
+    import synth
+
+    rows = synth.subset(synth.FUSED_WINDOW, hr_np.shape[0], m)
+    t0 = time.perf_counter()
+    a = oracle.head_logits(w_np, hr_np[rows])
+    b = oracle.head_logits(w_np, hc_np[rows])
+    oracle.score_rows(a, b, t_np[rows])
+    dt = time.perf_counter() - t0
+    return {"value": m / dt, "unit": "positions/s", "cores": _cores(), "kind": "oracle",
+            "sample": f"{m} seeded positions of the 2047-position window (head logits in f64 for "
+                      f"both sides over all 248,320 ids, then KL/argmax/NLL), {dt:.1f} s"}
+
+
+def logits_f32(steps, warmup, cpu_sample):
+    import numpy as np
+    import torch
+
+    import full_vocab_kl_amd as kld
+    import synth
+
+    n, v = 512, synth.VOCAB
+    wl = synth.LOGITS_F32
+    a_np, b_np = synth.logit_rows(wl, range(n), v)
+    t_np = synth.targets(wl, range(n), v)
+    dev = torch.device("cuda:0")
+    # two copies rotate so that one step's rows are not still in the 256 MB cache
+    sets = [(torch.from_numpy(a_np).to(dev), torch.from_numpy(b_np).to(dev)) for _ in range(2)]
+    tg = torch.from_numpy(t_np).to(dev)
+    ws = torch.empty(kld.kld_workspace_size(0, n, v), dtype=torch.uint8, device=dev)
+    ws_s = torch.empty(kld.kld_workspace_size(3, n, 0), dtype=torch.uint8, device=dev)
+    summ = torch.empty(8 + len(QUANTILES), dtype=torch.float64, device=dev)
+    out = None
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+
+    def step(i, ev=None):
+        nonlocal out
+        ra, rb = sets[i % 2]
+        out = kld.kld_from_logits(ra, rb, tg, ws=ws, out=out, events=ev)
+        kld.kld_summary(out["kl"], out["argmax_ref"], out["argmax_cand"], out["nll_ref"],
+                        out["nll_cand"], quantiles=QUANTILES, ws=ws_s, out=summ)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kms = [x.elapsed_time(y) for x, y in evs]
+    kernel_ms = sum(kms) / len(kms)
+    nbytes = 8.0 * n * v
+    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+    res = {
+        "value": n * steps / elapsed, "unit": "positions/s", "ms_per_step": elapsed * 1e3 / steps,
+        "dtype": "f32",
+        "config": {"workload": "kld_from_logits + kld_summary: N=512 rows, V=248,320 f32 logits",
+                   "positions": n, "V": v},
+        "roofline": {"bound": "hbm", "kernel": "logits_partial_kernel", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": _traffic("logits_partial_kernel_f32"),
+                     "kernel_ms": round(kernel_ms, 4),
+                     "algorithmic": f"8*N*V = {nbytes:.4e} bytes per launch"},
+    }
+    if cpu_sample:
+        import oracle
+        rows = np.arange(min(cpu_sample, n))
+        t0 = time.perf_counter()
+        oracle.score_rows(a_np[rows], b_np[rows], t_np[rows])
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": len(rows) / dt, "unit": "positions/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"first {len(rows)} rows, {dt:.1f} s"}
+    return res
+
+
+def _cores():
+    try:
+        import numpy  # noqa: F401
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS")
+    return min(n, int(env)) if env and env.isdigit() else n
+
+
+def main():
+    args = _args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build scores on exactly one GPU; multi-GPU runs are not part of it "
+              "(see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import full_vocab_kl_amd as kld
+    kld.lib()   # fails loudly if libkld.so is missing
+
+    if args.workload == "fused_window":
+        cpu = 48 if args.cpu_sample is None else args.cpu_sample
+        res = fused_window(args.steps, args.warmup, cpu)
+    else:
+        cpu = 64 if args.cpu_sample is None else args.cpu_sample
+        res = logits_f32(args.steps, args.warmup, cpu)
+
+    line = {"metric": METRIC, "value": round(res["value"], 1), "unit": res["unit"], "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": res["dtype"],
+            "data": "synthetic", "config": res["config"], "roofline": res["roofline"]}
+    if "cpu_baseline" in res:
+        line["cpu_baseline"] = res["cpu_baseline"]
+    if "result" in res:
+        line["result"] = res["result"]
+    if args.workload == "fused_window" and not args.no_secondary:
+        sec = logits_f32(max(5, args.steps), args.warmup, 0)
+        line["secondary"] = {"workload": sec["config"]["workload"], "value": round(sec["value"], 1),
+                             "unit": sec["unit"], "ms_per_step": round(sec["ms_per_step"], 4),
+                             "roofline": sec["roofline"]}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

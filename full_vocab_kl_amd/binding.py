@@ -43,6 +43,10 @@ class _Topk(ctypes.Structure):
                 ("ids_cand", ctypes.c_void_p), ("lp_cand", ctypes.c_void_p)]
 
 
+class _Opts(ctypes.Structure):
+    _fields_ = [("main_start", ctypes.c_void_p), ("main_stop", ctypes.c_void_p)]
+
+
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _I = ctypes.c_int
@@ -51,9 +55,9 @@ _SZ = ctypes.c_size_t
 _SIGS = {
     "kld_workspace_size": (_SZ, [_I, _I64, _I64, _I64, _I]),
     "kld_from_logits": (_I, [_P, _P, _I, _I64, _I64, _I64, _I64, _P, ctypes.POINTER(_Rows),
-                             ctypes.POINTER(_Topk), _P, _SZ, _P]),
+                             ctypes.POINTER(_Topk), _P, _SZ, _P, ctypes.POINTER(_Opts)]),
     "kld_fused_head": (_I, [_P, _I64, _I64, _P, _P, _I64, _P, ctypes.POINTER(_Rows),
-                            ctypes.POINTER(_Topk), _P, _SZ, _P]),
+                            ctypes.POINTER(_Topk), _P, _SZ, _P, ctypes.POINTER(_Opts)]),
     "topk_export": (_I, [_P, _I, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _SZ, _P]),
     "kld_topk_tail": (_I, [_P, _P, _P, _P, _I64, _I, _I64, _P, _P]),
     "kld_summary": (_I, [_P, _P, _P, _P, _P, _I64, _P, _I, _P, _P, _SZ, _P]),
@@ -101,6 +105,17 @@ def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _opts(events):
+    """events: None or (start, stop) torch.cuda.Event pair to time the main kernel."""
+    if events is None:
+        return None
+    start, stop = events
+    for e in (start, stop):
+        if e.cuda_event == 0:      # torch creates the HIP event lazily on first record
+            e.record()
+    return ctypes.byref(_Opts(start.cuda_event, stop.cuda_event))
 
 
 def _check(code: int, where: str):
@@ -162,7 +177,7 @@ def _topk_struct(tk):
 
 def kld_from_logits(ref: torch.Tensor, cand: torch.Tensor, target: torch.Tensor | None = None,
                     topk: bool = False, out: dict | None = None, ws: torch.Tensor | None = None,
-                    stream=None) -> dict:
+                    stream=None, events=None) -> dict:
     """Per-position KL(ref || cand), lse, argmax, NLL (with target) and the
     optional top-64 export, from two [n, v] logit tensors on the GPU."""
     n, v = ref.shape
@@ -179,7 +194,7 @@ def kld_from_logits(ref: torch.Tensor, cand: torch.Tensor, target: torch.Tensor 
     code = lib().kld_from_logits(_ptr(ref), _ptr(cand), dt, n, v, _rows_ld(ref), _rows_ld(cand),
                                  _ptr(target), ctypes.byref(rows),
                                  ctypes.byref(tks) if tks else None, _ptr(ws), ws.numel(),
-                                 _stream(stream))
+                                 _stream(stream), _opts(events))
     _check(code, "kld_from_logits")
     if tk:
         out.update(tk)
@@ -188,7 +203,7 @@ def kld_from_logits(ref: torch.Tensor, cand: torch.Tensor, target: torch.Tensor 
 
 def kld_fused_head(W: torch.Tensor, h_ref: torch.Tensor, h_cand: torch.Tensor,
                    target: torch.Tensor | None = None, topk: bool = False, out: dict | None = None,
-                   ws: torch.Tensor | None = None, stream=None) -> dict:
+                   ws: torch.Tensor | None = None, stream=None, events=None) -> dict:
     """Per-position scores from hidden states [n, d] through one shared bf16
     head W [v, d]; logits are never written to memory."""
     v, d = W.shape
@@ -205,7 +220,7 @@ def kld_fused_head(W: torch.Tensor, h_ref: torch.Tensor, h_cand: torch.Tensor,
     tks = _topk_struct(tk) if tk else None
     code = lib().kld_fused_head(_ptr(W), v, d, _ptr(h_ref), _ptr(h_cand), n, _ptr(target),
                                 ctypes.byref(rows), ctypes.byref(tks) if tks else None, _ptr(ws),
-                                ws.numel(), _stream(stream))
+                                ws.numel(), _stream(stream), _opts(events))
     _check(code, "kld_fused_head")
     if tk:
         out.update(tk)

@@ -70,6 +70,12 @@ size_t fused_workspace(int64_t n, int64_t v, int flags, Carver *c) {
 
 inline hipStream_t as_stream(void *s) { return (hipStream_t)s; }
 
+Events events_of(const kld_launch_opts *o) {
+  Events e;
+  if (o) { e.start = (hipEvent_t)o->main_start; e.stop = (hipEvent_t)o->main_stop; }
+  return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -95,6 +101,7 @@ size_t kld_workspace_size(int op, int64_t n, int64_t v, int64_t d, int flags) {
   switch (op) {
     case KLD_OP_FROM_LOGITS: return logits_workspace(n, v, flags, &c);
     case KLD_OP_FUSED_HEAD: return fused_workspace(n, v, flags, &c);
+    case KLD_OP_SUMMARY: return round_up(summary_workspace_bytes(n), kAlign);
     default: return 0;
   }
 }
@@ -102,7 +109,7 @@ size_t kld_workspace_size(int op, int64_t n, int64_t v, int64_t d, int flags) {
 kld_status kld_from_logits(const void *ref, const void *cand, int dtype, int64_t n, int64_t v,
                            int64_t ld_ref, int64_t ld_cand, const int32_t *target,
                            const kld_rows *out, const kld_topk *topk, void *ws, size_t ws_bytes,
-                           void *stream) {
+                           void *stream, const kld_launch_opts *opts) {
   if (dtype != KLD_F32 && dtype != KLD_BF16) return KLD_EDTYPE;
   if (n < 0 || v < 0) return KLD_EINVAL;
   if (!out) return KLD_EINVAL;
@@ -129,6 +136,7 @@ kld_status kld_from_logits(const void *ref, const void *cand, int dtype, int64_t
   a.out = RowsOut{out->kl, out->nll_ref, out->nll_cand, out->lse_ref, out->lse_cand,
                   out->argmax_ref, out->argmax_cand};
   a.stream = as_stream(stream);
+  a.ev = events_of(opts);
 
   Carver c(ws);
   RowState *part = c.take<RowState>((size_t)n * g.splits);
@@ -140,7 +148,7 @@ kld_status kld_from_logits(const void *ref, const void *cand, int dtype, int64_t
 kld_status kld_fused_head(const uint16_t *W, int64_t v, int64_t d, const uint16_t *h_ref,
                           const uint16_t *h_cand, int64_t n, const int32_t *target,
                           const kld_rows *out, const kld_topk *topk, void *ws, size_t ws_bytes,
-                          void *stream) {
+                          void *stream, const kld_launch_opts *opts) {
   if (n < 0 || v < 0 || d < 0) return KLD_EINVAL;
   if (!out) return KLD_EINVAL;
   if (n == 0) return KLD_OK;
@@ -165,6 +173,7 @@ kld_status kld_fused_head(const uint16_t *W, int64_t v, int64_t d, const uint16_
   a.out = RowsOut{out->kl, out->nll_ref, out->nll_cand, out->lse_ref, out->lse_cand,
                   out->argmax_ref, out->argmax_cand};
   a.stream = as_stream(stream);
+  a.ev = events_of(opts);
   if (launch_fused(a, part, zt) != hipSuccess) return KLD_EHIP;
   return KLD_OK;
 }
@@ -189,9 +198,33 @@ kld_status kld_summary(const float *kl, const int32_t *argmax_ref, const int32_t
                        const float *nll_ref, const float *nll_cand, int64_t n,
                        const double *quantiles, int nq, double *out, void *ws, size_t ws_bytes,
                        void *stream) {
-  (void)kl; (void)argmax_ref; (void)argmax_cand; (void)nll_ref; (void)nll_cand; (void)n;
-  (void)quantiles; (void)nq; (void)out; (void)ws; (void)ws_bytes; (void)stream;
-  return KLD_EUNSUPPORTED;
+  if (n < 0 || nq < 0) return KLD_EINVAL;
+  if (!out) return KLD_EINVAL;
+  if (n == 0) return KLD_OK;
+  if (n > 0x7fffffffLL || nq > KLD_MAX_QUANTILES) return KLD_ESHAPE;
+  if (!kl || (nq > 0 && !quantiles)) return KLD_EINVAL;
+  if ((argmax_ref == nullptr) != (argmax_cand == nullptr)) return KLD_EINVAL;
+  if ((nll_ref == nullptr) != (nll_cand == nullptr)) return KLD_EINVAL;
+  SummaryArgs a;
+  a.ranks.count = 2 * nq;
+  a.qs.count = nq;
+  for (int i = 0; i < nq; ++i) {
+    const double q = quantiles[i];
+    if (!(q >= 0.0 && q <= 1.0)) return KLD_ESHAPE;
+    const double h = q * (double)(n - 1);
+    int64_t lo = (int64_t)h;
+    if (lo > n - 1) lo = n - 1;
+    const int64_t hi = lo + 1 < n ? lo + 1 : n - 1;
+    a.ranks.rank[2 * i] = (uint32_t)lo;
+    a.ranks.rank[2 * i + 1] = (uint32_t)hi;
+    a.qs.frac[i] = h - (double)lo;
+  }
+  if (!ws || ws_bytes < kld_workspace_size(KLD_OP_SUMMARY, n, 0, 0, 0)) return KLD_EWORKSPACE;
+  a.kl = kl; a.argmax_ref = argmax_ref; a.argmax_cand = argmax_cand;
+  a.nll_ref = nll_ref; a.nll_cand = nll_cand; a.n = n; a.out = out;
+  a.stream = as_stream(stream);
+  if (launch_summary(a, ws) != hipSuccess) return KLD_EHIP;
+  return KLD_OK;
 }
 
 }  // extern "C"

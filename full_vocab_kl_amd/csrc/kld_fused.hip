@@ -323,10 +323,14 @@ hipError_t launch_fused(const FusedArgs &a, float *part, float *zt) {
                                      2 * STAGE_CHUNKS * (int)sizeof(u32x4));
   if (e != hipSuccess) return e;
   const int64_t nblocks = g.nvt * g.npt;
+  e = record(a.ev.start, a.stream);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fused_head_kernel, dim3((unsigned)nblocks), dim3(NT),
                      2 * STAGE_CHUNKS * sizeof(u32x4), a.stream, a.W, a.h_ref, a.h_cand, a.v, a.d,
                      a.n, (int)g.npt, g.npad, g.nvt, part);
   e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = record(a.ev.stop, a.stream);
   if (e != hipSuccess) return e;
   if (a.target) {
     hipLaunchKernelGGL(target_logit_kernel, dim3((unsigned)((a.n + 3) / 4)), dim3(256), 0,

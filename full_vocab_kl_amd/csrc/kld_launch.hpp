@@ -22,6 +22,11 @@ struct TopkOut {
 };
 
 // ---- logits path ---------------------------------------------------------
+struct Events {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+inline hipError_t record(hipEvent_t e, hipStream_t s) { return e ? hipEventRecord(e, s) : hipSuccess; }
+
 struct LogitsArgs {
   const void *ref, *cand;
   int dtype;              // 0 f32, 1 bf16
@@ -32,6 +37,7 @@ struct LogitsArgs {
   const int32_t *target;
   RowsOut out;
   hipStream_t stream;
+  Events ev;
 };
 int logits_vec_elems(int dtype);
 hipError_t launch_logits_state(const LogitsArgs &a, RowState *part);
@@ -44,6 +50,7 @@ struct FusedArgs {
   const int32_t *target;
   RowsOut out;
   hipStream_t stream;
+  Events ev;
 };
 struct FusedGeom {
   int64_t nvt, npt, npad;   // vocabulary tiles, position tiles, padded positions
@@ -51,5 +58,28 @@ struct FusedGeom {
 FusedGeom fused_geom(int64_t n, int64_t v);
 // part: 7 * nvt * npad floats; zt: 2 * n floats (used when a target is given)
 hipError_t launch_fused(const FusedArgs &a, float *part, float *zt);
+
+// ---- summary ---------------------------------------------------------------
+constexpr int kSummaryMaxRanks = 32;   // two order statistics per quantile, <= 16 quantiles
+struct SummaryRanks {
+  int count;
+  uint32_t rank[kSummaryMaxRanks];
+};
+struct SummaryQuantiles {
+  int count;
+  double frac[kSummaryMaxRanks / 2];
+};
+struct SummaryArgs {
+  const float *kl;
+  const int32_t *argmax_ref, *argmax_cand;
+  const float *nll_ref, *nll_cand;
+  int64_t n;
+  SummaryRanks ranks;
+  SummaryQuantiles qs;
+  double *out;
+  hipStream_t stream;
+};
+size_t summary_workspace_bytes(int64_t n);
+hipError_t launch_summary(const SummaryArgs &a, void *ws);
 
 }  // namespace kld

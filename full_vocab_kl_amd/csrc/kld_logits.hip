@@ -165,10 +165,13 @@ __global__ __launch_bounds__(256) void finalize_rows_kernel(
 template <typename T, int VEC, int U, bool ALIGNED>
 hipError_t launch_partial(const LogitsArgs &a, RowState *part) {
   dim3 grid((unsigned)(a.n * a.splits));
+  if (record(a.ev.start, a.stream) != hipSuccess) return hipErrorInvalidValue;
   hipLaunchKernelGGL((logits_partial_kernel<T, VEC, U, ALIGNED>), grid, dim3(kThreads), 0, a.stream,
                      (const T *)a.ref, (const T *)a.cand, a.ld_ref, a.ld_cand, a.v, a.chunk, a.splits,
                      part);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return record(a.ev.stop, a.stream);
 }
 
 template <typename T>

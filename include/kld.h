@@ -100,6 +100,15 @@ typedef struct kld_topk {
   uint16_t *lp_cand;
 } kld_topk;
 
+/* Optional launch options (any pointer may be NULL).  main_start/main_stop
+ * are hipEvent_t handles recorded on `stream` immediately before and after the
+ * call's dominant kernel (the streaming pass or the fused MFMA kernel), so a
+ * caller can time that kernel alone. */
+typedef struct kld_launch_opts {
+  void *main_start;
+  void *main_stop;
+} kld_launch_opts;
+
 /* Bytes of workspace an operation needs.  op is a KLD_OP_* code; flags may
  * hold KLD_FLAG_TOPK.  d is used by KLD_OP_FUSED_HEAD only; for
  * KLD_OP_SUMMARY, n is the number of positions.  Returns 0 for an unknown op
@@ -115,13 +124,14 @@ size_t kld_workspace_size(int op, int64_t n, int64_t v, int64_t d, int flags);
  * target    : [n] int32 true next-token ids, or NULL (then nll_* must be NULL).
  * out       : per-position outputs (see kld_rows).
  * topk      : NULL, or top-64 export of both sides (needs v >= 64).
+ * opts      : NULL, or launch options (timing events).
  * Definition: KL over all v ids per row ("Qwen3.8-27B fidelity suite v5",
  * opening paragraphs; "Qwen3.8-27B Quantization Challenge", "The score").
  */
 kld_status kld_from_logits(const void *ref, const void *cand, int dtype, int64_t n, int64_t v,
                            int64_t ld_ref, int64_t ld_cand, const int32_t *target,
                            const kld_rows *out, const kld_topk *topk, void *ws, size_t ws_bytes,
-                           void *stream);
+                           void *stream, const kld_launch_opts *opts);
 
 /*
  * kld_fused_head -- score n positions from final hidden states through one
@@ -133,12 +143,12 @@ kld_status kld_from_logits(const void *ref, const void *cand, int dtype, int64_t
  * h_ref, h_cand : [n, d] bf16 hidden states, row-major, contiguous.
  * Logits z = W h are accumulated in f32 from exact bf16 products and are not
  * rounded to bf16; the softmax is taken in f32.  d must be a multiple of 8.
- * target, out, topk as for kld_from_logits.
+ * target, out, topk, opts as for kld_from_logits.
  */
 kld_status kld_fused_head(const uint16_t *W, int64_t v, int64_t d, const uint16_t *h_ref,
                           const uint16_t *h_cand, int64_t n, const int32_t *target,
                           const kld_rows *out, const kld_topk *topk, void *ws, size_t ws_bytes,
-                          void *stream);
+                          void *stream, const kld_launch_opts *opts);
 
 /*
  * topk_export -- top-k ids and fp16 log-probs of one logit tensor, and the

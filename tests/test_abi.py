@@ -50,7 +50,7 @@ def _call_from_logits(ref=16, cand=16, dtype=0, n=4, v=100, ld_ref=100, ld_cand=
                       rows=None, topk=None, ws=16, ws_bytes=1 << 30):
     rows = rows if rows is not None else _rows()
     return kld.lib().kld_from_logits(ref, cand, dtype, n, v, ld_ref, ld_cand, target,
-                                     ctypes.byref(rows), topk, ws, ws_bytes, None)
+                                     ctypes.byref(rows), topk, ws, ws_bytes, None, None)
 
 
 def test_from_logits_validation_fails_closed():
@@ -71,3 +71,24 @@ def test_from_logits_validation_fails_closed():
     assert _call_from_logits(v=63, ld_ref=63, ld_cand=63, topk=ctypes.byref(tk)) == 2
     # n == 0 is a valid no-op
     assert _call_from_logits(n=0) == 0
+
+
+def test_summary_validation_fails_closed():
+    lib = kld.lib()
+    qs = (ctypes.c_double * 3)(0.5, 0.99, 0.999)
+    bad_q = (ctypes.c_double * 1)(1.5)
+    call = lambda **k: lib.kld_summary(k.get("kl", 16), k.get("ar", None), k.get("ac", None),  # noqa: E731
+                                       k.get("nr", None), k.get("nc", None), k.get("n", 10),
+                                       k.get("q", qs), k.get("nq", 3), k.get("out", 16),
+                                       k.get("ws", 16), k.get("wsb", 1 << 30), None)
+    assert call(kl=None) == 1
+    assert call(out=None) == 1
+    assert call(ar=16) == 1
+    assert call(nc=16) == 1
+    assert call(nq=17) == 2
+    assert call(q=bad_q, nq=1) == 2
+    assert call(q=None) == 1
+    assert call(ws=None) == 4
+    assert call(wsb=10) == 4
+    assert call(n=-1) == 1
+    assert call(n=0) == 0
