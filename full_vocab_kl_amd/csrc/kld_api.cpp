@@ -41,6 +41,7 @@ struct LogitsGeom {
 
 LogitsGeom logits_geom(int64_t n, int64_t v) {
   int64_t want = n > 0 ? (4096 + n - 1) / n : 1;
+  if (want > kMaxSplits) want = kMaxSplits;
   int64_t max_splits = (v + 4095) / 4096;
   if (max_splits < 1) max_splits = 1;
   if (want > max_splits) want = max_splits;
@@ -53,10 +54,23 @@ LogitsGeom logits_geom(int64_t n, int64_t v) {
   return g;
 }
 
+struct LogitsWs {
+  RowState *part;
+  uint64_t *keys;   // with top-k
+  double *lse;      // with top-k
+};
+
+LogitsWs logits_carve(int64_t n, int64_t v, bool topk, Carver *c) {
+  const LogitsGeom g = logits_geom(n, v);
+  LogitsWs w;
+  w.part = c->take<RowState>((size_t)n * g.splits);
+  w.keys = topk ? c->take<uint64_t>((size_t)n * g.splits * 2 * 64) : nullptr;
+  w.lse = topk ? c->take<double>((size_t)2 * n) : nullptr;
+  return w;
+}
+
 size_t logits_workspace(int64_t n, int64_t v, int flags, Carver *c) {
-  (void)flags;
-  LogitsGeom g = logits_geom(n, v);
-  c->take<RowState>((size_t)n * g.splits);
+  logits_carve(n, v, (flags & KLD_FLAG_TOPK) != 0, c);
   return round_up(c->used, kAlign);
 }
 
@@ -100,6 +114,7 @@ size_t kld_workspace_size(int op, int64_t n, int64_t v, int64_t d, int flags) {
   Carver c(nullptr);
   switch (op) {
     case KLD_OP_FROM_LOGITS: return logits_workspace(n, v, flags, &c);
+    case KLD_OP_TOPK_EXPORT: return logits_workspace(n, v, KLD_FLAG_TOPK, &c);
     case KLD_OP_FUSED_HEAD: return fused_workspace(n, v, flags, &c);
     case KLD_OP_SUMMARY: return round_up(summary_workspace_bytes(n), kAlign);
     default: return 0;
@@ -118,10 +133,7 @@ kld_status kld_from_logits(const void *ref, const void *cand, int dtype, int64_t
   if (!ref || !cand || !out->kl) return KLD_EINVAL;
   if (ld_ref < v || ld_cand < v) return KLD_ESHAPE;
   if ((out->nll_ref || out->nll_cand) && !target) return KLD_EINVAL;
-  if (topk) {
-    if (v < KLD_TOPK) return KLD_ESHAPE;
-    return KLD_EUNSUPPORTED;
-  }
+  if (topk && v < KLD_TOPK) return KLD_ESHAPE;
   const size_t need = kld_workspace_size(KLD_OP_FROM_LOGITS, n, v, 0, topk ? KLD_FLAG_TOPK : 0);
   if (!ws || ws_bytes < need) return KLD_EWORKSPACE;
 
@@ -132,6 +144,7 @@ kld_status kld_from_logits(const void *ref, const void *cand, int dtype, int64_t
   a.ld_ref = ld_ref; a.ld_cand = ld_cand; a.chunk = g.chunk; a.splits = g.splits;
   a.aligned = aligned16(ref) && aligned16(cand) && (ld_ref * esize) % 16 == 0 &&
               (ld_cand * esize) % 16 == 0;
+  a.two = true;
   a.target = target;
   a.out = RowsOut{out->kl, out->nll_ref, out->nll_cand, out->lse_ref, out->lse_cand,
                   out->argmax_ref, out->argmax_cand};
@@ -139,9 +152,14 @@ kld_status kld_from_logits(const void *ref, const void *cand, int dtype, int64_t
   a.ev = events_of(opts);
 
   Carver c(ws);
-  RowState *part = c.take<RowState>((size_t)n * g.splits);
-  if (launch_logits_state(a, part) != hipSuccess) return KLD_EHIP;
-  if (launch_logits_finalize(a, part) != hipSuccess) return KLD_EHIP;
+  const LogitsWs w = logits_carve(n, v, topk != nullptr, &c);
+  if (launch_logits_state(a, w.part, w.keys) != hipSuccess) return KLD_EHIP;
+  if (launch_logits_finalize(a, w.part, w.lse, nullptr) != hipSuccess) return KLD_EHIP;
+  if (topk) {
+    const TopkOut to{topk->ids_ref, topk->lp_ref, topk->ids_cand, topk->lp_cand};
+    if (launch_topk_merge(w.keys, g.splits, 2, n, w.lse, to, a.stream) != hipSuccess)
+      return KLD_EHIP;
+  }
   return KLD_OK;
 }
 
@@ -181,17 +199,45 @@ kld_status kld_fused_head(const uint16_t *W, int64_t v, int64_t d, const uint16_
 kld_status topk_export(const void *logits, int dtype, int64_t n, int64_t v, int64_t ld, int k,
                        int32_t *ids, uint16_t *lp, const int32_t *target, float *target_lp,
                        void *ws, size_t ws_bytes, void *stream) {
-  (void)logits; (void)dtype; (void)n; (void)v; (void)ld; (void)k; (void)ids; (void)lp;
-  (void)target; (void)target_lp; (void)ws; (void)ws_bytes; (void)stream;
-  return KLD_EUNSUPPORTED;
+  if (dtype != KLD_F32 && dtype != KLD_BF16) return KLD_EDTYPE;
+  if (n < 0 || v < 0) return KLD_EINVAL;
+  if (k != KLD_TOPK) return KLD_ESHAPE;
+  if (n == 0) return KLD_OK;
+  if (v < KLD_TOPK || v > 0x7fffffffLL || ld < v) return KLD_ESHAPE;
+  if (!logits || !ids || !lp) return KLD_EINVAL;
+  if (target_lp && !target) return KLD_EINVAL;
+  if (!ws || ws_bytes < kld_workspace_size(KLD_OP_TOPK_EXPORT, n, v, 0, KLD_FLAG_TOPK))
+    return KLD_EWORKSPACE;
+  const size_t esize = dtype == KLD_F32 ? 4 : 2;
+  const LogitsGeom g = logits_geom(n, v);
+  LogitsArgs a;
+  a.ref = logits; a.cand = logits; a.dtype = dtype; a.n = n; a.v = v;
+  a.ld_ref = ld; a.ld_cand = ld; a.chunk = g.chunk; a.splits = g.splits;
+  a.aligned = aligned16(logits) && (ld * esize) % 16 == 0;
+  a.two = false;
+  a.target = target;
+  a.out = RowsOut{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  a.stream = as_stream(stream);
+  Carver c(ws);
+  const LogitsWs w = logits_carve(n, v, true, &c);
+  if (launch_logits_state(a, w.part, w.keys) != hipSuccess) return KLD_EHIP;
+  if (launch_logits_finalize(a, w.part, w.lse, target_lp) != hipSuccess) return KLD_EHIP;
+  const TopkOut to{ids, lp, nullptr, nullptr};
+  if (launch_topk_merge(w.keys, g.splits, 1, n, w.lse, to, a.stream) != hipSuccess) return KLD_EHIP;
+  return KLD_OK;
 }
 
 kld_status kld_topk_tail(const int32_t *ids_p, const uint16_t *lp_p, const int32_t *ids_q,
                          const uint16_t *lp_q, int64_t n, int k, int64_t v, float *kl_tail,
                          void *stream) {
-  (void)ids_p; (void)lp_p; (void)ids_q; (void)lp_q; (void)n; (void)k; (void)v; (void)kl_tail;
-  (void)stream;
-  return KLD_EUNSUPPORTED;
+  if (n < 0 || v < 0) return KLD_EINVAL;
+  if (k != KLD_TOPK) return KLD_ESHAPE;
+  if (n == 0) return KLD_OK;
+  if (v <= KLD_TOPK || v > 0x7fffffffLL) return KLD_ESHAPE;
+  if (!ids_p || !lp_p || !ids_q || !lp_q || !kl_tail) return KLD_EINVAL;
+  if (launch_topk_tail(ids_p, lp_p, ids_q, lp_q, n, v, kl_tail, as_stream(stream)) != hipSuccess)
+    return KLD_EHIP;
+  return KLD_OK;
 }
 
 kld_status kld_summary(const float *kl, const int32_t *argmax_ref, const int32_t *argmax_cand,

@@ -137,6 +137,42 @@ __device__ inline RowResult finish(const RowState &s) {
   return r;
 }
 
+// ---- top-k keys ------------------------------------------------------------
+// A 64-bit key per (value, id): order-preserving bits of the value in the high
+// word (-0 folded onto +0), the complemented id in the low word, so a larger
+// key means a larger value, and among equal values the lower id.
+__device__ __forceinline__ uint32_t ord32(float x) {
+  const uint32_t b = __float_as_uint(x + 0.0f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ uint64_t topk_key(float x, int id) {
+  return ((uint64_t)ord32(x) << 32) | (uint64_t)(~(uint32_t)id);
+}
+__device__ __forceinline__ float key_value(uint64_t k) {
+  const uint32_t o = (uint32_t)(k >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+__device__ __forceinline__ int key_id(uint64_t k) { return (int)(~(uint32_t)k); }
+
+// Block-wide bitonic sort, descending, of buf[0, n) (LDS), n a power of two;
+// NT = threads in the block.  Every thread of the block must call it.
+template <int NT>
+__device__ void bitonic_desc(uint64_t *buf, int n) {
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n; i += NT) {
+        const int p = i ^ j;
+        if (p > i) {
+          const uint64_t a = buf[i], b = buf[p];
+          const bool first_half = (i & k) == 0;
+          if (first_half ? (a < b) : (a > b)) { buf[i] = b; buf[p] = a; }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t u) {
   return __uint_as_float(((uint32_t)u) << 16);
 }

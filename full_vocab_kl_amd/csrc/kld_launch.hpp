@@ -34,14 +34,27 @@ struct LogitsArgs {
   int64_t chunk;          // ids per split (multiple of the vector width)
   int splits;
   bool aligned;           // both row sets 16-byte aligned
+  bool two;               // both sides (false: reference only, top-k export)
   const int32_t *target;
   RowsOut out;
   hipStream_t stream;
   Events ev;
 };
 int logits_vec_elems(int dtype);
-hipError_t launch_logits_state(const LogitsArgs &a, RowState *part);
-hipError_t launch_logits_finalize(const LogitsArgs &a, const RowState *part);
+// topk_keys: NULL, or [n][splits][2][64] per-split best keys (sorted, 0-padded)
+hipError_t launch_logits_state(const LogitsArgs &a, RowState *part, uint64_t *topk_keys);
+// lse_d: NULL or [2][n] f64 log-sum-exp; target_lp: NULL or [n] ref log-prob of the target
+hipError_t launch_logits_finalize(const LogitsArgs &a, const RowState *part, double *lse_d,
+                                  float *target_lp);
+
+// ---- top-k merge and tail KLD -----------------------------------------------
+constexpr int kTopkMergeMax = 4096;   // splits * 64 candidate keys per row and side
+constexpr int kMaxSplits = kTopkMergeMax / 64;
+hipError_t launch_topk_merge(const uint64_t *keys, int splits, int nsides, int64_t n,
+                             const double *lse_d, const TopkOut &out, hipStream_t stream);
+hipError_t launch_topk_tail(const int32_t *ids_p, const uint16_t *lp_p, const int32_t *ids_q,
+                            const uint16_t *lp_q, int64_t n, int64_t v, float *kl_tail,
+                            hipStream_t stream);
 
 // ---- fused head path ------------------------------------------------------
 struct FusedArgs {

@@ -92,3 +92,28 @@ def test_summary_validation_fails_closed():
     assert call(wsb=10) == 4
     assert call(n=-1) == 1
     assert call(n=0) == 0
+
+
+def test_topk_and_tail_validation_fails_closed():
+    lib = kld.lib()
+    # topk_export(logits, dtype, n, v, ld, k, ids, lp, target, target_lp, ws, ws_bytes, stream)
+    ok = dict(logits=16, dtype=0, n=4, v=100, ld=100, k=64, ids=16, lp=16, target=None, tlp=None,
+              ws=16, wsb=1 << 30)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return lib.topk_export(a["logits"], a["dtype"], a["n"], a["v"], a["ld"], a["k"], a["ids"],
+                               a["lp"], a["target"], a["tlp"], a["ws"], a["wsb"], None)
+    assert call(k=32) == 2
+    assert call(v=63, ld=63) == 2
+    assert call(ld=99) == 2
+    assert call(dtype=5) == 3
+    assert call(ids=None) == 1
+    assert call(tlp=16) == 1
+    assert call(ws=None) == 4
+    assert call(n=0) == 0
+    # kld_topk_tail(ids_p, lp_p, ids_q, lp_q, n, k, v, kl_tail, stream)
+    assert lib.kld_topk_tail(16, 16, 16, 16, 4, 63, 1000, 16, None) == 2
+    assert lib.kld_topk_tail(16, 16, 16, 16, 4, 64, 64, 16, None) == 2
+    assert lib.kld_topk_tail(None, 16, 16, 16, 4, 64, 1000, 16, None) == 1
+    assert lib.kld_topk_tail(16, 16, 16, 16, 0, 64, 1000, 16, None) == 0
