@@ -74,11 +74,19 @@ size_t logits_workspace(int64_t n, int64_t v, int flags, Carver *c) {
   return round_up(c->used, kAlign);
 }
 
-size_t fused_workspace(int64_t n, int64_t v, int flags, Carver *c) {
-  (void)flags;
+FusedWs fused_carve(int64_t n, int64_t v, bool topk, Carver *c) {
   const FusedGeom g = fused_geom(n, v);
-  c->take<float>((size_t)7 * g.nvt * g.npad);
-  c->take<float>((size_t)2 * n);
+  FusedWs w;
+  w.part = c->take<float>((size_t)7 * g.nvt * g.npad);
+  w.zt = c->take<float>((size_t)2 * n);
+  w.lse = c->take<double>((size_t)2 * n);
+  w.ckeys = topk ? c->take<uint64_t>((size_t)2 * g.nvt * g.npad * 16) : nullptr;
+  w.resid = topk ? c->take<float>((size_t)2 * g.nvt * g.npad) : nullptr;
+  return w;
+}
+
+size_t fused_workspace(int64_t n, int64_t v, int flags, Carver *c) {
+  fused_carve(n, v, (flags & KLD_FLAG_TOPK) != 0, c);
   return round_up(c->used, kAlign);
 }
 
@@ -175,24 +183,21 @@ kld_status kld_fused_head(const uint16_t *W, int64_t v, int64_t d, const uint16_
   if ((out->nll_ref || out->nll_cand) && !target) return KLD_EINVAL;
   if (d % 8 != 0 || !aligned16(W) || !aligned16(h_ref) || !aligned16(h_cand))
     return KLD_EUNSUPPORTED;
-  if (topk) {
-    if (v < KLD_TOPK) return KLD_ESHAPE;
-    return KLD_EUNSUPPORTED;
-  }
+  if (topk && v < KLD_TOPK) return KLD_ESHAPE;
   const size_t need = kld_workspace_size(KLD_OP_FUSED_HEAD, n, v, d, topk ? KLD_FLAG_TOPK : 0);
   if (!ws || ws_bytes < need) return KLD_EWORKSPACE;
 
-  const FusedGeom g = fused_geom(n, v);
   Carver c(ws);
-  float *part = c.take<float>((size_t)7 * g.nvt * g.npad);
-  float *zt = c.take<float>((size_t)2 * n);
+  const FusedWs w = fused_carve(n, v, topk != nullptr, &c);
   FusedArgs a;
   a.W = W; a.h_ref = h_ref; a.h_cand = h_cand; a.v = v; a.d = d; a.n = n; a.target = target;
   a.out = RowsOut{out->kl, out->nll_ref, out->nll_cand, out->lse_ref, out->lse_cand,
                   out->argmax_ref, out->argmax_cand};
+  a.topk = topk ? TopkOut{topk->ids_ref, topk->lp_ref, topk->ids_cand, topk->lp_cand}
+                : TopkOut{nullptr, nullptr, nullptr, nullptr};
   a.stream = as_stream(stream);
   a.ev = events_of(opts);
-  if (launch_fused(a, part, zt) != hipSuccess) return KLD_EHIP;
+  if (launch_fused(a, w) != hipSuccess) return KLD_EHIP;
   return KLD_OK;
 }
 

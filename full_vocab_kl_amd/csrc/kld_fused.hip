@@ -60,10 +60,12 @@ __device__ __forceinline__ int logical_block(int b, int nb) {
   return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + slot;
 }
 
+template <bool TOPK>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restrict__ Hr,
                        const uint16_t *__restrict__ Hc, int64_t v, int64_t d, int64_t n, int npt,
-                       int64_t npad, int64_t nvt, float *__restrict__ part) {
+                       int64_t npad, int64_t nvt, float *__restrict__ part,
+                       uint64_t *__restrict__ ckeys, float *__restrict__ resid) {
   extern __shared__ u32x4 smem[];   // [2][STAGE_CHUNKS]
 
   const int L = logical_block((int)blockIdx.x, (int)gridDim.x);
@@ -157,9 +159,16 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
 
   // ---- epilogue: lane holds position p0 + wp*64 + pg*32 + (lane & 31) and
   // vocabulary ids vb + 32 vs + 8 (i / 4) + (i % 4), vb = v0 + 128 wv + 4 (lane >> 5).
+  // Each (lane, vs) holds a group of 16 ids of one position.  Per side and
+  // group: the maximum m1 with its lowest id and the second largest value m2.
+  // The row maximum and argmax come from the group maxima.  With top-k, every
+  // group maximum is written as a candidate key and the tile's residual --
+  // the largest m2 over its 16 groups -- bounds every id that is not a
+  // candidate.
   const int64_t vb = v0 + wv * 128 + 4 * fh;
   const bool vtail = v0 + BV > v;
-  RowState *xch = reinterpret_cast<RowState *>(smem);   // [2 pos waves][2 pg][32] states
+  RowState *xch = reinterpret_cast<RowState *>(smem);          // [2 pos waves][2 pg][32]
+  float *rx = reinterpret_cast<float *>(xch + 2 * 2 * 32);       // [2 sides][2][2][32]
 #pragma unroll
   for (int pg = 0; pg < 2; ++pg) {
     if (vtail) {
@@ -172,23 +181,34 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
             acc[vs][pg][1][i] = kNegInf;
           }
     }
-    float ma = kNegInf, mb = kNegInf;
+    float gm1[2][4], gm2[2][4];
+    int gid[2][4];
 #pragma unroll
-    for (int vs = 0; vs < 4; ++vs)
+    for (int sd = 0; sd < 2; ++sd)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        ma = fmaxf(ma, acc[vs][pg][0][i]);
-        mb = fmaxf(mb, acc[vs][pg][1][i]);
+      for (int vs = 0; vs < 4; ++vs) {
+        float m1 = kNegInf, m2 = kNegInf;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float x = acc[vs][pg][sd][i];
+          if (TOPK) m2 = fmaxf(m2, fminf(m1, x));
+          m1 = fmaxf(m1, x);
+        }
+        int id = kNoId;
+#pragma unroll
+        for (int i = 15; i >= 0; --i)
+          if (acc[vs][pg][sd][i] == m1) id = 32 * vs + 8 * (i >> 2) + (i & 3);
+        gm1[sd][vs] = m1; gm2[sd][vs] = m2; gid[sd][vs] = id;
       }
-    int ia = kNoId, ib = kNoId;
+    float ma = gm1[0][0], mb = gm1[1][0];
+    int ia = gid[0][0], ib = gid[1][0];
 #pragma unroll
-    for (int vs = 3; vs >= 0; --vs)
-#pragma unroll
-      for (int i = 15; i >= 0; --i) {
-        const int off = 32 * vs + 8 * (i >> 2) + (i & 3);
-        if (acc[vs][pg][0][i] == ma) ia = off;
-        if (acc[vs][pg][1][i] == mb) ib = off;
-      }
+    for (int vs = 1; vs < 4; ++vs) {   // groups ascend in id: strict > keeps the lowest id
+      if (gm1[0][vs] > ma) { ma = gm1[0][vs]; ia = gid[0][vs]; }
+      if (gm1[1][vs] > mb) { mb = gm1[1][vs]; ib = gid[1][vs]; }
+    }
+    if (ma == kNegInf) ia = kNoId;
+    if (mb == kNegInf) ib = kNoId;
     const float ra = ref_of(ma), rb = ref_of(mb);
     float sa = 0.f, sb = 0.f, t = 0.f;
 #pragma unroll
@@ -208,18 +228,42 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
     // lanes l and l ^ 32 hold the same position (interleaved ids)
     const RowState o = shfl_xor_state(st, 32);
     st = fh == 0 ? merge(st, o) : merge(o, st);
-    if (wv == 1 && fh == 0) xch[(wp * 2 + pg) * 32 + fr] = st;
+    const int64_t pos = p0 + wp * 64 + pg * 32 + fr;
+    float r2[2] = {kNegInf, kNegInf};
+    if constexpr (TOPK) {
+#pragma unroll
+      for (int sd = 0; sd < 2; ++sd) {
+        float r = fmaxf(fmaxf(gm2[sd][0], gm2[sd][1]), fmaxf(gm2[sd][2], gm2[sd][3]));
+        r2[sd] = fmaxf(r, __shfl_xor(r, 32));
+        if (pos < n) {
+          uint64_t *dst = ckeys + (((int64_t)sd * nvt + vt) * npad + pos) * 16 + (wv * 2 + fh) * 4;
+#pragma unroll
+          for (int vs = 0; vs < 4; ++vs)
+            dst[vs] = gm1[sd][vs] == kNegInf ? 0ull : topk_key(gm1[sd][vs], (int)(vb + gid[sd][vs]));
+        }
+      }
+    }
+    if (wv == 1 && fh == 0) {
+      xch[(wp * 2 + pg) * 32 + fr] = st;
+      if (TOPK) {
+        rx[((0 * 2 + wp) * 2 + pg) * 32 + fr] = r2[0];
+        rx[((1 * 2 + wp) * 2 + pg) * 32 + fr] = r2[1];
+      }
+    }
     __syncthreads();
-    if (wv == 0 && fh == 0) {
+    if (wv == 0 && fh == 0 && pos < n) {
       st = merge(st, xch[(wp * 2 + pg) * 32 + fr]);
-      const int64_t pos = p0 + wp * 64 + pg * 32 + fr;
-      if (pos < n) {
-        const int64_t plane = nvt * npad;
-        float *q = part + (int64_t)vt * npad + pos;
-        q[0] = st.ma; q[plane] = st.sa; q[2 * plane] = st.t; q[3 * plane] = st.mb;
-        q[4 * plane] = st.sb;
-        q[5 * plane] = __int_as_float(st.ia);
-        q[6 * plane] = __int_as_float(st.ib);
+      const int64_t plane = nvt * npad;
+      float *q = part + (int64_t)vt * npad + pos;
+      q[0] = st.ma; q[plane] = st.sa; q[2 * plane] = st.t; q[3 * plane] = st.mb;
+      q[4 * plane] = st.sb;
+      q[5 * plane] = __int_as_float(st.ia);
+      q[6 * plane] = __int_as_float(st.ib);
+      if (TOPK) {
+        resid[((int64_t)0 * nvt + vt) * npad + pos] =
+            fmaxf(r2[0], rx[((0 * 2 + wp) * 2 + pg) * 32 + fr]);
+        resid[((int64_t)1 * nvt + vt) * npad + pos] =
+            fmaxf(r2[1], rx[((1 * 2 + wp) * 2 + pg) * 32 + fr]);
       }
     }
     __syncthreads();
@@ -272,7 +316,8 @@ __global__ __launch_bounds__(256) void target_logit_kernel(
 constexpr int FP = 32, FG = 8;
 __global__ __launch_bounds__(FP * FG) void fused_finalize_kernel(
     const float *__restrict__ part, int64_t nvt, int64_t npad, int64_t n,
-    const float *__restrict__ zt, const int32_t *__restrict__ target, RowsOut out) {
+    const float *__restrict__ zt, const int32_t *__restrict__ target, RowsOut out,
+    double *__restrict__ lse_d) {
   __shared__ RowState red[FG][FP];
   const int pl = threadIdx.x % FP, g = threadIdx.x / FP;
   const int64_t pos = (int64_t)blockIdx.x * FP + pl;
@@ -292,6 +337,10 @@ __global__ __launch_bounds__(FP * FG) void fused_finalize_kernel(
   if (g == 0 && pos < n) {
     for (int i = 1; i < FG; ++i) s = merge(s, red[i][pl]);
     const RowResult r = finish(s);
+    if (lse_d) {
+      lse_d[pos] = (double)ref_of(s.ma) + log((double)s.sa);
+      lse_d[n + pos] = (double)ref_of(s.mb) + log((double)s.sb);
+    }
     out.kl[pos] = r.kl;
     if (out.lse_ref) out.lse_ref[pos] = r.lse_a;
     if (out.lse_cand) out.lse_cand[pos] = r.lse_b;
@@ -301,6 +350,147 @@ __global__ __launch_bounds__(FP * FG) void fused_finalize_kernel(
       if (out.nll_ref) out.nll_ref[pos] = (float)((double)r.lse_a - (double)zt[pos]);
       if (out.nll_cand) out.nll_cand[pos] = (float)((double)r.lse_b - (double)zt[n + pos]);
     }
+  }
+}
+
+// Exact top-64 of one (position, side) from the fused kernel's candidates.
+//
+// Candidates: for every vocabulary tile, the maximum of each of its 16
+// groups (key = value bits, then complemented id).  Every id that is not a
+// candidate is <= its tile's residual (the largest second-largest value of
+// the tile's groups).
+//  A. Radix-narrow (8 bits per pass, MSB first) the bucket that holds the
+//     64th largest candidate key until it fits the LDS buffer; gather every
+//     key at or above that bucket, sort, keep 64.  T = the 64th key.
+//  B. Any tile whose residual reaches T's value may hide an id that belongs
+//     in the top 64 (or fewer than 64 candidates exist): its 256 logits are
+//     recomputed here from W and h (f32 dot products), its old candidates
+//     are dropped, and the running top 64 is re-cut.  On generic inputs no
+//     tile is flagged; degenerate inputs (exact ties across many ids) only
+//     cost time.
+//  C. Write ids and fp16 log-probs lp = z - lse.
+constexpr int TK = 256;
+constexpr int kSelBuf = 4096;
+__global__ __launch_bounds__(TK) void fused_topk_kernel(
+    const uint64_t *__restrict__ ckeys, const float *__restrict__ resid, int64_t nvt, int64_t npad,
+    int64_t n, const uint16_t *__restrict__ W, const uint16_t *__restrict__ Hr,
+    const uint16_t *__restrict__ Hc, int64_t v, int64_t d, const double *__restrict__ lse_d,
+    TopkOut out) {
+  const int64_t pos = blockIdx.x >> 1;
+  const int side = blockIdx.x & 1;
+  int32_t *ids = side ? out.ids_cand : out.ids_ref;
+  uint16_t *lp = side ? out.lp_cand : out.lp_ref;
+  if ((!ids && !lp) || pos >= n) return;
+
+  __shared__ uint32_t hist[256];
+  __shared__ uint64_t buf[kSelBuf];
+  __shared__ uint64_t sh_prefix;
+  __shared__ int sh_pbits, sh_need, sh_cnt, sh_fill, sh_nflag;
+  __shared__ int flagged[TK];
+
+  const uint64_t *base = ckeys + ((int64_t)side * nvt * npad + pos) * 16;
+  const int64_t total = nvt * 16;
+  const int64_t tstride = npad * 16;
+  const int tid = threadIdx.x;
+
+  // ---- A: narrow the bucket of the 64th largest candidate key
+  uint64_t prefix = 0;
+  int pbits = 0, need = 64;
+  for (;;) {
+    hist[tid] = 0;
+    __syncthreads();
+    for (int64_t i = tid; i < total; i += TK) {
+      const uint64_t k = base[(i >> 4) * tstride + (i & 15)];
+      if (pbits == 0 || (k >> (64 - pbits)) == prefix) atomicAdd(&hist[(k >> (56 - pbits)) & 255], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int cum = 0, dd = 0;
+      for (dd = 255; dd > 0; --dd) {
+        if (cum + (int)hist[dd] >= need) break;
+        cum += (int)hist[dd];
+      }
+      sh_need = need - cum;
+      sh_prefix = (prefix << 8) | (uint64_t)dd;
+      sh_pbits = pbits + 8;
+      sh_cnt = (int)hist[dd];
+    }
+    __syncthreads();
+    prefix = sh_prefix; pbits = sh_pbits; need = sh_need;
+    const int cnt = sh_cnt;
+    __syncthreads();
+    if (pbits == 64 || cnt <= kSelBuf - 64) break;
+  }
+  // gather every key whose top pbits reach the bucket
+  if (tid == 0) sh_fill = 0;
+  __syncthreads();
+  for (int64_t i = tid; i < total; i += TK) {
+    const uint64_t k = base[(i >> 4) * tstride + (i & 15)];
+    if ((pbits == 64 ? k : (k >> (64 - pbits))) >= prefix && k != 0ull) {
+      const int slot = atomicAdd(&sh_fill, 1);
+      buf[slot] = k;
+    }
+  }
+  __syncthreads();
+  {
+    const int fill = sh_fill;
+    int m = 64;
+    while (m < fill) m <<= 1;
+    for (int i = fill + tid; i < m; i += TK) buf[i] = 0ull;
+    __syncthreads();
+    bitonic_desc<TK>(buf, m);
+  }
+  const uint64_t T = buf[63];
+  const float tval = key_value(T);
+
+  // ---- B: recompute tiles whose residual reaches T (all tiles if T is unset)
+  const uint16_t *h = (side ? Hc : Hr) + pos * d;
+  for (int64_t r0 = 0; r0 < nvt; r0 += TK) {
+    if (tid == 0) sh_nflag = 0;
+    __syncthreads();
+    const int64_t vt = r0 + tid;
+    if (vt < nvt && (T == 0ull || resid[((int64_t)side * nvt + vt) * npad + pos] >= tval))
+      flagged[atomicAdd(&sh_nflag, 1)] = (int)vt;
+    __syncthreads();
+    const int nf = sh_nflag;
+    for (int f = 0; f < nf; ++f) {
+      const int64_t t0 = (int64_t)flagged[f] * BV;   // the tile's first id
+      // drop the tile's old candidates from the running top 64
+      if (tid < 64) {
+        const int id = key_id(buf[tid]);
+        if (buf[tid] != 0ull && id >= t0 && id < t0 + BV) buf[tid] = 0ull;
+      }
+      // its 256 logits, one per thread
+      const int64_t j = t0 + tid;
+      uint64_t k = 0ull;
+      if (j < v) {
+        const uint16_t *w = W + j * d;
+        float z = 0.f;
+        for (int64_t e = 0; e < d; e += 8) {
+          const u32x4 qw = *reinterpret_cast<const u32x4 *>(w + e);
+          const u32x4 qh = *reinterpret_cast<const u32x4 *>(h + e);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            z = fmaf(__uint_as_float(qw[q] << 16), __uint_as_float(qh[q] << 16), z);
+            z = fmaf(__uint_as_float(qw[q] & 0xffff0000u), __uint_as_float(qh[q] & 0xffff0000u), z);
+          }
+        }
+        k = topk_key(z, (int)j);
+      }
+      buf[64 + tid] = k;
+      for (int i = 64 + TK + tid; i < 512; i += TK) buf[i] = 0ull;
+      __syncthreads();
+      bitonic_desc<TK>(buf, 512);
+    }
+    __syncthreads();
+  }
+
+  // ---- C: ids and log-probs
+  if (tid < 64) {
+    const uint64_t k = buf[tid];
+    const double l = lse_d[(int64_t)side * n + pos];
+    if (ids) ids[pos * 64 + tid] = key_id(k);
+    if (lp) lp[pos * 64 + tid] = f32_to_f16_bits((float)((double)key_value(k) - l));
   }
 }
 
@@ -314,32 +504,42 @@ FusedGeom fused_geom(int64_t n, int64_t v) {
   return g;
 }
 
-hipError_t launch_fused(const FusedArgs &a, float *part, float *zt) {
+hipError_t launch_fused(const FusedArgs &a, const FusedWs &w) {
   const FusedGeom g = fused_geom(a.n, a.v);
+  const bool tk = a.topk.ids_ref || a.topk.lp_ref || a.topk.ids_cand || a.topk.lp_cand;
+  const void *kern = tk ? (const void *)fused_head_kernel<true> : (const void *)fused_head_kernel<false>;
   // 128 KB of LDS per block (above the 64 KB default): set on every call so
   // that no library state is kept; the call is host-side and cheap.
-  hipError_t e = hipFuncSetAttribute((const void *)fused_head_kernel,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+  hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      2 * STAGE_CHUNKS * (int)sizeof(u32x4));
   if (e != hipSuccess) return e;
   const int64_t nblocks = g.nvt * g.npt;
   e = record(a.ev.start, a.stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fused_head_kernel, dim3((unsigned)nblocks), dim3(NT),
-                     2 * STAGE_CHUNKS * sizeof(u32x4), a.stream, a.W, a.h_ref, a.h_cand, a.v, a.d,
-                     a.n, (int)g.npt, g.npad, g.nvt, part);
+  if (tk)
+    hipLaunchKernelGGL(fused_head_kernel<true>, dim3((unsigned)nblocks), dim3(NT),
+                       2 * STAGE_CHUNKS * sizeof(u32x4), a.stream, a.W, a.h_ref, a.h_cand, a.v, a.d,
+                       a.n, (int)g.npt, g.npad, g.nvt, w.part, w.ckeys, w.resid);
+  else
+    hipLaunchKernelGGL(fused_head_kernel<false>, dim3((unsigned)nblocks), dim3(NT),
+                       2 * STAGE_CHUNKS * sizeof(u32x4), a.stream, a.W, a.h_ref, a.h_cand, a.v, a.d,
+                       a.n, (int)g.npt, g.npad, g.nvt, w.part, nullptr, nullptr);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = record(a.ev.stop, a.stream);
   if (e != hipSuccess) return e;
   if (a.target) {
     hipLaunchKernelGGL(target_logit_kernel, dim3((unsigned)((a.n + 3) / 4)), dim3(256), 0,
-                       a.stream, a.W, a.h_ref, a.h_cand, a.v, a.d, a.n, a.target, zt);
+                       a.stream, a.W, a.h_ref, a.h_cand, a.v, a.d, a.n, a.target, w.zt);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(fused_finalize_kernel, dim3((unsigned)((a.n + FP - 1) / FP)), dim3(FP * FG), 0,
-                     a.stream, part, g.nvt, g.npad, a.n, zt, a.target, a.out);
+                     a.stream, w.part, g.nvt, g.npad, a.n, w.zt, a.target, a.out, w.lse);
+  e = hipGetLastError();
+  if (e != hipSuccess || !tk) return e;
+  hipLaunchKernelGGL(fused_topk_kernel, dim3((unsigned)(2 * a.n)), dim3(TK), 0, a.stream, w.ckeys,
+                     w.resid, g.nvt, g.npad, a.n, a.W, a.h_ref, a.h_cand, a.v, a.d, w.lse, a.topk);
   return hipGetLastError();
 }
 

@@ -62,6 +62,7 @@ struct FusedArgs {
   int64_t v, d, n;
   const int32_t *target;
   RowsOut out;
+  TopkOut topk;           // all NULL: no top-k export
   hipStream_t stream;
   Events ev;
 };
@@ -69,8 +70,14 @@ struct FusedGeom {
   int64_t nvt, npt, npad;   // vocabulary tiles, position tiles, padded positions
 };
 FusedGeom fused_geom(int64_t n, int64_t v);
-// part: 7 * nvt * npad floats; zt: 2 * n floats (used when a target is given)
-hipError_t launch_fused(const FusedArgs &a, float *part, float *zt);
+struct FusedWs {
+  float *part;        // 7 * nvt * npad partial-state planes
+  float *zt;          // 2 * n target logits
+  double *lse;        // 2 * n log-sum-exp (top-k only)
+  uint64_t *ckeys;    // 2 * nvt * npad * 16 candidate keys (top-k only)
+  float *resid;       // 2 * nvt * npad tile residuals (top-k only)
+};
+hipError_t launch_fused(const FusedArgs &a, const FusedWs &w);
 
 // ---- summary ---------------------------------------------------------------
 constexpr int kSummaryMaxRanks = 32;   // two order statistics per quantile, <= 16 quantiles
