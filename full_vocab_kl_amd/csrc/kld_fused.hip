@@ -11,8 +11,10 @@
 // every lane's accumulators hold one position and 16 vocabulary ids, and the
 // per-position reduction over the vocabulary is mostly lane-local.  Reference
 // and candidate columns of the same position sit in the same lane and
-// register slot.  Operands are staged through LDS (double-buffered, 16-byte
-// chunks with an XOR swizzle so fragment reads spread over the banks).
+// register slot.  Operands stream straight from global memory into a
+// 4-stage LDS ring (global_load_lds, 16 bytes per lane; three stages in
+// flight while one is consumed), 64-byte rows with an XOR swizzle so
+// fragment reads spread over the banks.
 //
 // Epilogue: the block's 256 x 128 tile of (a, b) pairs is folded into one
 // RowState per position (kld_device.hpp) and written as a partial state for
@@ -37,20 +39,36 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BV = 256;            // vocabulary ids per block
 constexpr int BP = 128;            // positions per block (x2 sides = 256 B columns)
-constexpr int BK = 64;             // hidden elements per pipeline stage
+constexpr int BK = 32;             // hidden elements per pipeline stage
+constexpr int NSTAGE = 4;          // stages in the LDS ring (3 in flight while one is consumed)
 constexpr int NT = 256;            // threads per block (4 waves: 2 vocab x 2 position)
-constexpr int CH = BK / 8;         // 16-byte chunks per staged row
+constexpr int CH = BK / 8;         // 16-byte chunks per staged row (64-byte rows)
 constexpr int ROWS = BV + 2 * BP;  // staged rows per stage (head rows, then ref, then cand)
-constexpr int STAGE_CHUNKS = ROWS * CH;
-constexpr int LOADS = ROWS * CH / NT;   // 16-byte global loads per thread per stage
+constexpr int STAGE_CHUNKS = ROWS * CH;                  // 2048 chunks = 32 KB
+constexpr int ROWS_PER_LOAD = 64 / CH;                   // rows one wave-wide 16-byte load covers
+constexpr int LOADS = ROWS / ROWS_PER_LOAD / (NT / 64);  // wave-wide loads per wave per stage
 constexpr int kXcds = 8;
+constexpr size_t kFusedLds = (size_t)NSTAGE * STAGE_CHUNKS * 16;
 
-static_assert(LOADS == 16, "tile shape");
+static_assert(LOADS == 8, "tile shape");
 
-// Swizzled position of chunk c of staged row r.  Rows are 128 bytes; the
-// chunk index is XORed with (r ^ r >> 3) & 7 so that 8 consecutive rows (and
-// the even or odd rows among 16) read at one logical chunk hit distinct banks.
-__device__ __forceinline__ int swz(int r, int c) { return r * CH + (c ^ ((r ^ (r >> 3)) & 7)); }
+// Swizzled position of chunk c of staged row r.  Rows are 64 bytes (4
+// chunks); XORing the chunk with ((r >> 1) ^ (r >> 3)) & 3 makes the 16-byte
+// fragment reads of 8 (or 16) consecutive rows at one logical chunk fall on
+// distinct banks.
+__device__ __forceinline__ int swz(int r, int c) { return r * CH + (c ^ (((r >> 1) ^ (r >> 3)) & 3)); }
+
+// Workgroup execution barrier without the memory fence of __syncthreads();
+// the memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt immediate that waits until at most `vm` vector-memory operations
+// of this wave are outstanding (expcnt and lgkmcnt left unconstrained).
+template <int vm>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(vm >= 0 && vm < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 // Map the hardware block id to a logical tile id so that each XCD gets a
 // contiguous range of logical ids.
@@ -66,7 +84,7 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
                        const uint16_t *__restrict__ Hc, int64_t v, int64_t d, int64_t n, int npt,
                        int64_t npad, int64_t nvt, float *__restrict__ part,
                        uint64_t *__restrict__ ckeys, float *__restrict__ resid) {
-  extern __shared__ u32x4 smem[];   // [2][STAGE_CHUNKS]
+  extern __shared__ u32x4 smem[];   // [NSTAGE][STAGE_CHUNKS]
 
   const int L = logical_block((int)blockIdx.x, (int)gridDim.x);
   const int vt = L / npt, pt = L % npt;
@@ -74,44 +92,44 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wv = wave >> 1, wp = wave & 1;
 
-  // ---- global -> register staging: thread loads chunk (tid % 8) of staged
-  // rows tid / 8 + 32 j, j = 0..15 (rows 0..255 head, 256..383 ref, 384..511 cand).
-  const int lc = tid & 7, lr = tid >> 3;
-  const uint16_t *src[LOADS];
+  // ---- global -> LDS staging.  Wave w fills staged rows 16 (8 w + j) ..
+  // 16 (8 w + j) + 15, j = 0..7, with one wave-wide 16-byte load each: lane i
+  // lands at LDS chunk 64 (8 w + j) + i of the stage, i.e. row 16 (8 w + j) +
+  // i / 4, physical chunk i % 4, so it fetches the row's logical chunk
+  // (i % 4) ^ swizzle(row).  Rows 0..255 are head rows, 256..383 reference
+  // hidden rows, 384..511 candidate hidden rows.  Rows past v or n read a
+  // clamped valid row: their results are masked or discarded.
+  const uint16_t *src[LOADS];   // row starts
+  int coff[LOADS];               // element offset of this lane's chunk within a stage
 #pragma unroll
   for (int j = 0; j < LOADS; ++j) {
-    const int r = lr + 32 * j;
+    const int r = 16 * (8 * wave + j) + (lane >> 2);
+    coff[j] = 8 * ((lane & 3) ^ (((r >> 1) ^ (r >> 3)) & 3));
     if (r < BV) {
       const int64_t vr = v0 + r;
-      src[j] = W + (vr < v ? vr : v - 1) * d + lc * 8;
+      src[j] = W + (vr < v ? vr : v - 1) * d;
     } else {
       const int hr = r - BV;
       const int64_t pos = p0 + (hr & (BP - 1));
-      src[j] = (hr < BP ? Hr : Hc) + (pos < n ? pos : n - 1) * d + lc * 8;
+      src[j] = (hr < BP ? Hr : Hc) + (pos < n ? pos : n - 1) * d;
     }
   }
-  u32x4 stage[LOADS];
   const int KT = (int)((d + BK - 1) / BK);
+  const bool ktail = (d % BK) != 0;
 
-  // Rows beyond v or n read a valid clamped row: their results are masked or
-  // discarded.  Only hidden elements beyond d must read as zero, which can
-  // happen in the last stage alone.
-  auto load_stage = [&](int kt) {
-    const int64_t k = (int64_t)kt * BK + lc * 8;
-    if (k < d) {
+  // Issue stage kt into ring slot kt % NSTAGE.
+  auto issue = [&](int kt) {
+    u32x4 *dst = smem + (kt % NSTAGE) * STAGE_CHUNKS + (8 * wave) * 64;
 #pragma unroll
-      for (int j = 0; j < LOADS; ++j)
-        stage[j] = *reinterpret_cast<const u32x4 *>(src[j] + (int64_t)kt * BK);
-    } else {
-#pragma unroll
-      for (int j = 0; j < LOADS; ++j) stage[j] = u32x4{0u, 0u, 0u, 0u};
+    for (int j = 0; j < LOADS; ++j) {
+      const int64_t k = (int64_t)kt * BK + coff[j];
+      const uint16_t *g = src[j] + (k < d ? k : 0);   // past d: an in-bounds dummy, zeroed later
+      __builtin_amdgcn_global_load_lds((const void *)g,
+                                       (__attribute__((address_space(3))) void *)(dst + j * 64),
+                                       16, 0, 0);
     }
   };
-  auto store_stage = [&](int buf) {
-    u32x4 *s = smem + buf * STAGE_CHUNKS;
-#pragma unroll
-    for (int j = 0; j < LOADS; ++j) s[swz(lr + 32 * j, lc)] = stage[j];
-  };
+
 
   f32x16 acc[4][2][2];
 #pragma unroll
@@ -123,39 +141,92 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[a][b][c][i] = 0.f;
 
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-
   const int fr = lane & 31, fh = lane >> 5;
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) load_stage(kt + 1);
-    const u32x4 *s = smem + cur * STAGE_CHUNKS;
+  // fragments of one 16-wide K step: 4 head (A) and 2 x 2 hidden (B) operands
+  struct Frags {
+    bf16x8 a[4], b[2][2];
+  };
+  auto load_frags = [&](int slot, int ks, Frags &f) {
+    const u32x4 *sbuf = smem + slot * STAGE_CHUNKS;
+    const int c = 2 * ks + fh;
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int c = 2 * ks + fh;
-      bf16x8 fa[4], fb[2][2];
+    for (int pg = 0; pg < 2; ++pg)
 #pragma unroll
-      for (int vs = 0; vs < 4; ++vs)
-        fa[vs] = __builtin_bit_cast(bf16x8, s[swz(wv * 128 + vs * 32 + fr, c)]);
+      for (int sd = 0; sd < 2; ++sd)
+        f.b[pg][sd] = __builtin_bit_cast(bf16x8, sbuf[swz(BV + sd * BP + wp * 64 + pg * 32 + fr, c)]);
+#pragma unroll
+    for (int vs = 0; vs < 4; ++vs)
+      f.a[vs] = __builtin_bit_cast(bf16x8, sbuf[swz(wv * 128 + vs * 32 + fr, c)]);
+  };
+  auto mfma = [&](const Frags &f) {
+#pragma unroll
+    for (int vs = 0; vs < 4; ++vs)
 #pragma unroll
       for (int pg = 0; pg < 2; ++pg)
 #pragma unroll
         for (int sd = 0; sd < 2; ++sd)
-          fb[pg][sd] = __builtin_bit_cast(bf16x8, s[swz(BV + sd * BP + wp * 64 + pg * 32 + fr, c)]);
+          acc[vs][pg][sd] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[vs], f.b[pg][sd], acc[vs][pg][sd], 0, 0, 0);
+  };
+  // Hidden elements past d (the last stage of a width that is not a multiple
+  // of BK) were fetched from clamped in-bounds addresses; zero both operands.
+  auto mask_tail = [&](Frags &f, int kt, int ks) {
+    if ((int64_t)kt * BK + ks * 16 + 8 * fh >= d) {
+      const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
-      for (int vs = 0; vs < 4; ++vs)
+      for (int vs = 0; vs < 4; ++vs) f.a[vs] = z;
 #pragma unroll
-        for (int pg = 0; pg < 2; ++pg)
+      for (int pg = 0; pg < 2; ++pg)
 #pragma unroll
-          for (int sd = 0; sd < 2; ++sd)
-            acc[vs][pg][sd] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[vs], fb[pg][sd], acc[vs][pg][sd], 0, 0, 0);
+        for (int sd = 0; sd < 2; ++sd) f.b[pg][sd] = z;
     }
-    if (kt + 1 < KT) store_stage(cur ^ 1);
-    __syncthreads();
+  };
+
+  // Software pipeline (per wave).  Iteration kt runs the 16 MFMAs of K step 0
+  // of stage kt while the K step 1 fragments of stage kt load; then, once
+  // stage kt + 1 has landed and every wave has passed the barrier, it issues
+  // the global loads of stage kt + 4 into the slot stage kt just vacated and
+  // runs the 16 MFMAs of K step 1 while the K step 0 fragments of stage
+  // kt + 1 load.  Three stages stay in flight (past the end, stage loads read
+  // clamped in-bounds addresses into free slots, which keeps the loop free of
+  // branches); the barrier is the only point where waves synchronise.
+  Frags f0, f1;
+#pragma unroll
+  for (int s0 = 0; s0 < NSTAGE - 1; ++s0) issue(s0);
+  wait_vmcnt<(NSTAGE - 2) * LOADS>();
+  block_barrier();
+  issue(NSTAGE - 1);
+  load_frags(0, 0, f0);
+  for (int kt = 0; kt + 1 < KT; ++kt) {
+    load_frags(kt % NSTAGE, 1, f1);
+    mfma(f0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    wait_vmcnt<(NSTAGE - 2) * LOADS>();   // stage kt + 1 has landed
+    block_barrier();
+    issue(kt + NSTAGE);
+    load_frags((kt + 1) % NSTAGE, 0, f0);
+    mfma(f1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one global->LDS load
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   }
+  {   // last stage
+    const int kt = KT - 1;
+    load_frags(kt % NSTAGE, 1, f1);
+    if (ktail) { mask_tail(f0, kt, 0); mask_tail(f1, kt, 1); }
+    mfma(f0);
+    mfma(f1);
+  }
+  __syncthreads();   // all fragment reads done before the epilogue reuses LDS
 
   // ---- epilogue: lane holds position p0 + wp*64 + pg*32 + (lane & 31) and
   // vocabulary ids vb + 32 vs + 8 (i / 4) + (i % 4), vb = v0 + 128 wv + 4 (lane >> 5).
@@ -511,18 +582,18 @@ hipError_t launch_fused(const FusedArgs &a, const FusedWs &w) {
   // 128 KB of LDS per block (above the 64 KB default): set on every call so
   // that no library state is kept; the call is host-side and cheap.
   hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     2 * STAGE_CHUNKS * (int)sizeof(u32x4));
+                                     (int)kFusedLds);
   if (e != hipSuccess) return e;
   const int64_t nblocks = g.nvt * g.npt;
   e = record(a.ev.start, a.stream);
   if (e != hipSuccess) return e;
   if (tk)
     hipLaunchKernelGGL(fused_head_kernel<true>, dim3((unsigned)nblocks), dim3(NT),
-                       2 * STAGE_CHUNKS * sizeof(u32x4), a.stream, a.W, a.h_ref, a.h_cand, a.v, a.d,
+                       kFusedLds, a.stream, a.W, a.h_ref, a.h_cand, a.v, a.d,
                        a.n, (int)g.npt, g.npad, g.nvt, w.part, w.ckeys, w.resid);
   else
     hipLaunchKernelGGL(fused_head_kernel<false>, dim3((unsigned)nblocks), dim3(NT),
-                       2 * STAGE_CHUNKS * sizeof(u32x4), a.stream, a.W, a.h_ref, a.h_cand, a.v, a.d,
+                       kFusedLds, a.stream, a.W, a.h_ref, a.h_cand, a.v, a.d,
                        a.n, (int)g.npt, g.npad, g.nvt, w.part, nullptr, nullptr);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
