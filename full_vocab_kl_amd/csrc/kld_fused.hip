@@ -40,7 +40,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int BV = 256;            // vocabulary ids per block
 constexpr int BP = 128;            // positions per block (x2 sides = 256 B columns)
 constexpr int BK = 32;             // hidden elements per pipeline stage
-constexpr int NSTAGE = 4;          // stages in the LDS ring (3 in flight while one is consumed)
+constexpr int NSTAGE = 5;          // stages in the LDS ring
 constexpr int NT = 256;            // threads per block (4 waves: 2 vocab x 2 position)
 constexpr int CH = BK / 8;         // 16-byte chunks per staged row (64-byte rows)
 constexpr int ROWS = BV + 2 * BP;  // staged rows per stage (head rows, then ref, then cand)
@@ -53,10 +53,12 @@ constexpr size_t kFusedLds = (size_t)NSTAGE * STAGE_CHUNKS * 16;
 static_assert(LOADS == 8, "tile shape");
 
 // Swizzled position of chunk c of staged row r.  Rows are 64 bytes (4
-// chunks); XORing the chunk with ((r >> 1) ^ (r >> 3)) & 3 makes the 16-byte
-// fragment reads of 8 (or 16) consecutive rows at one logical chunk fall on
-// distinct banks.
-__device__ __forceinline__ int swz(int r, int c) { return r * CH + (c ^ (((r >> 1) ^ (r >> 3)) & 3)); }
+// chunks); the chunk index is XORed with bits 2..3 of the row.  Measured on
+// gfx950 (SQ_LDS_BANK_CONFLICT), this makes the fragment reads -- lanes 0..31
+// on 32 consecutive rows at chunk c, lanes 32..63 on the same rows at chunk
+// c + 1 -- free of bank conflicts.
+__device__ __forceinline__ int swz_key(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int swz(int r, int c) { return r * CH + (c ^ swz_key(r)); }
 
 // Workgroup execution barrier without the memory fence of __syncthreads();
 // the memory clobber keeps the compiler from moving LDS accesses across it.
@@ -104,7 +106,7 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
 #pragma unroll
   for (int j = 0; j < LOADS; ++j) {
     const int r = 16 * (8 * wave + j) + (lane >> 2);
-    coff[j] = 8 * ((lane & 3) ^ (((r >> 1) ^ (r >> 3)) & 3));
+    coff[j] = 8 * ((lane & 3) ^ swz_key(r));
     if (r < BV) {
       const int64_t vr = v0 + r;
       src[j] = W + (vr < v ? vr : v - 1) * d;
@@ -117,11 +119,11 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
   const int KT = (int)((d + BK - 1) / BK);
   const bool ktail = (d % BK) != 0;
 
-  // Issue stage kt into ring slot kt % NSTAGE.
-  auto issue = [&](int kt) {
+  // Issue loads j0 .. j0 + cnt - 1 of stage kt into ring slot kt % NSTAGE.
+  auto issue_part = [&](int kt, int j0, int cnt) {
     u32x4 *dst = smem + (kt % NSTAGE) * STAGE_CHUNKS + (8 * wave) * 64;
 #pragma unroll
-    for (int j = 0; j < LOADS; ++j) {
+    for (int j = j0; j < j0 + cnt; ++j) {
       const int64_t k = (int64_t)kt * BK + coff[j];
       const uint16_t *g = src[j] + (k < d ? k : 0);   // past d: an in-bounds dummy, zeroed later
       __builtin_amdgcn_global_load_lds((const void *)g,
@@ -129,6 +131,7 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
                                        16, 0, 0);
     }
   };
+  auto issue = [&](int kt) { issue_part(kt, 0, LOADS); };
 
 
   f32x16 acc[4][2][2];
@@ -183,41 +186,52 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
   };
 
   // Software pipeline (per wave).  Iteration kt runs the 16 MFMAs of K step 0
-  // of stage kt while the K step 1 fragments of stage kt load; then, once
-  // stage kt + 1 has landed and every wave has passed the barrier, it issues
-  // the global loads of stage kt + 4 into the slot stage kt just vacated and
-  // runs the 16 MFMAs of K step 1 while the K step 0 fragments of stage
-  // kt + 1 load.  Three stages stay in flight (past the end, stage loads read
-  // clamped in-bounds addresses into free slots, which keeps the loop free of
-  // branches); the barrier is the only point where waves synchronise.
+  // of stage kt while the K step 1 fragments of stage kt load and half of the
+  // global loads of stage kt + 4 go out; then, once stage kt + 1 has landed
+  // and every wave has passed the barrier, it runs the 16 MFMAs of K step 1
+  // while the K step 0 fragments of stage kt + 1 load and the other half of
+  // stage kt + 4 goes out.  Stage kt + 4 fills slot (kt + 4) % 5, which every
+  // wave released at the previous barrier, so the global loads spread evenly
+  // over both halves.  Past the end, stage loads read clamped in-bounds
+  // addresses into free slots, which keeps the loop free of branches; the
+  // barrier is the only point where waves synchronise.
+  static_assert(NSTAGE == 5, "the schedule below keeps four stages ahead");
   Frags f0, f1;
 #pragma unroll
   for (int s0 = 0; s0 < NSTAGE - 1; ++s0) issue(s0);
-  wait_vmcnt<(NSTAGE - 2) * LOADS>();
+  wait_vmcnt<(NSTAGE - 2) * LOADS>();   // stage 0 has landed
   block_barrier();
-  issue(NSTAGE - 1);
   load_frags(0, 0, f0);
   for (int kt = 0; kt + 1 < KT; ++kt) {
     load_frags(kt % NSTAGE, 1, f1);
+    issue_part(kt + NSTAGE - 1, 0, LOADS / 2);
     mfma(f0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    wait_vmcnt<(NSTAGE - 2) * LOADS>();   // stage kt + 1 has landed
-    block_barrier();
-    issue(kt + NSTAGE);
-    load_frags((kt + 1) % NSTAGE, 0, f0);
-    mfma(f1);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one global->LDS load
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    // stage kt + 1 has landed: outstanding are stages kt + 2, kt + 3 and half of kt + 4
+    wait_vmcnt<(NSTAGE - 3) * LOADS + LOADS / 2>();
+    block_barrier();
+    load_frags((kt + 1) % NSTAGE, 0, f0);
+    issue_part(kt + NSTAGE - 1, LOADS / 2, LOADS / 2);
+    mfma(f1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   }
   {   // last stage
     const int kt = KT - 1;
