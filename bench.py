@@ -4,10 +4,11 @@
 
 Default workload: one 2047-position window through the shared head
 (d = 5120, V = 248,320, bf16 head and hidden states, f32 softmax).  One step
-is the whole path over that window: kld_fused_head (logits, KL, argmax, NLL
-and lse of every position, both sides) followed by kld_summary (mean KL,
-top-1, perplexities, median / p99 / p99.9 KL).  Inputs are seeded synthetic
-data already resident in HBM when the timed region starts.
+is the whole path over that window: kld_fused_head (logits, KL, argmax, NLL,
+lse and the top-64 export of every position, both sides), kld_topk_tail (the
+top-64 + tail-bucket KLD from those exports) and kld_summary (mean KL, top-1,
+perplexities, median / p99 / p99.9 KL).  Inputs are seeded synthetic data
+already resident in HBM when the timed region starts.
 
 Prints one JSON line: positions/s over K timed steps, the roofline of the
 dominant kernel (its average duration from HIP events recorded around it on
@@ -41,17 +42,41 @@ def _args():
                    help="positions the CPU oracle scores for the baseline (0 = skip)")
     p.add_argument("--no-secondary", action="store_true",
                    help="skip the secondary logits-path measurement")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device copy (counter calibration)")
     return p.parse_args()
 
 
+KERNEL_SOURCES = {"fused_head_kernel<true>": "full_vocab_kl_amd/csrc/kld_fused.hip",
+                  "logits_partial_kernel_f32": "full_vocab_kl_amd/csrc/kld_logits.hip"}
+
+
 def _traffic(kernel_key):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, or None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel
+    calibration) from profiles/traffic.json, or None when missing or when the
+    kernel's source has changed since the counters were taken."""
+    import hashlib
     try:
-        with open(path) as f:
-            return json.load(f).get(kernel_key)
-    except (OSError, ValueError):
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            rec = json.load(f)["kernels"][kernel_key]
+        with open(os.path.join(ROOT, KERNEL_SOURCES[kernel_key]), "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError, KeyError):
         return None
+    return rec["bytes_per_launch"] if rec.get("source_sha256") == digest else None
+
+
+def copy_calibration(nbytes=1 << 30, reps=3):
+    """A plain device copy of known size, for scaling the FETCH_SIZE /
+    WRITE_SIZE counters (run under rocprofv3 --pmc)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
 # --------------------------------------------------------------------------
@@ -74,16 +99,18 @@ def fused_window(steps, warmup, cpu_sample):
     bf = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
     W, hr, hc = bf(w_np), bf(hr_np), bf(hc_np)
     tg = torch.from_numpy(t_np).to(dev)
-    ws = torch.empty(kld.kld_workspace_size(1, n, v, d), dtype=torch.uint8, device=dev)
+    ws = torch.empty(kld.kld_workspace_size(1, n, v, d, 1), dtype=torch.uint8, device=dev)
     ws_s = torch.empty(kld.kld_workspace_size(3, n, 0), dtype=torch.uint8, device=dev)
     summ = torch.empty(8 + len(QUANTILES), dtype=torch.float64, device=dev)
+    tail = torch.empty(n, dtype=torch.float32, device=dev)
     out = None
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
 
     def step(ev=None):
         nonlocal out
-        out = kld.kld_fused_head(W, hr, hc, tg, ws=ws, out=out, events=ev)
+        out = kld.kld_fused_head(W, hr, hc, tg, topk=True, ws=ws, events=ev, out=out)
+        kld.kld_topk_tail(out["ids_ref"], out["lp_ref"], out["ids_cand"], out["lp_cand"], v, out=tail)
         kld.kld_summary(out["kl"], out["argmax_ref"], out["argmax_cand"], out["nll_ref"],
                         out["nll_cand"], quantiles=QUANTILES, ws=ws_s, out=summ)
 
@@ -104,17 +131,19 @@ def fused_window(steps, warmup, cpu_sample):
     res = {
         "value": n * steps / elapsed, "unit": "positions/s", "ms_per_step": elapsed * 1e3 / steps,
         "dtype": "bf16",
-        "config": {"workload": "kld_fused_head + kld_summary: one window, N=2047 positions, "
-                               "d=5120, V=248,320, bf16 head W~N(0,0.02^2), hidden RMS-normalised, "
-                               "cand noise 0.01, f32 accumulate and softmax",
+        "config": {"workload": "kld_fused_head (+top-64 export) + kld_topk_tail + kld_summary: "
+                               "one window, N=2047 positions, d=5120, V=248,320, bf16 head "
+                               "W~N(0,0.02^2), hidden RMS-normalised, cand noise 0.01, f32 "
+                               "accumulate and softmax",
                    "positions": n, "d": d, "V": v},
-        "roofline": {"bound": "mfma", "kernel": "fused_head_kernel",
+        "roofline": {"bound": "mfma", "kernel": "fused_head_kernel<true>",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": _traffic("fused_head_kernel"),
+                     "traffic": _traffic("fused_head_kernel<true>"),
                      "kernel_ms": round(kernel_ms, 4),
                      "algorithmic": f"4*N*d*V = {flops:.4e} flop per launch"},
-        "result": {"mean_kl": summary["mean_kl"], "top1": summary["top1"],
+        "result": {"mean_kl": summary["mean_kl"], "mean_tail_kl": float(tail.double().mean()),
+                   "top1": summary["top1"],
                    "ppl_ref": summary["ppl_ref"], "ppl_cand": summary["ppl_cand"],
                    "p99": summary["quantiles"][0.99], "p999": summary["quantiles"][0.999]},
     }
@@ -133,11 +162,16 @@ def cpu_fused(w_np, hr_np, hc_np, t_np, m):
     t0 = time.perf_counter()
     a = oracle.head_logits(w_np, hr_np[rows])
     b = oracle.head_logits(w_np, hc_np[rows])
-    oracle.score_rows(a, b, t_np[rows])
+    s = oracle.score_rows(a, b, t_np[rows], k=64)
+    for i in range(len(rows)):
+        oracle.tail_kld_row(s["ids_ref"][i], s["lp_ref"][i], s["ids_cand"][i], s["lp_cand"][i],
+                            w_np.shape[0])
+    oracle.summarize(s["kl"], s["argmax_ref"], s["argmax_cand"], s["nll_ref"], s["nll_cand"])
     dt = time.perf_counter() - t0
     return {"value": m / dt, "unit": "positions/s", "cores": _cores(), "kind": "oracle",
             "sample": f"{m} seeded positions of the 2047-position window (head logits in f64 for "
-                      f"both sides over all 248,320 ids, then KL/argmax/NLL), {dt:.1f} s"}
+                      f"both sides over all 248,320 ids, KL/argmax/NLL, top-64 + tail KLD, "
+                      f"summary), {dt:.1f} s"}
 
 
 def logits_f32(steps, warmup, cpu_sample):
@@ -224,11 +258,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import full_vocab_kl_amd as kld
     kld.lib()   # fails loudly if libkld.so is missing
 
     if args.workload == "fused_window":
-        cpu = 48 if args.cpu_sample is None else args.cpu_sample
+        cpu = 128 if args.cpu_sample is None else args.cpu_sample
         res = fused_window(args.steps, args.warmup, cpu)
     else:
         cpu = 64 if args.cpu_sample is None else args.cpu_sample

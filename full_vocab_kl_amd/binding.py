@@ -161,6 +161,16 @@ def _rows_struct(out):
                              "argmax_cand")))
 
 
+_TOPK_KEYS = ("ids_ref", "lp_ref", "ids_cand", "lp_cand")
+
+
+def _topk_from(out, n, device):
+    """Reuse top-k buffers present in `out`, else allocate them."""
+    if out is not None and all(out.get(k) is not None for k in _TOPK_KEYS):
+        return {k: out[k] for k in _TOPK_KEYS}
+    return _alloc_topk(n, device)
+
+
 def _alloc_topk(n, device):
     return {"ids_ref": torch.empty((n, TOPK), dtype=torch.int32, device=device),
             "lp_ref": torch.empty((n, TOPK), dtype=torch.float16, device=device),
@@ -186,8 +196,8 @@ def kld_from_logits(ref: torch.Tensor, cand: torch.Tensor, target: torch.Tensor 
     dt = _dtype_code(ref)
     if _dtype_code(cand) != dt:
         raise TypeError("ref and cand must have the same dtype")
+    tk = _topk_from(out, n, ref.device) if topk else None
     out = out if out is not None else _alloc_rows(n, ref.device, target)
-    tk = _alloc_topk(n, ref.device) if topk else None
     ws, need = _workspace(OP_FROM_LOGITS, n, v, 0, FLAG_TOPK if topk else 0, ref.device, ws)
     rows = _rows_struct(out)
     tks = _topk_struct(tk) if tk else None
@@ -213,8 +223,8 @@ def kld_fused_head(W: torch.Tensor, h_ref: torch.Tensor, h_cand: torch.Tensor,
             raise TypeError("W and hidden states must be contiguous bf16 (or 16-bit bit-pattern) tensors")
     if h_ref.shape != (n, d) or h_cand.shape != (n, d):
         raise ValueError("hidden states must be [n, d] with d = W.shape[1]")
+    tk = _topk_from(out, n, W.device) if topk else None
     out = out if out is not None else _alloc_rows(n, W.device, target)
-    tk = _alloc_topk(n, W.device) if topk else None
     ws, need = _workspace(OP_FUSED_HEAD, n, v, d, FLAG_TOPK if topk else 0, W.device, ws)
     rows = _rows_struct(out)
     tks = _topk_struct(tk) if tk else None
