@@ -178,7 +178,7 @@ kld_status kld_fused_head(const uint16_t *W, int64_t v, int64_t d, const uint16_
   if (n < 0 || v < 0 || d < 0) return KLD_EINVAL;
   if (!out) return KLD_EINVAL;
   if (n == 0) return KLD_OK;
-  if (v < 1 || v > 0x7fffffffLL || d < 1) return KLD_ESHAPE;
+  if (v < 1 || v > 0x7fffffffLL || d < 1 || d > (1 << 20)) return KLD_ESHAPE;
   if (!W || !h_ref || !h_cand || !out->kl) return KLD_EINVAL;
   if ((out->nll_ref || out->nll_cand) && !target) return KLD_EINVAL;
   if (d % 8 != 0 || !aligned16(W) || !aligned16(h_ref) || !aligned16(h_cand))

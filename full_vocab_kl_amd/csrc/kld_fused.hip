@@ -12,9 +12,13 @@
 // per-position reduction over the vocabulary is mostly lane-local.  Reference
 // and candidate columns of the same position sit in the same lane and
 // register slot.  Operands stream straight from global memory into a
-// 4-stage LDS ring (global_load_lds, 16 bytes per lane; three stages in
-// flight while one is consumed), 64-byte rows with an XOR swizzle so
-// fragment reads spread over the banks.
+// 5-unit LDS ring (buffer loads into LDS, 16 bytes per lane): a stage of 64
+// hidden elements is a head unit and a hidden unit of 256 rows x 128 bytes
+// each, and three units are in flight while a stage is consumed.  Whole
+// 128-byte row segments per load matter on gfx950: measured, L2-resident
+// loads of 64-byte row pieces move about two thirds of the bytes per cycle
+// that 128-byte segments do.  Rows carry an XOR swizzle so fragment reads
+// spread over the LDS banks.
 //
 // Epilogue: the block's 256 x 128 tile of (a, b) pairs is folded into one
 // RowState per position (kld_device.hpp) and written as a partial state for
@@ -39,25 +43,24 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BV = 256;            // vocabulary ids per block
 constexpr int BP = 128;            // positions per block (x2 sides = 256 B columns)
-constexpr int BK = 32;             // hidden elements per pipeline stage
-constexpr int NSTAGE = 5;          // stages in the LDS ring
+constexpr int BK = 64;             // hidden elements per pipeline stage
+constexpr int CH = BK / 8;         // 16-byte chunks per staged row (128-byte rows)
 constexpr int NT = 256;            // threads per block (4 waves: 2 vocab x 2 position)
-constexpr int CH = BK / 8;         // 16-byte chunks per staged row (64-byte rows)
-constexpr int ROWS = BV + 2 * BP;  // staged rows per stage (head rows, then ref, then cand)
-constexpr int STAGE_CHUNKS = ROWS * CH;                  // 2048 chunks = 32 KB
-constexpr int ROWS_PER_LOAD = 64 / CH;                   // rows one wave-wide 16-byte load covers
-constexpr int LOADS = ROWS / ROWS_PER_LOAD / (NT / 64);  // wave-wide loads per wave per stage
+constexpr int UROWS = 256;         // staged rows per unit: a stage is a head unit + a hidden unit
+constexpr int UCHUNKS = UROWS * CH;                 // 2048 chunks = 32 KB
+constexpr int NSLOT = 5;                            // units in the LDS ring
+constexpr int ULOADS = UCHUNKS / 64 / (NT / 64);    // wave-wide loads per wave per unit
 constexpr int kXcds = 8;
-constexpr size_t kFusedLds = (size_t)NSTAGE * STAGE_CHUNKS * 16;
+constexpr size_t kFusedLds = (size_t)NSLOT * UCHUNKS * 16;   // 160 KB
 
-static_assert(LOADS == 8, "tile shape");
+static_assert(ULOADS == 8 && BV == UROWS && 2 * BP == UROWS, "tile shape");
 
-// Swizzled position of chunk c of staged row r.  Rows are 64 bytes (4
-// chunks); the chunk index is XORed with bits 2..3 of the row.  Measured on
-// gfx950 (SQ_LDS_BANK_CONFLICT), this makes the fragment reads -- lanes 0..31
-// on 32 consecutive rows at chunk c, lanes 32..63 on the same rows at chunk
-// c + 1 -- free of bank conflicts.
-__device__ __forceinline__ int swz_key(int r) { return (r >> 2) & 3; }
+// Swizzled position of chunk c of staged row r.  Rows are 128 bytes (8
+// chunks); the chunk index is XORed with (r ^ r >> 3) & 7.  Measured on gfx950
+// (SQ_LDS_BANK_CONFLICT), the fragment reads -- lanes 0..31 on 32 consecutive
+// rows at chunk c, lanes 32..63 on the same rows at chunk c + 1 -- are then
+// free of bank conflicts.
+__device__ __forceinline__ int swz_key(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int swz(int r, int c) { return r * CH + (c ^ swz_key(r)); }
 
 // Workgroup execution barrier without the memory fence of __syncthreads();
@@ -71,6 +74,8 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(vm >= 0 && vm < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// Wait until every LDS access of this wave has completed.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
 // Map the hardware block id to a logical tile id so that each XCD gets a
 // contiguous range of logical ids.
@@ -80,59 +85,71 @@ __device__ __forceinline__ int logical_block(int b, int nb) {
   return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + slot;
 }
 
+// Buffer resource over `bytes` bytes at p (raw addressing, no stride): loads
+// at offsets past the range return zero and touch no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64_t bytes) {
+  const int num = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, num, 0x00020000);
+}
+
 template <bool TOPK>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restrict__ Hr,
                        const uint16_t *__restrict__ Hc, int64_t v, int64_t d, int64_t n, int npt,
                        int64_t npad, int64_t nvt, float *__restrict__ part,
                        uint64_t *__restrict__ ckeys, float *__restrict__ resid) {
-  extern __shared__ u32x4 smem[];   // [NSTAGE][STAGE_CHUNKS]
+  extern __shared__ u32x4 smem[];   // [NSLOT][UCHUNKS]
 
   const int L = logical_block((int)blockIdx.x, (int)gridDim.x);
   const int vt = L / npt, pt = L % npt;
   const int64_t v0 = (int64_t)vt * BV, p0 = (int64_t)pt * BP;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wv = wave >> 1, wp = wave & 1;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
-  // ---- global -> LDS staging.  Wave w fills staged rows 16 (8 w + j) ..
-  // 16 (8 w + j) + 15, j = 0..7, with one wave-wide 16-byte load each: lane i
-  // lands at LDS chunk 64 (8 w + j) + i of the stage, i.e. row 16 (8 w + j) +
-  // i / 4, physical chunk i % 4, so it fetches the row's logical chunk
-  // (i % 4) ^ swizzle(row).  Rows 0..255 are head rows, 256..383 reference
-  // hidden rows, 384..511 candidate hidden rows.  Rows past v or n read a
-  // clamped valid row: their results are masked or discarded.
-  const uint16_t *src[LOADS];   // row starts
-  int coff[LOADS];               // element offset of this lane's chunk within a stage
+  // ---- global -> LDS staging.  A stage (BK hidden elements) is two units of
+  // 256 staged rows x 128 bytes: the head unit (rows = vocabulary ids v0 ..
+  // v0 + 255) and the hidden unit (rows 0..127 reference positions p0 .., rows
+  // 128..255 candidate positions).  Unit u = 2 s + (0 head | 1 hidden) of
+  // stage s lives in ring slot u % 5.  Wave w fills rows 64 w .. 64 w + 63 of
+  // a unit with 8 wave-wide 16-byte buffer loads straight into LDS: load j
+  // covers rows 64 w + 8 j .. + 7, lane i lands at physical chunk i % 8 of row
+  // 64 w + 8 j + i / 8 and fetches the logical chunk (i % 8) ^ swizzle(row),
+  // so every load reads eight whole 128-byte row segments.  Rows past v or n
+  // read a clamped valid row (their results are masked or discarded); hidden
+  // elements past d are zeroed in the fragments of the last stage.
+  uint32_t vo_w[ULOADS], vo_h[ULOADS];   // byte offsets of this lane's chunk in row block
 #pragma unroll
-  for (int j = 0; j < LOADS; ++j) {
-    const int r = 16 * (8 * wave + j) + (lane >> 2);
-    coff[j] = 8 * ((lane & 3) ^ swz_key(r));
-    if (r < BV) {
-      const int64_t vr = v0 + r;
-      src[j] = W + (vr < v ? vr : v - 1) * d;
-    } else {
-      const int hr = r - BV;
-      const int64_t pos = p0 + (hr & (BP - 1));
-      src[j] = (hr < BP ? Hr : Hc) + (pos < n ? pos : n - 1) * d;
-    }
+  for (int j = 0; j < ULOADS; ++j) {
+    const int r = 64 * wave + 8 * j + (lane >> 3);
+    const int cl = (lane & 7) ^ swz_key(r);
+    const int64_t rw = v0 + r < v ? r : v - 1 - v0;
+    const int q = r & (BP - 1);
+    const int64_t rh = p0 + q < n ? q : n - 1 - p0;
+    vo_w[j] = (uint32_t)(rw * d * 2 + cl * 16);
+    vo_h[j] = (uint32_t)(rh * d * 2 + cl * 16);
   }
+  const uint16_t *wbase = W + v0 * d;
+  const uint16_t *hbase = (wave_u < 2 ? Hr : Hc) + p0 * d;
+  const int64_t wbytes = (v - v0) * d * 2, hbytes = (n - p0) * d * 2;
   const int KT = (int)((d + BK - 1) / BK);
   const bool ktail = (d % BK) != 0;
 
-  // Issue loads j0 .. j0 + cnt - 1 of stage kt into ring slot kt % NSTAGE.
-  auto issue_part = [&](int kt, int j0, int cnt) {
-    u32x4 *dst = smem + (kt % NSTAGE) * STAGE_CHUNKS + (8 * wave) * 64;
+  // Issue loads j0 .. j0 + cnt - 1 of the head (H = false) or hidden unit of
+  // stage st.  The resource starts at the stage's first element, so offsets
+  // past the end of the operand -- the K tail of its last row, and stages past
+  // the last one -- fetch nothing.
+  auto issue = [&](int st, bool H, int j0, int cnt) {
+    const int64_t kb = (int64_t)st * BK * 2;
+    const __amdgpu_buffer_rsrc_t rs =
+        H ? make_rsrc(hbase + (int64_t)st * BK, hbytes - kb) : make_rsrc(wbase + (int64_t)st * BK, wbytes - kb);
+    u32x4 *dst = smem + ((2 * st + (H ? 1 : 0)) % NSLOT) * UCHUNKS + wave_u * (UCHUNKS / 4);
 #pragma unroll
-    for (int j = j0; j < j0 + cnt; ++j) {
-      const int64_t k = (int64_t)kt * BK + coff[j];
-      const uint16_t *g = src[j] + (k < d ? k : 0);   // past d: an in-bounds dummy, zeroed later
-      __builtin_amdgcn_global_load_lds((const void *)g,
-                                       (__attribute__((address_space(3))) void *)(dst + j * 64),
-                                       16, 0, 0);
-    }
+    for (int j = j0; j < j0 + cnt; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void *)(dst + j * 64), 16, H ? vo_h[j] : vo_w[j],
+          0, 0, 0);
   };
-  auto issue = [&](int kt) { issue_part(kt, 0, LOADS); };
-
 
   f32x16 acc[4][2][2];
 #pragma unroll
@@ -145,21 +162,24 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
         for (int i = 0; i < 16; ++i) acc[a][b][c][i] = 0.f;
 
   const int fr = lane & 31, fh = lane >> 5;
-  // fragments of one 16-wide K step: 4 head (A) and 2 x 2 hidden (B) operands
+  // fragments of one 16-wide K step: 4 head (A) and 2 x 2 hidden (B) operands.
+  // K step ks of a stage uses chunks 2 ks (lanes 0..31) and 2 ks + 1 (lanes
+  // 32..63) of the same rows for both operands.
   struct Frags {
     bf16x8 a[4], b[2][2];
   };
-  auto load_frags = [&](int slot, int ks, Frags &f) {
-    const u32x4 *sbuf = smem + slot * STAGE_CHUNKS;
+  auto load_frags = [&](int st, int ks, Frags &f) {
+    const u32x4 *sw = smem + ((2 * st) % NSLOT) * UCHUNKS;
+    const u32x4 *sh = smem + ((2 * st + 1) % NSLOT) * UCHUNKS;
     const int c = 2 * ks + fh;
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg)
 #pragma unroll
       for (int sd = 0; sd < 2; ++sd)
-        f.b[pg][sd] = __builtin_bit_cast(bf16x8, sbuf[swz(BV + sd * BP + wp * 64 + pg * 32 + fr, c)]);
+        f.b[pg][sd] = __builtin_bit_cast(bf16x8, sh[swz(sd * BP + wp * 64 + pg * 32 + fr, c)]);
 #pragma unroll
     for (int vs = 0; vs < 4; ++vs)
-      f.a[vs] = __builtin_bit_cast(bf16x8, sbuf[swz(wv * 128 + vs * 32 + fr, c)]);
+      f.a[vs] = __builtin_bit_cast(bf16x8, sw[swz(wv * 128 + vs * 32 + fr, c)]);
   };
   auto mfma = [&](const Frags &f) {
 #pragma unroll
@@ -172,9 +192,9 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
               __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[vs], f.b[pg][sd], acc[vs][pg][sd], 0, 0, 0);
   };
   // Hidden elements past d (the last stage of a width that is not a multiple
-  // of BK) were fetched from clamped in-bounds addresses; zero both operands.
-  auto mask_tail = [&](Frags &f, int kt, int ks) {
-    if ((int64_t)kt * BK + ks * 16 + 8 * fh >= d) {
+  // of BK) hold zeros or data of the next row; zero both operands there.
+  auto mask_tail = [&](Frags &f, int st, int ks) {
+    if ((int64_t)st * BK + (2 * ks + fh) * 8 >= d) {
       const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
       for (int vs = 0; vs < 4; ++vs) f.a[vs] = z;
@@ -184,62 +204,80 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
         for (int sd = 0; sd < 2; ++sd) f.b[pg][sd] = z;
     }
   };
-
-  // Software pipeline (per wave).  Iteration kt runs the 16 MFMAs of K step 0
-  // of stage kt while the K step 1 fragments of stage kt load and half of the
-  // global loads of stage kt + 4 go out; then, once stage kt + 1 has landed
-  // and every wave has passed the barrier, it runs the 16 MFMAs of K step 1
-  // while the K step 0 fragments of stage kt + 1 load and the other half of
-  // stage kt + 4 goes out.  Stage kt + 4 fills slot (kt + 4) % 5, which every
-  // wave released at the previous barrier, so the global loads spread evenly
-  // over both halves.  Past the end, stage loads read clamped in-bounds
-  // addresses into free slots, which keeps the loop free of branches; the
-  // barrier is the only point where waves synchronise.
-  static_assert(NSTAGE == 5, "the schedule below keeps four stages ahead");
-  Frags f0, f1;
-#pragma unroll
-  for (int s0 = 0; s0 < NSTAGE - 1; ++s0) issue(s0);
-  wait_vmcnt<(NSTAGE - 2) * LOADS>();   // stage 0 has landed
-  block_barrier();
-  load_frags(0, 0, f0);
-  for (int kt = 0; kt + 1 < KT; ++kt) {
-    load_frags(kt % NSTAGE, 1, f1);
-    issue_part(kt + NSTAGE - 1, 0, LOADS / 2);
-    mfma(f0);
+  // 16 MFMAs interleaved with 8 LDS fragment reads and 4 global loads.
+  auto interleave = [&]() {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one global->LDS load
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one global load
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    // stage kt + 1 has landed: outstanding are stages kt + 2, kt + 3 and half of kt + 4
-    wait_vmcnt<(NSTAGE - 3) * LOADS + LOADS / 2>();
-    block_barrier();
-    load_frags((kt + 1) % NSTAGE, 0, f0);
-    issue_part(kt + NSTAGE - 1, LOADS / 2, LOADS / 2);
+  };
+
+  // Software pipeline (per wave).  Stage s runs four K steps of 16 MFMAs on
+  // four fragment buffers; each K step reads the fragments of the step two
+  // ahead and issues 4 of the 16 loads that go out between two barriers.
+  // Barrier s sits between K steps 1 and 2 of stage s.  Between barrier s - 1
+  // and barrier s (K steps 2, 3 of stage s - 1 and 0, 1 of stage s) a wave
+  // issues the hidden unit of stage s + 1 (unit 2 s + 3) and then the head
+  // unit of stage s + 2 (unit 2 s + 4), into the slots of stage s - 1, which
+  // every wave released at barrier s - 1.  Before barrier s a wave waits for
+  // its loads of stage s + 1 (all but the last 8 loads) and for its own LDS
+  // reads, the last of which belong to stage s, so after the barrier stage
+  // s + 1 is in LDS and the slots of stage s are free.  Units of stages past
+  // the last one read in-bounds data, or nothing, into free slots, which
+  // keeps the loop free of branches.
+  static_assert(NSLOT == 5, "the schedule below keeps three units ahead");
+  Frags f0, f1, f2, f3;
+  issue(0, false, 0, ULOADS);
+  issue(0, true, 0, ULOADS);
+  issue(1, false, 0, ULOADS);
+  issue(1, true, 0, ULOADS);
+  wait_vmcnt<2 * ULOADS>();   // stage 0 has landed
+  block_barrier();
+  load_frags(0, 0, f0);
+  load_frags(0, 1, f1);
+  for (int s = 0; s + 1 < KT; ++s) {
+    load_frags(s, 2, f2);
+    issue(s + 2, false, 0, ULOADS / 2);
+    mfma(f0);
+    interleave();
+    load_frags(s, 3, f3);
+    issue(s + 2, false, ULOADS / 2, ULOADS / 2);
     mfma(f1);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    interleave();
+    wait_vmcnt<ULOADS>();
+    wait_lgkm0();
+    block_barrier();
+    load_frags(s + 1, 0, f0);
+    issue(s + 2, true, 0, ULOADS / 2);
+    mfma(f2);
+    interleave();
+    load_frags(s + 1, 1, f1);
+    issue(s + 2, true, ULOADS / 2, ULOADS / 2);
+    mfma(f3);
+    interleave();
   }
   {   // last stage
-    const int kt = KT - 1;
-    load_frags(kt % NSTAGE, 1, f1);
-    if (ktail) { mask_tail(f0, kt, 0); mask_tail(f1, kt, 1); }
+    const int s = KT - 1;
+    load_frags(s, 2, f2);
+    load_frags(s, 3, f3);
+    if (ktail) {
+      mask_tail(f0, s, 0);
+      mask_tail(f1, s, 1);
+      mask_tail(f2, s, 2);
+      mask_tail(f3, s, 3);
+    }
     mfma(f0);
     mfma(f1);
+    mfma(f2);
+    mfma(f3);
   }
+  wait_vmcnt<0>();   // no load may still write LDS when the epilogue reuses it
   __syncthreads();   // all fragment reads done before the epilogue reuses LDS
 
   // ---- epilogue: lane holds position p0 + wp*64 + pg*32 + (lane & 31) and

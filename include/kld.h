@@ -142,7 +142,8 @@ kld_status kld_from_logits(const void *ref, const void *cand, int dtype, int64_t
  * W             : [v, d] bf16 head, row-major, contiguous.
  * h_ref, h_cand : [n, d] bf16 hidden states, row-major, contiguous.
  * Logits z = W h are accumulated in f32 from exact bf16 products and are not
- * rounded to bf16; the softmax is taken in f32.  d must be a multiple of 8.
+ * rounded to bf16; the softmax is taken in f32.  d must be a multiple of 8
+ * and at most 2^20 (KLD_ESHAPE otherwise).
  * target, out, topk, opts as for kld_from_logits.
  */
 kld_status kld_fused_head(const uint16_t *W, int64_t v, int64_t d, const uint16_t *h_ref,
