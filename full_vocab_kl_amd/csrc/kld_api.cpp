@@ -82,6 +82,8 @@ FusedWs fused_carve(int64_t n, int64_t v, bool topk, Carver *c) {
   w.lse = c->take<double>((size_t)2 * n);
   w.ckeys = topk ? c->take<uint64_t>((size_t)2 * g.nvt * g.npad * 16) : nullptr;
   w.resid = topk ? c->take<float>((size_t)2 * g.nvt * g.npad) : nullptr;
+  w.rinfo = topk ? c->take<uint64_t>((size_t)2 * g.nvt * g.npad) : nullptr;
+  w.tkeys = topk ? c->take<uint64_t>((size_t)2 * g.npad * g.nvt) : nullptr;
   return w;
 }
 

@@ -97,7 +97,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restrict__ Hr,
                        const uint16_t *__restrict__ Hc, int64_t v, int64_t d, int64_t n, int npt,
                        int64_t npad, int64_t nvt, float *__restrict__ part,
-                       uint64_t *__restrict__ ckeys, float *__restrict__ resid) {
+                       uint64_t *__restrict__ ckeys, float *__restrict__ resid,
+                       uint64_t *__restrict__ rinfo, uint64_t *__restrict__ tkeys) {
   extern __shared__ u32x4 smem[];   // [NSLOT][UCHUNKS]
 
   const int L = logical_block((int)blockIdx.x, (int)gridDim.x);
@@ -292,85 +293,111 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
   const bool vtail = v0 + BV > v;
   RowState *xch = reinterpret_cast<RowState *>(smem);          // [2 pos waves][2 pg][32]
   float *rx = reinterpret_cast<float *>(xch + 2 * 2 * 32);       // [2 sides][2][2][32]
+  float *qx = rx + 2 * 2 * 2 * 32;                                 // same shape
+  int *gx = reinterpret_cast<int *>(qx + 2 * 2 * 2 * 32);          // same shape
 #pragma unroll
   for (int pg = 0; pg < 2; ++pg) {
     if (vtail) {
+      const int lim = (int)(v - v0) - (wv * 128 + 4 * fh);   // lane offsets >= lim are past v
 #pragma unroll
       for (int vs = 0; vs < 4; ++vs)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (vb + 32 * vs + 8 * (i >> 2) + (i & 3) >= v) {
+          if (32 * vs + 8 * (i >> 2) + (i & 3) >= lim) {
             acc[vs][pg][0][i] = kNegInf;
             acc[vs][pg][1][i] = kNegInf;
           }
     }
-    float gm1[2][4], gm2[2][4];
-    int gid[2][4];
+    // Group by group (the 16 ids of (lane, vs), ascending in vs and in id):
+    // per side the maximum m1 with its lowest id and, with top-k, the second
+    // largest value m2; the group's partial state relative to its own maxima,
+    // merged into the lane's state in id order.  With top-k, every group
+    // maximum is written as a candidate key at once, and per side the two
+    // largest m2 are kept with the group of the largest.
+    const int64_t pos = p0 + wp * 64 + pg * 32 + fr;
+    float a1[2] = {kNegInf, kNegInf}, a2[2] = {kNegInf, kNegInf};
+    int i1[2] = {0, 0};
+    RowState st = empty_state();
 #pragma unroll
-    for (int sd = 0; sd < 2; ++sd)
-#pragma unroll
-      for (int vs = 0; vs < 4; ++vs) {
-        float m1 = kNegInf, m2 = kNegInf;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float x = acc[vs][pg][sd][i];
-          if (TOPK) m2 = fmaxf(m2, fminf(m1, x));
-          m1 = fmaxf(m1, x);
-        }
-        int id = kNoId;
-#pragma unroll
-        for (int i = 15; i >= 0; --i)
-          if (acc[vs][pg][sd][i] == m1) id = 32 * vs + 8 * (i >> 2) + (i & 3);
-        gm1[sd][vs] = m1; gm2[sd][vs] = m2; gid[sd][vs] = id;
-      }
-    float ma = gm1[0][0], mb = gm1[1][0];
-    int ia = gid[0][0], ib = gid[1][0];
-#pragma unroll
-    for (int vs = 1; vs < 4; ++vs) {   // groups ascend in id: strict > keeps the lowest id
-      if (gm1[0][vs] > ma) { ma = gm1[0][vs]; ia = gid[0][vs]; }
-      if (gm1[1][vs] > mb) { mb = gm1[1][vs]; ib = gid[1][vs]; }
-    }
-    if (ma == kNegInf) ia = kNoId;
-    if (mb == kNegInf) ib = kNoId;
-    const float ra = ref_of(ma), rb = ref_of(mb);
-    float sa = 0.f, sb = 0.f, t = 0.f;
-#pragma unroll
-    for (int vs = 0; vs < 4; ++vs)
+    for (int vs = 0; vs < 4; ++vs) {
+      // the group's 2 x 16 values, pinned in VGPRs here so that only one
+      // group is held outside the accumulators at a time
+      float xs[2][16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float x = acc[vs][pg][0][i] - ra, y = acc[vs][pg][1][i] - rb;
+        xs[0][i] = acc[vs][pg][0][i];
+        xs[1][i] = acc[vs][pg][1][i];
+        asm volatile("" : "+v"(xs[0][i]), "+v"(xs[1][i]));
+      }
+      float m1[2], m2[2];
+      int id[2];
+#pragma unroll
+      for (int sd = 0; sd < 2; ++sd) {
+        float x1 = kNegInf, x2 = kNegInf;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float x = xs[sd][i];
+          if (TOPK) x2 = fmaxf(x2, fminf(x1, x));
+          x1 = fmaxf(x1, x);
+        }
+        int k = kNoId;
+#pragma unroll
+        for (int i = 15; i >= 0; --i)
+          if (xs[sd][i] == x1) k = 32 * vs + 8 * (i >> 2) + (i & 3);
+        m1[sd] = x1; m2[sd] = x2;
+        id[sd] = x1 == kNegInf ? kNoId : (int)(vb + k);
+        if constexpr (TOPK) {   // (positions n .. npad - 1 are padding: no branch needed)
+          ckeys[(((int64_t)sd * nvt + vt) * npad + pos) * 16 + (wv * 2 + fh) * 4 + vs] =
+              x1 == kNegInf ? 0ull : topk_key(x1, id[sd]);
+          if (x2 > a1[sd]) { a2[sd] = a1[sd]; a1[sd] = x2; i1[sd] = vs; }
+          else { a2[sd] = fmaxf(a2[sd], x2); }
+        }
+      }
+      const float ra = ref_of(m1[0]), rb = ref_of(m1[1]);
+      float sa = 0.f, sb = 0.f, t = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float x = xs[0][i] - ra, y = xs[1][i] - rb;
         const float w = exp2_fast(x * kL2E);
         sa += w;
         t = fmaf(w, fmaxf(x - y, -kFltMax), t);
         sb += exp2_fast(y * kL2E);
       }
-    RowState st;
-    st.ma = ma; st.sa = sa; st.t = t; st.mb = mb; st.sb = sb;
-    st.ia = ia == kNoId ? kNoId : (int)(vb + ia);
-    st.ib = ib == kNoId ? kNoId : (int)(vb + ib);
+      // the group's sums are complete here, before the next group is read
+      asm volatile("" : "+v"(sa), "+v"(sb), "+v"(t));
+      RowState g;
+      g.ma = m1[0]; g.sa = sa; g.t = t; g.mb = m1[1]; g.sb = sb; g.ia = id[0]; g.ib = id[1];
+      st = vs == 0 ? g : merge(st, g);
+    }
     // lanes l and l ^ 32 hold the same position (interleaved ids)
     const RowState o = shfl_xor_state(st, 32);
     st = fh == 0 ? merge(st, o) : merge(o, st);
-    const int64_t pos = p0 + wp * 64 + pg * 32 + fr;
-    float r2[2] = {kNegInf, kNegInf};
+    // Per side: the largest group second value r2 (the tile residual), the
+    // group g2 that holds it (lowest group index among equals) and the
+    // largest second value q2 of the other groups.
+    float r2[2] = {kNegInf, kNegInf}, q2[2] = {kNegInf, kNegInf};
+    int g2[2] = {0, 0};
     if constexpr (TOPK) {
 #pragma unroll
       for (int sd = 0; sd < 2; ++sd) {
-        float r = fmaxf(fmaxf(gm2[sd][0], gm2[sd][1]), fmaxf(gm2[sd][2], gm2[sd][3]));
-        r2[sd] = fmaxf(r, __shfl_xor(r, 32));
-        if (pos < n) {
-          uint64_t *dst = ckeys + (((int64_t)sd * nvt + vt) * npad + pos) * 16 + (wv * 2 + fh) * 4;
-#pragma unroll
-          for (int vs = 0; vs < 4; ++vs)
-            dst[vs] = gm1[sd][vs] == kNegInf ? 0ull : topk_key(gm1[sd][vs], (int)(vb + gid[sd][vs]));
-        }
+        const int ga = wv * 8 + fh * 4 + i1[sd];
+        const float b1 = __shfl_xor(a1[sd], 32), b2 = __shfl_xor(a2[sd], 32);
+        const int gb = __shfl_xor(ga, 32);
+        const bool aw = a1[sd] > b1 || (a1[sd] == b1 && ga < gb);
+        r2[sd] = aw ? a1[sd] : b1;
+        g2[sd] = aw ? ga : gb;
+        q2[sd] = aw ? fmaxf(a2[sd], b1) : fmaxf(b2, a1[sd]);
       }
     }
     if (wv == 1 && fh == 0) {
       xch[(wp * 2 + pg) * 32 + fr] = st;
       if (TOPK) {
-        rx[((0 * 2 + wp) * 2 + pg) * 32 + fr] = r2[0];
-        rx[((1 * 2 + wp) * 2 + pg) * 32 + fr] = r2[1];
+#pragma unroll
+        for (int sd = 0; sd < 2; ++sd) {
+          rx[((sd * 2 + wp) * 2 + pg) * 32 + fr] = r2[sd];
+          qx[((sd * 2 + wp) * 2 + pg) * 32 + fr] = q2[sd];
+          gx[((sd * 2 + wp) * 2 + pg) * 32 + fr] = g2[sd];
+        }
       }
     }
     __syncthreads();
@@ -383,10 +410,21 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
       q[5 * plane] = __int_as_float(st.ia);
       q[6 * plane] = __int_as_float(st.ib);
       if (TOPK) {
-        resid[((int64_t)0 * nvt + vt) * npad + pos] =
-            fmaxf(r2[0], rx[((0 * 2 + wp) * 2 + pg) * 32 + fr]);
-        resid[((int64_t)1 * nvt + vt) * npad + pos] =
-            fmaxf(r2[1], rx[((1 * 2 + wp) * 2 + pg) * 32 + fr]);
+#pragma unroll
+        for (int sd = 0; sd < 2; ++sd) {
+          const int xi = ((sd * 2 + wp) * 2 + pg) * 32 + fr;
+          const float b1 = rx[xi], b2 = qx[xi];
+          const int gb = gx[xi];
+          const bool aw = r2[sd] > b1 || (r2[sd] == b1 && g2[sd] < gb);
+          const int64_t ti = ((int64_t)sd * nvt + vt) * npad + pos;
+          resid[ti] = aw ? r2[sd] : b1;
+          rinfo[ti] = (uint64_t)__float_as_uint(aw ? fmaxf(q2[sd], b1) : fmaxf(b2, r2[sd])) |
+                      ((uint64_t)(uint32_t)(aw ? g2[sd] : gb) << 32);
+        }
+        // the tile's largest candidate key per side (the maximum and its
+        // lowest id), position-major for the selection
+        tkeys[((int64_t)0 * npad + pos) * nvt + vt] = st.ma == kNegInf ? 0ull : topk_key(st.ma, st.ia);
+        tkeys[((int64_t)1 * npad + pos) * nvt + vt] = st.mb == kNegInf ? 0ull : topk_key(st.mb, st.ib);
       }
     }
     __syncthreads();
@@ -482,20 +520,101 @@ __global__ __launch_bounds__(FP * FG) void fused_finalize_kernel(
 // groups (key = value bits, then complemented id).  Every id that is not a
 // candidate is <= its tile's residual (the largest second-largest value of
 // the tile's groups).
-//  A. Radix-narrow (8 bits per pass, MSB first) the bucket that holds the
-//     64th largest candidate key until it fits the LDS buffer; gather every
-//     key at or above that bucket, sort, keep 64.  T = the 64th key.
+//  A. Tile maxima (the largest of a tile's 16 keys) are cut to the 64
+//     largest, in chunks through a sorted LDS buffer.  A candidate of any
+//     other tile is below 64 larger tile maxima, so the top 64 candidates lie
+//     in these 64 tiles: their 1024 keys are sorted and the first 64 kept.
+//     T = the 64th key.
 //  B. Any tile whose residual reaches T's value may hide an id that belongs
 //     in the top 64 (or fewer than 64 candidates exist): its 256 logits are
 //     recomputed here from W and h (f32 dot products), its old candidates
-//     are dropped, and the running top 64 is re-cut.  On generic inputs no
-//     tile is flagged; degenerate inputs (exact ties across many ids) only
-//     cost time.
+//     are dropped, and the running top 64 is re-cut.  Only the 64 tiles of A
+//     can qualify: every other tile's residual is at most its maximum, which
+//     is below T, or equal to T's value only with larger ids.  On generic
+//     inputs no tile is flagged; degenerate inputs (exact ties across many
+//     ids) only cost time.
 //  C. Write ids and fp16 log-probs lp = z - lse.
 constexpr int TK = 256;
-constexpr int kSelBuf = 4096;
+
+// Block-wide (TK threads) selection of the 64 largest nonzero keys among the
+// K keys each thread holds (0 = no key; nonzero keys are distinct).  Radix
+// select, 8 bits per pass from the top: a 256-bin LDS histogram of the keys
+// that match the digits fixed so far, and wave 0 finds the bin that holds the
+// wanted rank.  Returns the 64th largest key, or 0 when fewer than 64 keys are
+// nonzero; stores the selected keys (every nonzero key when fewer than 64) in
+// top[0..63], zero-filled, in no particular order.
+template <int K>
+__device__ uint64_t select64(const uint64_t (&k)[K], uint64_t *top, uint32_t *hist,
+                             uint32_t *sh) {
+  static_assert(TK == 256, "one histogram bin per thread");
+  const int tid = threadIdx.x;
+  uint64_t prefix = 0;
+  uint32_t need = 64;
+  bool found = true;
+  for (int pass = 0; pass < 8; ++pass) {
+    const int shift = 56 - 8 * pass;
+    hist[tid] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < K; ++q) {
+      const uint64_t x = k[q];
+      if (x != 0ull && (pass == 0 || (x >> (shift + 8)) == (prefix >> (shift + 8))))
+        atomicAdd(&hist[(x >> shift) & 255], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane l owns bins 4 l .. 4 l + 3; count the keys in higher bins
+      uint32_t c[4], s4 = 0;
+#pragma unroll
+      for (int bq = 0; bq < 4; ++bq) { c[bq] = hist[4 * tid + bq]; s4 += c[bq]; }
+      uint32_t suf = s4;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_down(suf, o);
+        if (tid + o < 64) suf += t;
+      }
+      uint32_t above = suf - s4;
+      int bin = -1;
+      uint32_t left = 0;
+#pragma unroll
+      for (int bq = 3; bq >= 0; --bq) {
+        if (bin < 0 && above < need && above + c[bq] >= need) { bin = 4 * tid + bq; left = need - above; }
+        above += c[bq];
+      }
+      const uint64_t m = __ballot(bin >= 0);
+      if (m == 0ull) {
+        if (tid == 0) sh[0] = 0xffffffffu;
+      } else {
+        const int src = __ffsll((long long)m) - 1;
+        const int bb = __shfl(bin, src);
+        const uint32_t ll = __shfl(left, src);
+        if (tid == 0) { sh[0] = (uint32_t)bb; sh[1] = ll; }
+      }
+    }
+    __syncthreads();
+    const uint32_t dd = sh[0];
+    need = sh[1];
+    __syncthreads();
+    if (dd == 0xffffffffu) { found = false; break; }
+    prefix |= (uint64_t)dd << shift;
+  }
+  const uint64_t T = found ? prefix : 0ull;
+  if (tid == 0) sh[2] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < K; ++q)
+    if (k[q] != 0ull && k[q] >= T) top[atomicAdd(&sh[2], 1u)] = k[q];
+  __syncthreads();
+  const uint32_t cnt = sh[2];
+  for (uint32_t i = cnt + tid; i < 64; i += TK) top[i] = 0ull;
+  __syncthreads();
+  return T;
+}
+
 __global__ __launch_bounds__(TK) void fused_topk_kernel(
-    const uint64_t *__restrict__ ckeys, const float *__restrict__ resid, int64_t nvt, int64_t npad,
+    const uint64_t *__restrict__ ckeys, const float *__restrict__ resid,
+    const uint64_t *__restrict__ rinfo, const uint64_t *__restrict__ tkeys, int64_t nvt,
+    int64_t npad,
     int64_t n, const uint16_t *__restrict__ W, const uint16_t *__restrict__ Hr,
     const uint16_t *__restrict__ Hc, int64_t v, int64_t d, const double *__restrict__ lse_d,
     TopkOut out) {
@@ -505,112 +624,151 @@ __global__ __launch_bounds__(TK) void fused_topk_kernel(
   uint16_t *lp = side ? out.lp_cand : out.lp_ref;
   if ((!ids && !lp) || pos >= n) return;
 
+  __shared__ uint64_t buf[64 + TK];
   __shared__ uint32_t hist[256];
-  __shared__ uint64_t buf[kSelBuf];
-  __shared__ uint64_t sh_prefix;
-  __shared__ int sh_pbits, sh_need, sh_cnt, sh_fill, sh_nflag;
+  __shared__ uint32_t sh[4];
+  __shared__ int tiles[64];
+  __shared__ int sh_nflag;
   __shared__ int flagged[TK];
 
   const uint64_t *base = ckeys + ((int64_t)side * nvt * npad + pos) * 16;
-  const int64_t total = nvt * 16;
   const int64_t tstride = npad * 16;
   const int tid = threadIdx.x;
 
-  // ---- A: narrow the bucket of the 64th largest candidate key
-  uint64_t prefix = 0;
-  int pbits = 0, need = 64;
-  for (;;) {
-    hist[tid] = 0;
-    __syncthreads();
-    for (int64_t i = tid; i < total; i += TK) {
-      const uint64_t k = base[(i >> 4) * tstride + (i & 15)];
-      if (pbits == 0 || (k >> (64 - pbits)) == prefix) atomicAdd(&hist[(k >> (56 - pbits)) & 255], 1u);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int cum = 0, dd = 0;
-      for (dd = 255; dd > 0; --dd) {
-        if (cum + (int)hist[dd] >= need) break;
-        cum += (int)hist[dd];
-      }
-      sh_need = need - cum;
-      sh_prefix = (prefix << 8) | (uint64_t)dd;
-      sh_pbits = pbits + 8;
-      sh_cnt = (int)hist[dd];
-    }
-    __syncthreads();
-    prefix = sh_prefix; pbits = sh_pbits; need = sh_need;
-    const int cnt = sh_cnt;
-    __syncthreads();
-    if (pbits == 64 || cnt <= kSelBuf - 64) break;
-  }
-  // gather every key whose top pbits reach the bucket
-  if (tid == 0) sh_fill = 0;
+  // ---- A1: the 64 largest tile maxima, in chunks of 3 TK tiles plus the
+  // running 64 (buf[0..63]).
+  const uint64_t *tk = tkeys + ((int64_t)side * npad + pos) * nvt;
+  if (tid < 64) buf[tid] = 0ull;
   __syncthreads();
-  for (int64_t i = tid; i < total; i += TK) {
-    const uint64_t k = base[(i >> 4) * tstride + (i & 15)];
-    if ((pbits == 64 ? k : (k >> (64 - pbits))) >= prefix && k != 0ull) {
-      const int slot = atomicAdd(&sh_fill, 1);
-      buf[slot] = k;
+  for (int64_t c0 = 0; c0 < nvt; c0 += 3 * TK) {
+    uint64_t k4[4];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int64_t t = c0 + q * TK + tid;
+      k4[q] = t < nvt ? tk[t] : 0ull;
     }
+    k4[3] = tid < 64 ? buf[tid] : 0ull;
+    __syncthreads();
+    select64<4>(k4, buf, hist, sh);
   }
+  // ---- A2: the 64 largest of those tiles' 16 candidates each
+  if (tid < 64) tiles[tid] = buf[tid] == 0ull ? -1 : (int)((uint32_t)key_id(buf[tid]) / BV);
   __syncthreads();
+  uint64_t T;
   {
-    const int fill = sh_fill;
-    int m = 64;
-    while (m < fill) m <<= 1;
-    for (int i = fill + tid; i < m; i += TK) buf[i] = 0ull;
-    __syncthreads();
-    bitonic_desc<TK>(buf, m);
+    uint64_t k4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = q * TK + tid;
+      const int t = tiles[i >> 4];
+      k4[q] = t < 0 ? 0ull : base[(int64_t)t * tstride + (i & 15)];
+    }
+    T = select64<4>(k4, buf, hist, sh);
   }
-  const uint64_t T = buf[63];
   const float tval = key_value(T);
 
-  // ---- B: recompute tiles whose residual reaches T (all tiles if T is unset)
+  // ---- B: recompute what may hide a missing id: when T is unset, every tile;
+  // else, among the 64 tiles of A, each tile whose residual reaches T -- only
+  // the group that holds the residual when no other group's second value
+  // reaches T, else the whole tile.
   const uint16_t *h = (side ? Hc : Hr) + pos * d;
-  for (int64_t r0 = 0; r0 < nvt; r0 += TK) {
+  const int64_t nscan = T == 0ull ? nvt : 64;
+  for (int64_t r0 = 0; r0 < nscan; r0 += TK) {
     if (tid == 0) sh_nflag = 0;
     __syncthreads();
-    const int64_t vt = r0 + tid;
-    if (vt < nvt && (T == 0ull || resid[((int64_t)side * nvt + vt) * npad + pos] >= tval))
-      flagged[atomicAdd(&sh_nflag, 1)] = (int)vt;
+    const int64_t vt = T == 0ull ? r0 + tid : (tid < 64 ? tiles[tid] : -1);
+    if (r0 + tid < nscan && vt >= 0) {
+      const int64_t ti = ((int64_t)side * nvt + vt) * npad + pos;
+      if (T == 0ull) {
+        flagged[atomicAdd(&sh_nflag, 1)] = (int)vt;
+      } else if (resid[ti] >= tval) {
+        const uint64_t info = rinfo[ti];
+        const int grp = __uint_as_float((uint32_t)info) < tval ? (int)(info >> 32) : -1;
+        flagged[atomicAdd(&sh_nflag, 1)] = (int)vt | ((grp + 1) << 24);
+      }
+    }
     __syncthreads();
     const int nf = sh_nflag;
     for (int f = 0; f < nf; ++f) {
-      const int64_t t0 = (int64_t)flagged[f] * BV;   // the tile's first id
-      // drop the tile's old candidates from the running top 64
+      const int64_t t0 = (int64_t)(flagged[f] & 0xffffff) * BV;   // the tile's first id
+      const int grp = (flagged[f] >> 24) - 1;                     // -1: the whole tile
+      // Offset in the tile of row q of group g: ids of group (wv, fh, vs) are
+      // 128 wv + 4 fh + 32 vs + 8 (i / 4) + i % 4, i = 0..15.
+      auto grp_off = [](int g, int q) {
+        return (g >> 3) * 128 + ((g >> 2) & 1) * 4 + (g & 3) * 32 + 8 * (q >> 2) + (q & 3);
+      };
+      auto grp_of = [](int off) { return ((off >> 7) & 1) * 8 + ((off >> 2) & 1) * 4 + ((off >> 5) & 3); };
+      // drop the recomputed ids' old candidates from the running top 64
       if (tid < 64) {
-        const int id = key_id(buf[tid]);
-        if (buf[tid] != 0ull && id >= t0 && id < t0 + BV) buf[tid] = 0ull;
+        const int64_t id = key_id(buf[tid]);
+        if (buf[tid] != 0ull && id >= t0 && id < t0 + BV && (grp < 0 || grp_of((int)(id - t0)) == grp))
+          buf[tid] = 0ull;
       }
-      // its 256 logits, one per thread
-      const int64_t j = t0 + tid;
-      uint64_t k = 0ull;
-      if (j < v) {
-        const uint16_t *w = W + j * d;
-        float z = 0.f;
-        for (int64_t e = 0; e < d; e += 8) {
-          const u32x4 qw = *reinterpret_cast<const u32x4 *>(w + e);
-          const u32x4 qh = *reinterpret_cast<const u32x4 *>(h + e);
+      // the logits: wave w computes a quarter of the rows, four at a time;
+      // lane l sums elements 8 l .. 8 l + 7 of every 512 in order, then the 64
+      // lane sums are added in a fixed butterfly order.
+      const int nrows = grp < 0 ? BV : 16;
+      {
+        const int wv = tid >> 6, ln = tid & 63;
+        const int per = nrows / 4;
+        for (int r = 0; r < per; r += 4) {
+          float z4[4] = {0.f, 0.f, 0.f, 0.f};
+          const uint16_t *w4[4];
+          int64_t j4[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            z = fmaf(__uint_as_float(qw[q] << 16), __uint_as_float(qh[q] << 16), z);
-            z = fmaf(__uint_as_float(qw[q] & 0xffff0000u), __uint_as_float(qh[q] & 0xffff0000u), z);
+            const int row = wv * per + r + q;
+            j4[q] = t0 + (grp < 0 ? row : grp_off(grp, row));
+            w4[q] = W + (j4[q] < v ? j4[q] : v - 1) * d;
+          }
+          for (int64_t e = (int64_t)ln * 8; e < d; e += 512) {
+            const u32x4 qh = *reinterpret_cast<const u32x4 *>(h + e);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const u32x4 qw = *reinterpret_cast<const u32x4 *>(w4[q] + e);
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                z4[q] = fmaf(__uint_as_float(qw[c] << 16), __uint_as_float(qh[c] << 16), z4[q]);
+                z4[q] = fmaf(__uint_as_float(qw[c] & 0xffff0000u), __uint_as_float(qh[c] & 0xffff0000u), z4[q]);
+              }
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int m = 32; m >= 1; m >>= 1) {
+              const float o = __shfl_xor(z4[q], m);
+              z4[q] = (ln & m) == 0 ? z4[q] + o : o + z4[q];
+            }
+          }
+          if (ln < 4) {
+            const float z = ln == 0 ? z4[0] : ln == 1 ? z4[1] : ln == 2 ? z4[2] : z4[3];
+            const int64_t j = ln == 0 ? j4[0] : ln == 1 ? j4[1] : ln == 2 ? j4[2] : j4[3];
+            buf[64 + wv * per + r + ln] = j < v ? topk_key(z, (int)j) : 0ull;
           }
         }
-        k = topk_key(z, (int)j);
       }
-      buf[64 + tid] = k;
-      for (int i = 64 + TK + tid; i < 512; i += TK) buf[i] = 0ull;
+      if (tid >= nrows) buf[64 + tid] = 0ull;
       __syncthreads();
-      bitonic_desc<TK>(buf, 512);
+      uint64_t k2[2] = {buf[64 + tid], tid < 64 ? buf[tid] : 0ull};
+      __syncthreads();
+      select64<2>(k2, buf, hist, sh);
     }
     __syncthreads();
   }
 
-  // ---- C: ids and log-probs
+  // ---- C: ids and log-probs, in descending key order (bitonic sort of the
+  // 64 selected keys across the lanes of wave 0)
   if (tid < 64) {
-    const uint64_t k = buf[tid];
+    uint64_t k = buf[tid];
+#pragma unroll
+    for (int kk = 2; kk <= 64; kk <<= 1)
+#pragma unroll
+      for (int j = kk >> 1; j > 0; j >>= 1) {
+        const uint64_t o = __shfl_xor(k, j);
+        const bool desc = (tid & kk) == 0, lower = (tid & j) == 0;
+        k = (desc == lower) ? (o > k ? o : k) : (o < k ? o : k);
+      }
     const double l = lse_d[(int64_t)side * n + pos];
     if (ids) ids[pos * 64 + tid] = key_id(k);
     if (lp) lp[pos * 64 + tid] = f32_to_f16_bits((float)((double)key_value(k) - l));
@@ -642,11 +800,11 @@ hipError_t launch_fused(const FusedArgs &a, const FusedWs &w) {
   if (tk)
     hipLaunchKernelGGL(fused_head_kernel<true>, dim3((unsigned)nblocks), dim3(NT),
                        kFusedLds, a.stream, a.W, a.h_ref, a.h_cand, a.v, a.d,
-                       a.n, (int)g.npt, g.npad, g.nvt, w.part, w.ckeys, w.resid);
+                       a.n, (int)g.npt, g.npad, g.nvt, w.part, w.ckeys, w.resid, w.rinfo, w.tkeys);
   else
     hipLaunchKernelGGL(fused_head_kernel<false>, dim3((unsigned)nblocks), dim3(NT),
                        kFusedLds, a.stream, a.W, a.h_ref, a.h_cand, a.v, a.d,
-                       a.n, (int)g.npt, g.npad, g.nvt, w.part, nullptr, nullptr);
+                       a.n, (int)g.npt, g.npad, g.nvt, w.part, nullptr, nullptr, nullptr, nullptr);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = record(a.ev.stop, a.stream);
@@ -662,7 +820,8 @@ hipError_t launch_fused(const FusedArgs &a, const FusedWs &w) {
   e = hipGetLastError();
   if (e != hipSuccess || !tk) return e;
   hipLaunchKernelGGL(fused_topk_kernel, dim3((unsigned)(2 * a.n)), dim3(TK), 0, a.stream, w.ckeys,
-                     w.resid, g.nvt, g.npad, a.n, a.W, a.h_ref, a.h_cand, a.v, a.d, w.lse, a.topk);
+                     w.resid, w.rinfo, w.tkeys, g.nvt, g.npad, a.n, a.W, a.h_ref, a.h_cand, a.v, a.d, w.lse,
+                     a.topk);
   return hipGetLastError();
 }
 

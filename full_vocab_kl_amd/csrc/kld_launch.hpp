@@ -76,6 +76,8 @@ struct FusedWs {
   double *lse;        // 2 * n log-sum-exp (top-k only)
   uint64_t *ckeys;    // 2 * nvt * npad * 16 candidate keys (top-k only)
   float *resid;       // 2 * nvt * npad tile residuals (top-k only)
+  uint64_t *rinfo;    // 2 * nvt * npad: runner-up group residual | residual group << 32
+  uint64_t *tkeys;    // 2 * npad * nvt tile-maximum keys, position-major (top-k only)
 };
 hipError_t launch_fused(const FusedArgs &a, const FusedWs &w);
 
