@@ -30,6 +30,8 @@
 // so that each XCD receives a contiguous range of tiles, position tiles
 // fastest, so all position tiles of one head tile run together on one XCD
 // and the head tile is fetched from HBM about once into that XCD's L2.
+#include <type_traits>
+
 #include "kld_device.hpp"
 #include "kld_launch.hpp"
 
@@ -137,14 +139,18 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
   const bool ktail = (d % BK) != 0;
 
   // Issue loads j0 .. j0 + cnt - 1 of the head (H = false) or hidden unit of
-  // stage st.  The resource starts at the stage's first element, so offsets
-  // past the end of the operand -- the K tail of its last row, and stages past
-  // the last one -- fetch nothing.
-  auto issue = [&](int st, bool H, int j0, int cnt) {
-    const int64_t kb = (int64_t)st * BK * 2;
-    const __amdgpu_buffer_rsrc_t rs =
-        H ? make_rsrc(hbase + (int64_t)st * BK, hbytes - kb) : make_rsrc(wbase + (int64_t)st * BK, wbytes - kb);
-    u32x4 *dst = smem + ((2 * st + (H ? 1 : 0)) % NSLOT) * UCHUNKS + wave_u * (UCHUNKS / 4);
+  // stage st into ring slot `slot`.  The resource starts at the stage's first
+  // element, so offsets past the end of the operand -- the K tail of its last
+  // row, and stages past the last one -- fetch nothing.  (Byte counts are
+  // clamped to 2^31 - 1, far beyond the 256 rows a block reads.)
+  const uint32_t wb32 = (uint32_t)(wbytes < 0x7fffffff ? wbytes : 0x7fffffff);
+  const uint32_t hb32 = (uint32_t)(hbytes < 0x7fffffff ? hbytes : 0x7fffffff);
+  auto issue = [&](int st, bool H, int j0, int cnt, int slot) {
+    const int rem = (int)(H ? hb32 : wb32) - st * (BK * 2);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>((H ? hbase : wbase) + (int64_t)st * BK), (short)0,
+        __builtin_amdgcn_readfirstlane(rem > 0 ? rem : 0), 0x00020000);
+    u32x4 *dst = smem + slot * UCHUNKS + wave_u * (UCHUNKS / 4);
 #pragma unroll
     for (int j = j0; j < j0 + cnt; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -169,18 +175,30 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
   struct Frags {
     bf16x8 a[4], b[2][2];
   };
-  auto load_frags = [&](int st, int ks, Frags &f) {
-    const u32x4 *sw = smem + ((2 * st) % NSLOT) * UCHUNKS;
-    const u32x4 *sh = smem + ((2 * st + 1) % NSLOT) * UCHUNKS;
-    const int c = 2 * ks + fh;
+  // Per-lane byte offsets of the fragment reads within a slot.  A row
+  // wv*128 + vs*32 + fr and B row sd*128 + wp*64 + pg*32 + fr share their
+  // swizzle key with the row 64 (resp. 128) below, so the lane offset depends
+  // only on (K step, vs & 1) or (K step, pg); the rest is a constant.
+  uint32_t offA[4][2], offB[4][2];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int ra = wv * 128 + x * 32 + fr, rb = wp * 64 + x * 32 + fr;
+      offA[ks][x] = (uint32_t)(ra * CH + ((2 * ks + fh) ^ swz_key(ra))) * 16;
+      offB[ks][x] = (uint32_t)(rb * CH + ((2 * ks + fh) ^ swz_key(rb))) * 16;
+    }
+  auto load_frags = [&](int slot_w, int slot_h, int ks, Frags &f) {
+    const char *sw = reinterpret_cast<const char *>(smem + slot_w * UCHUNKS);
+    const char *sh = reinterpret_cast<const char *>(smem + slot_h * UCHUNKS);
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg)
 #pragma unroll
       for (int sd = 0; sd < 2; ++sd)
-        f.b[pg][sd] = __builtin_bit_cast(bf16x8, sh[swz(sd * BP + wp * 64 + pg * 32 + fr, c)]);
+        f.b[pg][sd] = *reinterpret_cast<const bf16x8 *>(sh + offB[ks][pg] + sd * (BP * CH * 16));
 #pragma unroll
     for (int vs = 0; vs < 4; ++vs)
-      f.a[vs] = __builtin_bit_cast(bf16x8, sw[swz(wv * 128 + vs * 32 + fr, c)]);
+      f.a[vs] = *reinterpret_cast<const bf16x8 *>(sw + offA[ks][vs & 1] + (vs >> 1) * (64 * CH * 16));
   };
   auto mfma = [&](const Frags &f) {
 #pragma unroll
@@ -205,7 +223,9 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
         for (int sd = 0; sd < 2; ++sd) f.b[pg][sd] = z;
     }
   };
-  // 16 MFMAs interleaved with 8 LDS fragment reads and 4 global loads.
+  // 16 MFMAs interleaved with 8 LDS fragment reads and 4 global loads; the
+  // scheduling fence after each K step keeps the pattern from being merged
+  // across the steps of the unrolled stages.
   auto interleave = [&]() {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -217,6 +237,7 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);   // keep each K step's mix within the step
   };
 
   // Software pipeline (per wave).  Stage s runs four K steps of 16 MFMAs on
@@ -234,39 +255,62 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
   // keeps the loop free of branches.
   static_assert(NSLOT == 5, "the schedule below keeps three units ahead");
   Frags f0, f1, f2, f3;
-  issue(0, false, 0, ULOADS);
-  issue(0, true, 0, ULOADS);
-  issue(1, false, 0, ULOADS);
-  issue(1, true, 0, ULOADS);
+  issue(0, false, 0, ULOADS, 0);
+  issue(0, true, 0, ULOADS, 1);
+  issue(1, false, 0, ULOADS, 2);
+  issue(1, true, 0, ULOADS, 3);
   wait_vmcnt<2 * ULOADS>();   // stage 0 has landed
   block_barrier();
-  load_frags(0, 0, f0);
-  load_frags(0, 1, f1);
-  for (int s = 0; s + 1 < KT; ++s) {
-    load_frags(s, 2, f2);
-    issue(s + 2, false, 0, ULOADS / 2);
+  load_frags(0, 1, 0, f0);
+  load_frags(0, 1, 1, f1);
+  // One stage; R = s % 5 is a compile-time constant in the unrolled loop, so
+  // every slot index (and LDS offset) below is one too.
+  auto stage = [&](int s, auto R) {
+    constexpr int r = decltype(R)::value;
+    constexpr int sw = (2 * r) % NSLOT, sh = (2 * r + 1) % NSLOT;           // stage s
+    constexpr int nw = (2 * r + 2) % NSLOT, nh = (2 * r + 3) % NSLOT;       // stage s + 1
+    constexpr int lw = (2 * r + 4) % NSLOT, lh = (2 * r + 5) % NSLOT;       // stage s + 2
+    load_frags(sw, sh, 2, f2);
+    issue(s + 2, false, 0, ULOADS / 2, lw);
     mfma(f0);
     interleave();
-    load_frags(s, 3, f3);
-    issue(s + 2, false, ULOADS / 2, ULOADS / 2);
+    load_frags(sw, sh, 3, f3);
+    issue(s + 2, false, ULOADS / 2, ULOADS / 2, lw);
     mfma(f1);
     interleave();
     wait_vmcnt<ULOADS>();
     wait_lgkm0();
     block_barrier();
-    load_frags(s + 1, 0, f0);
-    issue(s + 2, true, 0, ULOADS / 2);
+    load_frags(nw, nh, 0, f0);
+    issue(s + 2, true, 0, ULOADS / 2, lh);
     mfma(f2);
     interleave();
-    load_frags(s + 1, 1, f1);
-    issue(s + 2, true, ULOADS / 2, ULOADS / 2);
+    load_frags(nw, nh, 1, f1);
+    issue(s + 2, true, ULOADS / 2, ULOADS / 2, lh);
     mfma(f3);
     interleave();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  int s = 0;
+  for (; s + NSLOT < KT; s += NSLOT) {
+    stage(s, I0{});
+    stage(s + 1, I1{});
+    stage(s + 2, I2{});
+    stage(s + 3, I3{});
+    stage(s + 4, I4{});
   }
-  {   // last stage
-    const int s = KT - 1;
-    load_frags(s, 2, f2);
-    load_frags(s, 3, f3);
+  if (s + 1 < KT) { stage(s, I0{}); ++s; }
+  if (s + 1 < KT) { stage(s, I1{}); ++s; }
+  if (s + 1 < KT) { stage(s, I2{}); ++s; }
+  if (s + 1 < KT) { stage(s, I3{}); ++s; }
+  {   // last stage, s = KT - 1
+    const int sw = (2 * s) % NSLOT, sh = (2 * s + 1) % NSLOT;
+    load_frags(sw, sh, 2, f2);
+    load_frags(sw, sh, 3, f3);
     if (ktail) {
       mask_tail(f0, s, 0);
       mask_tail(f1, s, 1);
