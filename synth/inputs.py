@@ -1,10 +1,12 @@
 """Seeded, row-addressable synthetic inputs.
 
-Every row r of stream k for workload c is drawn from
+Every logits row r of stream k for workload c is drawn from
 ``numpy.random.default_rng(SeedSequence([BASE_SEED, c, k, r]))`` so any
 subset of rows can be regenerated on its own.  The head weight is drawn in
-blocks of ``HEAD_BLOCK`` vocabulary rows (block b uses index b).  Rounding
-to bf16 is round-to-nearest-even from float32.
+blocks of ``HEAD_BLOCK`` vocabulary rows and hidden states in blocks of
+``HIDDEN_BLOCK`` positions (block b uses index b), so a row is regenerated
+from its block.  All fused-head workloads share the head of the one-window
+workload.  Rounding to bf16 is round-to-nearest-even from float32.
 
 The shapes follow the pages' workloads: a 248,320-id vocabulary, hidden
 width 5120, windows of 2048 tokens with 2047 scored positions, a 2.54 GB
@@ -14,6 +16,7 @@ not available.
 """
 from __future__ import annotations
 
+import functools
 import os
 from concurrent.futures import ThreadPoolExecutor
 
@@ -26,6 +29,7 @@ WINDOW_POSITIONS = 2047
 
 STREAM_BASE, STREAM_NOISE, STREAM_BOOST, STREAM_TARGET, STREAM_HEAD, STREAM_SUBSET = range(6)
 HEAD_BLOCK = 2048
+HIDDEN_BLOCK = 256
 
 # workload ids used as the second seed word
 LOGITS_F32, FUSED_WINDOW, LOGITS_BF16_TOPK, FUSED_BATCH, LONG_TRACE = range(5)
@@ -107,8 +111,11 @@ def targets(workload: int, rows, v: int) -> np.ndarray:
 # fused head inputs
 # --------------------------------------------------------------------------
 
+@functools.lru_cache(maxsize=8)
 def head_weight(workload: int, v: int, d: int, std: float = 0.02) -> np.ndarray:
-    """Shared head W [v, d] as bf16 bits, W ~ N(0, std^2)."""
+    """Shared head W [v, d] as bf16 bits, W ~ N(0, std^2).  The array is
+    cached because the full head takes tens of seconds to draw: callers must
+    not modify it."""
     w = np.empty((v, d), np.uint16)
 
     def one(blk):
@@ -121,26 +128,37 @@ def head_weight(workload: int, v: int, d: int, std: float = 0.02) -> np.ndarray:
     return w
 
 
-def hidden_row_pair(workload: int, r: int, d: int, noise: float):
-    """h = N(0,1) row scaled to unit RMS (float32); reference = bf16(h),
-    candidate = bf16(h + N(0, noise^2))."""
-    z = rng(workload, STREAM_BASE, r).standard_normal(d, dtype=np.float32)
-    rms = np.float32(np.sqrt(np.mean(z.astype(np.float64) ** 2)))
+def _hidden_block(workload: int, blk: int, d: int, noise):
+    """Positions blk*HIDDEN_BLOCK .. +HIDDEN_BLOCK-1: h = N(0,1) rows scaled to
+    unit RMS (float32); reference = bf16(h), candidate = bf16(h + N(0, s^2))
+    with s = noise(row) (or the constant noise)."""
+    r0 = blk * HIDDEN_BLOCK
+    z = rng(workload, STREAM_BASE, blk).standard_normal((HIDDEN_BLOCK, d), dtype=np.float32)
+    rms = np.sqrt(np.mean(np.square(z, dtype=np.float64), axis=1, keepdims=True)).astype(np.float32)
     h = (z / rms).astype(np.float32)
-    hc = h + np.float32(noise) * rng(workload, STREAM_NOISE, r).standard_normal(d, dtype=np.float32)
-    return f32_to_bf16_bits(h), f32_to_bf16_bits(hc.astype(np.float32))
+    e = rng(workload, STREAM_NOISE, blk).standard_normal((HIDDEN_BLOCK, d), dtype=np.float32)
+    if callable(noise):
+        s = np.array([noise(r0 + i) for i in range(HIDDEN_BLOCK)], np.float32)[:, None]
+    else:
+        s = np.float32(noise)
+    hc = (h + s * e).astype(np.float32)
+    return f32_to_bf16_bits(h), f32_to_bf16_bits(hc)
 
 
 def hidden_rows(workload: int, rows, d: int, noise) -> tuple:
-    """Hidden-state rows; ``noise`` is a float or a callable row -> std."""
-    rows = list(rows)
+    """Hidden-state rows (bf16 bits) for the given positions; ``noise`` is a
+    float or a callable position -> std."""
+    rows = np.asarray(list(rows), np.int64)
     hr = np.empty((len(rows), d), np.uint16)
     hc = np.empty_like(hr)
+    blocks = np.unique(rows // HIDDEN_BLOCK) if len(rows) else np.zeros(0, np.int64)
 
-    def one(i):
-        s = noise(rows[i]) if callable(noise) else noise
-        hr[i], hc[i] = hidden_row_pair(workload, rows[i], d, s)
-    _pmap(one, range(len(rows)))
+    def one(blk):
+        br, bc = _hidden_block(workload, int(blk), d, noise)
+        sel = np.nonzero(rows // HIDDEN_BLOCK == blk)[0]
+        hr[sel] = br[rows[sel] - blk * HIDDEN_BLOCK]
+        hc[sel] = bc[rows[sel] - blk * HIDDEN_BLOCK]
+    _pmap(one, blocks)
     return hr, hc
 
 

@@ -115,17 +115,20 @@ def test_topk_export_single_side_with_target(bf16):
         assert abs(res["target_lp"][i].item() - want_t) <= 1e-5 * max(1.0, abs(want_t))
 
 
-def test_topk_tail_matches_oracle_on_exported_lists():
+def test_topk_tail_matches_oracle_on_oracle_lists():
+    """The tail kernel on top-64 lists the oracle exports from seeded bf16
+    logits, against the oracle's tail KLD on the same lists."""
     need_gpu()
     n, v = 64, 248_320
     a, b = synth.logit_rows(synth.LOGITS_BF16_TOPK, range(n), v, dtype="bf16")
-    out = kld.kld_from_logits(to_dev(a, True), to_dev(b, True), None, topk=True)
-    tail = kld.kld_topk_tail(out["ids_ref"], out["lp_ref"], out["ids_cand"], out["lp_cand"], v)
+    want = oracle.score_rows(oracle.bf16_bits_to_f64(a), oracle.bf16_bits_to_f64(b), None, k=64)
+    lists = [want[k] for k in ("ids_ref", "lp_ref", "ids_cand", "lp_cand")]
+    dev = [torch.from_numpy(np.ascontiguousarray(x.view(np.int16) if x.dtype == np.uint16 else x)).cuda()
+           for x in lists]
+    tail = kld.kld_topk_tail(*dev, v)
     torch.cuda.synchronize()
-    ip, lp = out["ids_ref"].cpu().numpy(), out["lp_ref"].cpu().numpy().view(np.uint16)
-    iq, lq = out["ids_cand"].cpu().numpy(), out["lp_cand"].cpu().numpy().view(np.uint16)
-    want = np.array([oracle.tail_kld_row(ip[i], lp[i], iq[i], lq[i], v) for i in range(n)])
-    assert_kl_close(tail.cpu().numpy(), want, "tail")
+    wt = np.array([oracle.tail_kld_row(*(x[i] for x in lists), v) for i in range(n)])
+    assert_kl_close(tail.cpu().numpy(), wt, "tail")
 
 
 def test_topk_tail_hand_example_and_edges():
