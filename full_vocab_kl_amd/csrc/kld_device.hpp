@@ -137,6 +137,83 @@ __device__ inline RowResult finish(const RowState &s) {
   return r;
 }
 
+// ---- f64 accumulation of partial states -------------------------------------
+// The final merges over splits or vocabulary tiles run in f64: partial sums
+// arrive in f32, the running sums, rebase factors and t are kept in f64, so
+// the merge order adds no rounding visible at the f32 result.
+struct RowStateD {
+  float ma, mb;
+  double sa, t, sb;
+  int ia, ib;
+};
+
+__device__ inline RowStateD empty_state_d() {
+  RowStateD s;
+  s.ma = kNegInf; s.mb = kNegInf; s.sa = 0.0; s.t = 0.0; s.sb = 0.0;
+  s.ia = kNoId; s.ib = kNoId;
+  return s;
+}
+
+__device__ inline RowStateD to_d(const RowState &x) {
+  RowStateD s;
+  s.ma = x.ma; s.mb = x.mb; s.sa = x.sa; s.t = x.t; s.sb = x.sb; s.ia = x.ia; s.ib = x.ib;
+  return s;
+}
+
+// exp(m_old - ref(m_new)) in f64: the factor that moves a sum to the new offset.
+__device__ __forceinline__ double rescale_d(float m_old, float m_new) {
+  return m_old == kNegInf ? 0.0 : exp((double)m_old - (double)ref_of(m_new));
+}
+
+__device__ inline void rebase_d(const RowStateD &x, float ma, float mb, double &sa, double &t,
+                                double &sb) {
+  const double fa = rescale_d(x.ma, ma), fb = rescale_d(x.mb, mb);
+  const double da = (double)ref_of(ma) - (double)ref_of(x.ma);
+  const double db = (double)ref_of(mb) - (double)ref_of(x.mb);
+  const double tt = x.sa == 0.0 ? x.t : fma(x.sa, db - da, x.t);
+  sa = x.sa * fa;
+  t = tt * fa;
+  sb = x.sb * fb;
+}
+
+__device__ inline RowStateD merge_d(const RowStateD &x, const RowStateD &y) {
+  RowStateD r;
+  r.ma = fmaxf(x.ma, y.ma);
+  r.mb = fmaxf(x.mb, y.mb);
+  double xs, xt, xb, ys, yt, yb;
+  rebase_d(x, r.ma, r.mb, xs, xt, xb);
+  rebase_d(y, r.ma, r.mb, ys, yt, yb);
+  r.sa = xs + ys;
+  r.t = xt + yt;
+  r.sb = xb + yb;
+  r.ia = beats(x.ma, x.ia, y.ma, y.ia) ? x.ia : y.ia;
+  r.ib = beats(x.mb, x.ib, y.mb, y.ib) ? x.ib : y.ib;
+  return r;
+}
+
+__device__ inline RowResult finish_d(const RowStateD &s, double *lse_a = nullptr,
+                                     double *lse_b = nullptr) {
+  RowResult r;
+  double kl;
+  if (isnan(s.sa) || isnan(s.sb) || !(s.sa > 0.0) || !(s.sb > 0.0)) {
+    kl = __builtin_nan("");
+  } else if (isnan(s.t)) {
+    kl = __builtin_inf();   // 0 * inf: p > 0 where q = 0 (see finish)
+  } else {
+    kl = s.t / s.sa + log(s.sb / s.sa);
+    if (kl < 0.0) kl = 0.0;
+  }
+  const double la = (double)ref_of(s.ma) + log(s.sa), lb = (double)ref_of(s.mb) + log(s.sb);
+  if (lse_a) *lse_a = la;
+  if (lse_b) *lse_b = lb;
+  r.kl = kl == 0.0 ? 0.0f : (float)kl;
+  r.lse_a = (float)la;
+  r.lse_b = (float)lb;
+  r.ia = s.ia == kNoId ? 0 : s.ia;
+  r.ib = s.ib == kNoId ? 0 : s.ib;
+  return r;
+}
+
 // ---- top-k keys ------------------------------------------------------------
 // A 64-bit key per (value, id): order-preserving bits of the value in the high
 // word (-0 folded onto +0), the complemented id in the low word, so a larger

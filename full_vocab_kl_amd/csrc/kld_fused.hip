@@ -516,35 +516,37 @@ __global__ __launch_bounds__(256) void target_logit_kernel(
 }
 
 // Merge the partial states of each position over the vocabulary tiles: block
-// = 32 positions x 8 groups; group g merges tiles g, g + 8, ... in order, then
-// the 8 group states merge in order through LDS.
-constexpr int FP = 32, FG = 8;
+// = 32 positions x 32 groups; group g merges tiles g, g + 32, ... in order,
+// then the 32 group states merge in order through LDS.  (32 groups rather
+// than fewer: the merges are latency-bound, so a window needs ~64K threads.)
+constexpr int FP = 32, FG = 32;
 __global__ __launch_bounds__(FP * FG) void fused_finalize_kernel(
     const float *__restrict__ part, int64_t nvt, int64_t npad, int64_t n,
     const float *__restrict__ zt, const int32_t *__restrict__ target, RowsOut out,
     double *__restrict__ lse_d) {
-  __shared__ RowState red[FG][FP];
+  __shared__ RowStateD red[FG][FP];
   const int pl = threadIdx.x % FP, g = threadIdx.x / FP;
   const int64_t pos = (int64_t)blockIdx.x * FP + pl;
   const int64_t plane = nvt * npad;
-  RowState s = empty_state();
+  RowStateD s = empty_state_d();
   if (pos < n) {
     for (int64_t vt = g; vt < nvt; vt += FG) {
       const float *q = part + vt * npad + pos;
       RowState x;
       x.ma = q[0]; x.sa = q[plane]; x.t = q[2 * plane]; x.mb = q[3 * plane]; x.sb = q[4 * plane];
       x.ia = __float_as_int(q[5 * plane]); x.ib = __float_as_int(q[6 * plane]);
-      s = merge(s, x);
+      s = merge_d(s, to_d(x));
     }
   }
   red[g][pl] = s;
   __syncthreads();
   if (g == 0 && pos < n) {
-    for (int i = 1; i < FG; ++i) s = merge(s, red[i][pl]);
-    const RowResult r = finish(s);
+    for (int i = 1; i < FG; ++i) s = merge_d(s, red[i][pl]);
+    double la, lb;
+    const RowResult r = finish_d(s, &la, &lb);
     if (lse_d) {
-      lse_d[pos] = (double)ref_of(s.ma) + log((double)s.sa);
-      lse_d[n + pos] = (double)ref_of(s.mb) + log((double)s.sb);
+      lse_d[pos] = la;
+      lse_d[n + pos] = lb;
     }
     out.kl[pos] = r.kl;
     if (out.lse_ref) out.lse_ref[pos] = r.lse_a;
@@ -552,8 +554,8 @@ __global__ __launch_bounds__(FP * FG) void fused_finalize_kernel(
     if (out.argmax_ref) out.argmax_ref[pos] = r.ia;
     if (out.argmax_cand) out.argmax_cand[pos] = r.ib;
     if (target) {
-      if (out.nll_ref) out.nll_ref[pos] = (float)((double)r.lse_a - (double)zt[pos]);
-      if (out.nll_cand) out.nll_cand[pos] = (float)((double)r.lse_b - (double)zt[n + pos]);
+      if (out.nll_ref) out.nll_ref[pos] = (float)(la - (double)zt[pos]);
+      if (out.nll_cand) out.nll_cand[pos] = (float)(lb - (double)zt[n + pos]);
     }
   }
 }

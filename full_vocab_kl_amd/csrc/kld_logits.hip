@@ -5,7 +5,7 @@
 // elements into an online RowState (kld_device.hpp), batch by batch: one
 // max per batch, one rebase when the max moves, then one exp2 per element
 // per side.  Lanes merge by butterfly, waves through LDS, and the block
-// writes one partial state; finalize_rows_kernel merges the splits in a
+// writes one partial state; finalize_rows_kernel merges the splits (in f64) in a
 // fixed order and writes the per-position outputs.  HBM-bound: 2 v sizeof(T)
 // bytes per position are read once.
 //
@@ -282,11 +282,10 @@ __global__ __launch_bounds__(256) void finalize_rows_kernel(
     float *__restrict__ target_lp) {
   const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (row >= n) return;
-  RowState s = part[row * splits];
-  for (int i = 1; i < splits; ++i) s = merge(s, part[row * splits + i]);
-  const RowResult r = finish(s);
-  const double la = (double)ref_of(s.ma) + log((double)s.sa);
-  const double lb = (double)ref_of(s.mb) + log((double)s.sb);
+  RowStateD s = to_d(part[row * splits]);
+  for (int i = 1; i < splits; ++i) s = merge_d(s, to_d(part[row * splits + i]));
+  double la, lb;
+  const RowResult r = finish_d(s, &la, &lb);
   if (lse_d) { lse_d[row] = la; lse_d[n + row] = lb; }
   if (out.kl) out.kl[row] = r.kl;
   if (out.lse_ref) out.lse_ref[row] = r.lse_a;
