@@ -65,6 +65,24 @@ static_assert(ULOADS == 8 && BV == UROWS && 2 * BP == UROWS, "tile shape");
 __device__ __forceinline__ int swz_key(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int swz(int r, int c) { return r * CH + (c ^ swz_key(r)); }
 
+// f32 max / median of three without operand canonicalisation (fmaxf in IEEE
+// mode quiets signalling NaNs first; values produced by MFMA never are).
+__device__ __forceinline__ float vmax2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float vmed3(float a, float b, float c) {
+  float r;
+  asm("v_med3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // Workgroup execution barrier without the memory fence of __syncthreads();
 // the memory clobber keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
@@ -373,23 +391,42 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
         xs[1][i] = acc[vs][pg][1][i];
         asm volatile("" : "+v"(xs[0][i]), "+v"(xs[1][i]));
       }
+      // Group maxima by v_max3 (the accumulators never hold signalling NaNs,
+      // so the canonicalising moves that fmaxf implies are not needed); with
+      // top-k the second value by v_med3 (m1 >= m2: med3(m1, m2, x) is the
+      // new second largest).  Then the lowest id of each side's maximum, the
+      // two sides' compare chains interleaved.
       float m1[2], m2[2];
+#pragma unroll
+      for (int sd = 0; sd < 2; ++sd) {
+        const float *x = xs[sd];
+        if constexpr (TOPK) {
+          float x1 = kNegInf, x2 = kNegInf;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            x2 = vmed3(x1, x2, x[i]);
+            x1 = vmax2(x1, x[i]);
+          }
+          m1[sd] = x1; m2[sd] = x2;
+        } else {
+          const float a = vmax3(x[0], x[1], x[2]), b = vmax3(x[3], x[4], x[5]);
+          const float c = vmax3(x[6], x[7], x[8]), d = vmax3(x[9], x[10], x[11]);
+          const float e = vmax3(x[12], x[13], x[14]);
+          m1[sd] = vmax2(vmax3(a, b, c), vmax3(d, e, x[15]));
+          m2[sd] = kNegInf;
+        }
+      }
+      int k[2] = {kNoId, kNoId};
+#pragma unroll
+      for (int i = 15; i >= 0; --i)
+#pragma unroll
+        for (int sd = 0; sd < 2; ++sd)
+          if (xs[sd][i] == m1[sd]) k[sd] = 32 * vs + 8 * (i >> 2) + (i & 3);
       int id[2];
 #pragma unroll
       for (int sd = 0; sd < 2; ++sd) {
-        float x1 = kNegInf, x2 = kNegInf;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float x = xs[sd][i];
-          if (TOPK) x2 = fmaxf(x2, fminf(x1, x));
-          x1 = fmaxf(x1, x);
-        }
-        int k = kNoId;
-#pragma unroll
-        for (int i = 15; i >= 0; --i)
-          if (xs[sd][i] == x1) k = 32 * vs + 8 * (i >> 2) + (i & 3);
-        m1[sd] = x1; m2[sd] = x2;
-        id[sd] = x1 == kNegInf ? kNoId : (int)(vb + k);
+        const float x1 = m1[sd], x2 = m2[sd];
+        id[sd] = x1 == kNegInf ? kNoId : (int)(vb + k[sd]);
         if constexpr (TOPK) {   // (positions n .. npad - 1 are padding: no branch needed)
           ckeys[(((int64_t)sd * nvt + vt) * npad + pos) * 16 + (wv * 2 + fh) * 4 + vs] =
               x1 == kNegInf ? 0ull : topk_key(x1, id[sd]);
