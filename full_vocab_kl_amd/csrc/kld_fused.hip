@@ -623,7 +623,9 @@ constexpr int TK = 256;
 // K keys each thread holds (0 = no key; nonzero keys are distinct).  Radix
 // select, 8 bits per pass from the top: a 256-bin LDS histogram of the keys
 // that match the digits fixed so far, and wave 0 finds the bin that holds the
-// wanted rank.  Returns the 64th largest key, or 0 when fewer than 64 keys are
+// wanted rank; the passes stop early once that bin holds exactly the keys
+// still wanted (then every key at or above it is selected and the smallest of
+// them is the 64th).  Returns the 64th largest key, or 0 when fewer than 64 keys are
 // nonzero; stores the selected keys (every nonzero key when fewer than 64) in
 // top[0..63], zero-filled, in no particular order.
 template <int K>
@@ -633,16 +635,17 @@ __device__ uint64_t select64(const uint64_t (&k)[K], uint64_t *top, uint32_t *hi
   const int tid = threadIdx.x;
   uint64_t prefix = 0;
   uint32_t need = 64;
+  int shift = 64;        // keys are selected by their bits at and above `shift`
   bool found = true;
   for (int pass = 0; pass < 8; ++pass) {
-    const int shift = 56 - 8 * pass;
+    const int sh8 = 56 - 8 * pass;
     hist[tid] = 0;
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < K; ++q) {
       const uint64_t x = k[q];
-      if (x != 0ull && (pass == 0 || (x >> (shift + 8)) == (prefix >> (shift + 8))))
-        atomicAdd(&hist[(x >> shift) & 255], 1u);
+      if (x != 0ull && (pass == 0 || (x >> (sh8 + 8)) == (prefix >> (sh8 + 8))))
+        atomicAdd(&hist[(x >> sh8) & 255], 1u);
     }
     __syncthreads();
     if (tid < 64) {
@@ -658,10 +661,12 @@ __device__ uint64_t select64(const uint64_t (&k)[K], uint64_t *top, uint32_t *hi
       }
       uint32_t above = suf - s4;
       int bin = -1;
-      uint32_t left = 0;
+      uint32_t left = 0, cnt = 0;
 #pragma unroll
       for (int bq = 3; bq >= 0; --bq) {
-        if (bin < 0 && above < need && above + c[bq] >= need) { bin = 4 * tid + bq; left = need - above; }
+        if (bin < 0 && above < need && above + c[bq] >= need) {
+          bin = 4 * tid + bq; left = need - above; cnt = c[bq];
+        }
         above += c[bq];
       }
       const uint64_t m = __ballot(bin >= 0);
@@ -670,25 +675,36 @@ __device__ uint64_t select64(const uint64_t (&k)[K], uint64_t *top, uint32_t *hi
       } else {
         const int src = __ffsll((long long)m) - 1;
         const int bb = __shfl(bin, src);
-        const uint32_t ll = __shfl(left, src);
-        if (tid == 0) { sh[0] = (uint32_t)bb; sh[1] = ll; }
+        const uint32_t ll = __shfl(left, src), cc = __shfl(cnt, src);
+        if (tid == 0) { sh[0] = (uint32_t)bb; sh[1] = ll; sh[3] = cc; }
       }
     }
     __syncthreads();
     const uint32_t dd = sh[0];
     need = sh[1];
+    const uint32_t bucket = sh[3];
     __syncthreads();
     if (dd == 0xffffffffu) { found = false; break; }
-    prefix |= (uint64_t)dd << shift;
+    prefix |= (uint64_t)dd << sh8;
+    shift = sh8;
+    if (bucket == need) break;   // every key of the bucket is selected: the set is fixed
   }
-  const uint64_t T = found ? prefix : 0ull;
-  if (tid == 0) sh[2] = 0;
+  // Selected: the keys whose bits at and above `shift` reach the prefix (all
+  // nonzero keys when fewer than 64 exist).  T = the smallest selected key.
+  if (tid == 0) { sh[2] = 0; sh[4] = 0xffffffffu; sh[5] = 0xffffffffu; }
   __syncthreads();
+  unsigned long long *tmin = reinterpret_cast<unsigned long long *>(sh + 4);
 #pragma unroll
-  for (int q = 0; q < K; ++q)
-    if (k[q] != 0ull && k[q] >= T) top[atomicAdd(&sh[2], 1u)] = k[q];
+  for (int q = 0; q < K; ++q) {
+    const uint64_t x = k[q];
+    if (x != 0ull && (!found || (shift == 64 ? true : (x >> shift) >= (prefix >> shift)))) {
+      top[atomicAdd(&sh[2], 1u)] = x;
+      atomicMin(tmin, (unsigned long long)x);
+    }
+  }
   __syncthreads();
   const uint32_t cnt = sh[2];
+  const uint64_t T = found ? (uint64_t)*tmin : 0ull;
   for (uint32_t i = cnt + tid; i < 64; i += TK) top[i] = 0ull;
   __syncthreads();
   return T;
@@ -709,7 +725,7 @@ __global__ __launch_bounds__(TK) void fused_topk_kernel(
 
   __shared__ uint64_t buf[64 + TK];
   __shared__ uint32_t hist[256];
-  __shared__ uint32_t sh[4];
+  __shared__ __align__(8) uint32_t sh[6];
   __shared__ int tiles[64];
   __shared__ int sh_nflag;
   __shared__ int flagged[TK];
