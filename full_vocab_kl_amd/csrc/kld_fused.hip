@@ -552,33 +552,67 @@ __global__ __launch_bounds__(256) void target_logit_kernel(
   if (lane == 0) { zt[pos] = sr; zt[n + pos] = sc; }
 }
 
-// Merge the partial states of each position over the vocabulary tiles: block
-// = 32 positions x 32 groups; group g merges tiles g, g + 32, ... in order,
-// then the 32 group states merge in order through LDS.  (32 groups rather
-// than fewer: the merges are latency-bound, so a window needs ~64K threads.)
-constexpr int FP = 32, FG = 32;
+// Merge the partial states of each position over the vocabulary tiles.
+// Block = 8 positions x 32 groups; group g takes tiles g, g + 32, ...  Pass 1:
+// the maxima (and lowest-id argmax) of both sides over all tiles.  Pass 2:
+// every tile's sums moved to those maxima (one f64 exp per side and tile, no
+// running rebase) and added in f64; the 32 group results are combined in a
+// fixed order through LDS.  (Many groups and small blocks: a window must
+// spread over every CU.)
+constexpr int FP = 8, FG = 32;
 __global__ __launch_bounds__(FP * FG) void fused_finalize_kernel(
     const float *__restrict__ part, int64_t nvt, int64_t npad, int64_t n,
     const float *__restrict__ zt, const int32_t *__restrict__ target, RowsOut out,
     double *__restrict__ lse_d) {
-  __shared__ RowStateD red[FG][FP];
+  struct Mx { float ma, mb; int ia, ib; };
+  struct Sm { double sa, t, sb; };
+  __shared__ Mx rm[FG][FP];
+  __shared__ Sm rs[FG][FP];
   const int pl = threadIdx.x % FP, g = threadIdx.x / FP;
   const int64_t pos = (int64_t)blockIdx.x * FP + pl;
   const int64_t plane = nvt * npad;
-  RowStateD s = empty_state_d();
-  if (pos < n) {
+  const bool live = pos < n;
+  // pass 1: maxima
+  Mx m = {kNegInf, kNegInf, kNoId, kNoId};
+  if (live) {
     for (int64_t vt = g; vt < nvt; vt += FG) {
       const float *q = part + vt * npad + pos;
-      RowState x;
-      x.ma = q[0]; x.sa = q[plane]; x.t = q[2 * plane]; x.mb = q[3 * plane]; x.sb = q[4 * plane];
-      x.ia = __float_as_int(q[5 * plane]); x.ib = __float_as_int(q[6 * plane]);
-      s = merge_d(s, to_d(x));
+      const float xa = q[0], xb = q[3 * plane];
+      const int ja = __float_as_int(q[5 * plane]), jb = __float_as_int(q[6 * plane]);
+      if (beats(xa, ja, m.ma, m.ia)) { m.ma = xa; m.ia = ja; }
+      if (beats(xb, jb, m.mb, m.ib)) { m.mb = xb; m.ib = jb; }
     }
   }
-  red[g][pl] = s;
+  rm[g][pl] = m;
   __syncthreads();
-  if (g == 0 && pos < n) {
-    for (int i = 1; i < FG; ++i) s = merge_d(s, red[i][pl]);
+  m = rm[0][pl];
+  for (int i = 1; i < FG; ++i) {
+    const Mx o = rm[i][pl];
+    if (beats(o.ma, o.ia, m.ma, m.ia)) { m.ma = o.ma; m.ia = o.ia; }
+    if (beats(o.mb, o.ib, m.mb, m.ib)) { m.mb = o.mb; m.ib = o.ib; }
+  }
+  // pass 2: sums at the final offsets
+  const double ra = (double)ref_of(m.ma), rb = (double)ref_of(m.mb);
+  Sm sm = {0.0, 0.0, 0.0};
+  if (live) {
+    for (int64_t vt = g; vt < nvt; vt += FG) {
+      const float *q = part + vt * npad + pos;
+      const float xa = q[0], xsa = q[plane], xt = q[2 * plane], xb = q[3 * plane], xsb = q[4 * plane];
+      const double oa = (double)ref_of(xa), ob = (double)ref_of(xb);
+      const double fa = xa == kNegInf ? 0.0 : exp(oa - ra), fb = xb == kNegInf ? 0.0 : exp(ob - rb);
+      const double tt = xsa == 0.f ? (double)xt : fma((double)xsa, (rb - ob) - (ra - oa), (double)xt);
+      sm.sa += (double)xsa * fa;
+      sm.t += tt * fa;
+      sm.sb += (double)xsb * fb;
+    }
+  }
+  rs[g][pl] = sm;
+  __syncthreads();
+  if (g == 0 && live) {
+    RowStateD s;
+    s.ma = m.ma; s.mb = m.mb; s.ia = m.ia; s.ib = m.ib;
+    s.sa = rs[0][pl].sa; s.t = rs[0][pl].t; s.sb = rs[0][pl].sb;
+    for (int i = 1; i < FG; ++i) { s.sa += rs[i][pl].sa; s.t += rs[i][pl].t; s.sb += rs[i][pl].sb; }
     double la, lb;
     const RowResult r = finish_d(s, &la, &lb);
     if (lse_d) {

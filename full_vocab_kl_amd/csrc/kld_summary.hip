@@ -5,7 +5,7 @@
 // is exp of the mean NLL of the true next token).
 //
 // Sums are taken in f64 in a fixed order (per-thread strided partials, an LDS
-// tree per block, block partials summed in order), so results are
+// tree per block, block partials by strided sums and a fixed LDS tree), so results are
 // reproducible.  Quantiles interpolate linearly between exact order
 // statistics (h = q (n - 1)); each order statistic is found by a 4-pass MSB
 // radix select on the f32 bit patterns (KL >= +0, so unsigned bit order is
@@ -93,31 +93,64 @@ __global__ void summary_init_kernel(uint32_t *hist, int count, uint32_t *prefix,
   }
 }
 
-// After pass `pass`: fix each rank's digit.  After the last pass, also write
+// After pass `pass`: fix each rank's digit (one wave per rank: lane l owns
+// bins 4 l .. 4 l + 3, a shuffle scan counts the keys below them, and the lane
+// whose bins hold the rank fixes the digit).  After the last pass, also write
 // the summary record.
-__global__ void summary_scan_kernel(int pass, int nranks, const uint32_t *__restrict__ hist,
-                                    uint32_t *__restrict__ prefix, uint32_t *__restrict__ rank,
-                                    int nblocks, const SumPart *__restrict__ parts, int64_t n,
-                                    bool have_top1, bool have_nll, SummaryQuantiles qs,
-                                    double *__restrict__ out) {
-  const int r = threadIdx.x;
+constexpr int SCAN_T = 256;
+__global__ __launch_bounds__(SCAN_T) void summary_scan_kernel(
+    int pass, int nranks, const uint32_t *__restrict__ hist, uint32_t *__restrict__ prefix,
+    uint32_t *__restrict__ rank, int nblocks, const SumPart *__restrict__ parts, int64_t n,
+    bool have_top1, bool have_nll, SummaryQuantiles qs, double *__restrict__ out) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int shift = 24 - 8 * pass;
-  if (r < nranks) {
+  for (int r = wave; r < nranks; r += SCAN_T / 64) {
     const uint32_t *h = hist + r * 256;
-    uint32_t k = rank[r], below = 0;
-    int dig = 255;
-    for (int b = 0; b < 256; ++b) {
-      if (below + h[b] > k) { dig = b; break; }
-      below += h[b];
+    uint32_t c[4], s4 = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) { c[b] = h[4 * lane + b]; s4 += c[b]; }
+    uint32_t inc = s4;   // inclusive prefix over lanes 0..lane
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t t = __shfl_up(inc, o);
+      if (lane >= o) inc += t;
     }
-    prefix[r] |= (uint32_t)dig << shift;
-    rank[r] = k - below;
+    const uint32_t k = rank[r];
+    uint32_t below = inc - s4;
+    int dig = -1;
+    uint32_t bel = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      if (dig < 0 && below + c[b] > k) { dig = 4 * lane + b; bel = below; }
+      below += c[b];
+    }
+    const uint64_t m = __ballot(dig >= 0);
+    if (m != 0ull) {
+      const int src = __ffsll((long long)m) - 1;
+      const int dd = __shfl(dig, src);
+      const uint32_t bb = __shfl(bel, src);
+      if (lane == 0) {
+        prefix[r] |= (uint32_t)dd << shift;
+        rank[r] = k - bb;
+      }
+    } else if (lane == 0) {   // rank >= count (cannot happen for a valid rank)
+      prefix[r] |= 255u << shift;
+    }
   }
   if (pass != 3) return;
+  // block partials: thread i sums partials i, i + SCAN_T, ... in order, then a
+  // fixed tree through LDS (deterministic)
+  __shared__ SumPart red[SCAN_T];
+  SumPart s = {0.0, 0.0, 0.0, 0ull, 0ull};
+  for (int b = threadIdx.x; b < nblocks; b += SCAN_T) s = add(s, parts[b]);
+  red[threadIdx.x] = s;
   __syncthreads();
+  for (int w = SCAN_T / 2; w >= 1; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] = add(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
   if (threadIdx.x != 0) return;
-  SumPart s = parts[0];
-  for (int b = 1; b < nblocks; ++b) s = add(s, parts[b]);
+  s = red[0];
   const double nan = __builtin_nan(""), dn = (double)n;
   out[0] = s.kl / dn;
   out[1] = have_top1 ? (double)s.top1 / dn : nan;
@@ -161,7 +194,7 @@ hipError_t launch_summary(const SummaryArgs &a, void *ws) {
     hipLaunchKernelGGL(summary_hist_kernel, dim3(nb), dim3(ST), 0, a.stream, a.kl, a.argmax_ref,
                        a.argmax_cand, a.nll_ref, a.nll_cand, a.n, pass, R, prefix, h, parts);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(summary_scan_kernel, dim3(1), dim3(64), 0, a.stream, pass, R, h, prefix,
+    hipLaunchKernelGGL(summary_scan_kernel, dim3(1), dim3(SCAN_T), 0, a.stream, pass, R, h, prefix,
                        rank, nb, parts, a.n, a.argmax_ref != nullptr, a.nll_ref != nullptr, a.qs,
                        a.out);
     if ((e = hipGetLastError()) != hipSuccess) return e;
