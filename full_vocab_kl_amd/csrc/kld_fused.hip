@@ -119,7 +119,16 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
                        int64_t npad, int64_t nvt, float *__restrict__ part,
                        uint64_t *__restrict__ ckeys, float *__restrict__ resid,
                        uint64_t *__restrict__ rinfo, uint64_t *__restrict__ tkeys) {
-  extern __shared__ u32x4 smem[];   // [NSLOT][UCHUNKS]
+  // The five ring slots (160 KB, the whole LDS) are separate LDS objects, so
+  // that the compiler knows the loads into one slot never touch the fragment
+  // reads of another and can interleave the two (with one array it kept
+  // every read ahead of every later load).
+  __shared__ u32x4 lds0[UCHUNKS], lds1[UCHUNKS], lds2[UCHUNKS], lds3[UCHUNKS], lds4[UCHUNKS];
+  auto slot_ptr = [&](int slot) -> u32x4 * {
+    return slot == 0 ? lds0 : slot == 1 ? lds1 : slot == 2 ? lds2 : slot == 3 ? lds3 : lds4;
+  };
+  static_assert(sizeof(u32x4) * UCHUNKS * NSLOT == kFusedLds, "ring = all of LDS");
+  u32x4 *const smem = lds0;   // epilogue exchange area (after the loop)
 
   const int L = logical_block((int)blockIdx.x, (int)gridDim.x);
   const int vt = L / npt, pt = L % npt;
@@ -168,7 +177,7 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>((H ? hbase : wbase) + (int64_t)st * BK), (short)0,
         __builtin_amdgcn_readfirstlane(rem > 0 ? rem : 0), 0x00020000);
-    u32x4 *dst = smem + slot * UCHUNKS + wave_u * (UCHUNKS / 4);
+    u32x4 *dst = slot_ptr(slot) + wave_u * (UCHUNKS / 4);
 #pragma unroll
     for (int j = j0; j < j0 + cnt; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -206,17 +215,39 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
       offA[ks][x] = (uint32_t)(ra * CH + ((2 * ks + fh) ^ swz_key(ra))) * 16;
       offB[ks][x] = (uint32_t)(rb * CH + ((2 * ks + fh) ^ swz_key(rb))) * 16;
     }
+  // The LDS read offset field reaches 64 KB past the address register, so
+  // every lane offset is also kept biased by 64 KB and 128 KB (opaque to the
+  // compiler, which would otherwise fold the bias back into a VALU op per
+  // read): a read of slot k uses the copy biased by 64 KB * (k / 2), and the
+  // rest of the slot base (slots are laid out in order, 32 KB apart) is an
+  // immediate.  Any other layout only costs the VALU ops back.
+  uint32_t offA1[4][2], offB1[4][2], offA2[4][2], offB2[4][2];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      offA1[ks][x] = offA[ks][x] + 65536u;
+      offB1[ks][x] = offB[ks][x] + 65536u;
+      offA2[ks][x] = offA[ks][x] + 131072u;
+      offB2[ks][x] = offB[ks][x] + 131072u;
+      asm volatile("" : "+v"(offA1[ks][x]), "+v"(offB1[ks][x]), "+v"(offA2[ks][x]), "+v"(offB2[ks][x]));
+    }
+  auto lane_off = [&](bool a, int slot, int ks, int x) -> uint32_t {
+    const int g = slot >> 1;
+    return a ? (g == 0 ? offA[ks][x] : g == 1 ? offA1[ks][x] - 65536u : offA2[ks][x] - 131072u)
+             : (g == 0 ? offB[ks][x] : g == 1 ? offB1[ks][x] - 65536u : offB2[ks][x] - 131072u);
+  };
   auto load_frags = [&](int slot_w, int slot_h, int ks, Frags &f) {
-    const char *sw = reinterpret_cast<const char *>(smem + slot_w * UCHUNKS);
-    const char *sh = reinterpret_cast<const char *>(smem + slot_h * UCHUNKS);
+    const char *sw = reinterpret_cast<const char *>(slot_ptr(slot_w));
+    const char *sh = reinterpret_cast<const char *>(slot_ptr(slot_h));
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg)
 #pragma unroll
       for (int sd = 0; sd < 2; ++sd)
-        f.b[pg][sd] = *reinterpret_cast<const bf16x8 *>(sh + offB[ks][pg] + sd * (BP * CH * 16));
+        f.b[pg][sd] = *reinterpret_cast<const bf16x8 *>(sh + lane_off(false, slot_h, ks, pg) + sd * (BP * CH * 16));
 #pragma unroll
     for (int vs = 0; vs < 4; ++vs)
-      f.a[vs] = *reinterpret_cast<const bf16x8 *>(sw + offA[ks][vs & 1] + (vs >> 1) * (64 * CH * 16));
+      f.a[vs] = *reinterpret_cast<const bf16x8 *>(sw + lane_off(true, slot_w, ks, vs & 1) + (vs >> 1) * (64 * CH * 16));
   };
   auto mfma = [&](const Frags &f) {
 #pragma unroll
@@ -921,22 +952,17 @@ FusedGeom fused_geom(int64_t n, int64_t v) {
 hipError_t launch_fused(const FusedArgs &a, const FusedWs &w) {
   const FusedGeom g = fused_geom(a.n, a.v);
   const bool tk = a.topk.ids_ref || a.topk.lp_ref || a.topk.ids_cand || a.topk.lp_cand;
-  const void *kern = tk ? (const void *)fused_head_kernel<true> : (const void *)fused_head_kernel<false>;
-  // 128 KB of LDS per block (above the 64 KB default): set on every call so
-  // that no library state is kept; the call is host-side and cheap.
-  hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)kFusedLds);
-  if (e != hipSuccess) return e;
+  hipError_t e;   // the kernel's 160 KB of LDS is static: no launch attribute to set
   const int64_t nblocks = g.nvt * g.npt;
   e = record(a.ev.start, a.stream);
   if (e != hipSuccess) return e;
   if (tk)
     hipLaunchKernelGGL(fused_head_kernel<true>, dim3((unsigned)nblocks), dim3(NT),
-                       kFusedLds, a.stream, a.W, a.h_ref, a.h_cand, a.v, a.d,
+                       0, a.stream, a.W, a.h_ref, a.h_cand, a.v, a.d,
                        a.n, (int)g.npt, g.npad, g.nvt, w.part, w.ckeys, w.resid, w.rinfo, w.tkeys);
   else
     hipLaunchKernelGGL(fused_head_kernel<false>, dim3((unsigned)nblocks), dim3(NT),
-                       kFusedLds, a.stream, a.W, a.h_ref, a.h_cand, a.v, a.d,
+                       0, a.stream, a.W, a.h_ref, a.h_cand, a.v, a.d,
                        a.n, (int)g.npt, g.npad, g.nvt, w.part, nullptr, nullptr, nullptr, nullptr);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
