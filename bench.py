@@ -37,7 +37,8 @@ def _args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="fused_window", choices=["fused_window", "logits_f32"])
+    p.add_argument("--workload", default="fused_window",
+                   choices=["fused_window", "logits_f32", "logits_bf16_topk"])
     p.add_argument("--cpu-sample", type=int, default=None,
                    help="positions the CPU oracle scores for the baseline (0 = skip)")
     p.add_argument("--no-secondary", action="store_true",
@@ -48,7 +49,8 @@ def _args():
 
 
 KERNEL_SOURCES = {"fused_head_kernel<true>": "full_vocab_kl_amd/csrc/kld_fused.hip",
-                  "logits_partial_kernel_f32": "full_vocab_kl_amd/csrc/kld_logits.hip"}
+                  "logits_partial_kernel_f32": "full_vocab_kl_amd/csrc/kld_logits.hip",
+                  "logits_partial_kernel_bf16_topk": "full_vocab_kl_amd/csrc/kld_logits.hip"}
 
 
 def _traffic(kernel_key):
@@ -238,6 +240,79 @@ def logits_f32(steps, warmup, cpu_sample):
     return res
 
 
+def logits_bf16_topk(steps, warmup, cpu_sample):
+    """One 4096-row batch of the bf16 top-64 workload: full KL + argmax + lse
+    and both sides' top-64 export in one pass over the logits, then the
+    top-64 + tail-bucket KLD and the summary of the batch."""
+    import numpy as np
+    import torch
+
+    import full_vocab_kl_amd as kld
+    import synth
+
+    n, v = 4096, synth.VOCAB
+    wl = synth.LOGITS_BF16_TOPK
+    a_np, b_np = synth.logit_rows(wl, range(n), v, dtype="bf16")
+    dev = torch.device("cuda:0")
+    bf = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    ra, rb = bf(a_np), bf(b_np)   # 2 x 2.03 GB: far beyond the 256 MB cache
+    ws = torch.empty(kld.kld_workspace_size(0, n, v, 0, 1), dtype=torch.uint8, device=dev)
+    ws_s = torch.empty(kld.kld_workspace_size(3, n, 0), dtype=torch.uint8, device=dev)
+    summ = torch.empty(8 + len(QUANTILES), dtype=torch.float64, device=dev)
+    tail = torch.empty(n, dtype=torch.float32, device=dev)
+    out = None
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+
+    def step(ev=None):
+        nonlocal out
+        out = kld.kld_from_logits(ra, rb, None, topk=True, ws=ws, out=out, events=ev)
+        kld.kld_topk_tail(out["ids_ref"], out["lp_ref"], out["ids_cand"], out["lp_cand"], v, out=tail)
+        kld.kld_summary(out["kl"], out["argmax_ref"], out["argmax_cand"], quantiles=QUANTILES,
+                        ws=ws_s, out=summ)   # no targets in this workload: no NLL
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kms = [x.elapsed_time(y) for x, y in evs]
+    kernel_ms = sum(kms) / len(kms)
+    nbytes = 4.0 * n * v
+    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+    res = {
+        "value": n * steps / elapsed, "unit": "positions/s", "ms_per_step": elapsed * 1e3 / steps,
+        "dtype": "bf16",
+        "config": {"workload": "kld_from_logits (+top-64 export) + kld_topk_tail + kld_summary: "
+                               "one 4096-row batch, V=248,320 bf16 logits",
+                   "positions": n, "V": v},
+        "roofline": {"bound": "hbm", "kernel": "logits_partial_kernel", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": _traffic("logits_partial_kernel_bf16_topk"),
+                     "kernel_ms": round(kernel_ms, 4),
+                     "algorithmic": f"4*N*V = {nbytes:.4e} bytes per launch"},
+        "result": {"mean_kl": float(out["kl"].double().mean()),
+                   "mean_tail_kl": float(tail.double().mean())},
+    }
+    if cpu_sample:
+        import oracle
+        rows = np.arange(min(cpu_sample, n))
+        t0 = time.perf_counter()
+        za, zb = oracle.bf16_bits_to_f64(a_np[rows]), oracle.bf16_bits_to_f64(b_np[rows])
+        s = oracle.score_rows(za, zb, None, k=64)
+        for i in range(len(rows)):
+            oracle.tail_kld_row(s["ids_ref"][i], s["lp_ref"][i], s["ids_cand"][i], s["lp_cand"][i], v)
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": len(rows) / dt, "unit": "positions/s", "cores": _cores(),
+                               "kind": "oracle",
+                               "sample": f"first {len(rows)} rows (KL, argmax, lse, top-64 + tail "
+                                         f"KLD), {dt:.1f} s"}
+    return res
+
+
 def _cores():
     try:
         import numpy  # noqa: F401
@@ -267,6 +342,9 @@ def main():
     if args.workload == "fused_window":
         cpu = 128 if args.cpu_sample is None else args.cpu_sample
         res = fused_window(args.steps, args.warmup, cpu)
+    elif args.workload == "logits_bf16_topk":
+        cpu = 64 if args.cpu_sample is None else args.cpu_sample
+        res = logits_bf16_topk(args.steps, args.warmup, cpu)
     else:
         cpu = 64 if args.cpu_sample is None else args.cpu_sample
         res = logits_f32(args.steps, args.warmup, cpu)
@@ -280,10 +358,13 @@ def main():
     if "result" in res:
         line["result"] = res["result"]
     if args.workload == "fused_window" and not args.no_secondary:
-        sec = logits_f32(max(5, args.steps), args.warmup, 0)
-        line["secondary"] = {"workload": sec["config"]["workload"], "value": round(sec["value"], 1),
-                             "unit": sec["unit"], "ms_per_step": round(sec["ms_per_step"], 4),
-                             "roofline": sec["roofline"]}
+        line["secondary"] = []
+        for fn in (logits_f32, logits_bf16_topk):
+            sec = fn(max(5, args.steps), args.warmup, 0)
+            line["secondary"].append({"workload": sec["config"]["workload"],
+                                      "value": round(sec["value"], 1), "unit": sec["unit"],
+                                      "ms_per_step": round(sec["ms_per_step"], 4),
+                                      "roofline": sec["roofline"]})
     print(json.dumps(line), flush=True)
 
 

@@ -45,6 +45,9 @@ LogitsGeom logits_geom(int64_t n, int64_t v) {
   int64_t max_splits = (v + 4095) / 4096;
   if (max_splits < 1) max_splits = 1;
   if (want > max_splits) want = max_splits;
+  // a split spans at most kMaxChunk ids (its byte offsets fit 32 bits)
+  const int64_t min_splits = (v + kMaxChunk - 1) / kMaxChunk;
+  if (want < min_splits) want = min_splits;
   if (want < 1) want = 1;
   int64_t chunk = (v + want - 1) / want;
   chunk = (chunk + 7) / 8 * 8;

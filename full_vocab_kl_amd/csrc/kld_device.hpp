@@ -98,7 +98,7 @@ __device__ __forceinline__ RowState shfl_xor_state(const RowState &s, int mask) 
 
 // Butterfly over the 64 lanes of a wave: every lane ends with the merge of
 // all 64 states.  The pairing order is fixed, so the result is reproducible.
-__device__ inline RowState wave_merge(RowState s) {
+__device__ __forceinline__ RowState wave_merge(RowState s) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {
     RowState o = shfl_xor_state(s, m);
@@ -248,6 +248,125 @@ __device__ void bitonic_desc(uint64_t *buf, int n) {
       __syncthreads();
     }
   }
+}
+
+
+// Descending bitonic sort of one value per lane across the 64 lanes of a wave
+// (lane 0 ends with the largest).
+__device__ __forceinline__ float wave_sort_desc(float x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const float o = __shfl_xor(x, j);
+      const bool desc = (lane & k) == 0, lower = (lane & j) == 0;
+      x = (desc == lower) ? fmaxf(x, o) : fminf(x, o);
+    }
+  return x;
+}
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint64_t o = __shfl_xor(x, j);
+      const bool desc = (lane & k) == 0, lower = (lane & j) == 0;
+      x = (desc == lower) ? (o > x ? o : x) : (o < x ? o : x);
+    }
+  return x;
+}
+
+// Block-wide (256 threads) selection of the 64 largest nonzero keys among the
+// K keys each thread holds (0 = no key; nonzero keys are distinct).  Radix
+// select, 8 bits per pass from the top: a 256-bin LDS histogram of the keys
+// that match the digits fixed so far, and wave 0 finds the bin that holds the
+// wanted rank; the passes stop early once that bin holds exactly the keys
+// still wanted (then every key at or above it is selected and the smallest of
+// them is the 64th).  Returns the 64th largest key, or 0 when fewer than 64 keys are
+// nonzero; stores the selected keys (every nonzero key when fewer than 64) in
+// top[0..63], zero-filled, in no particular order.  LDS scratch: hist[256],
+// sh[6] 8-byte aligned; every thread of the block must call it.
+template <int K>
+__device__ __forceinline__ uint64_t block_select64(const uint64_t (&k)[K], uint64_t *top, uint32_t *hist,
+                                   uint32_t *sh) {
+  const int tid = threadIdx.x;
+  uint64_t prefix = 0;
+  uint32_t need = 64;
+  int shift = 64;        // keys are selected by their bits at and above `shift`
+  bool found = true;
+  for (int pass = 0; pass < 8; ++pass) {
+    const int sh8 = 56 - 8 * pass;
+    hist[tid] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < K; ++q) {
+      const uint64_t x = k[q];
+      if (x != 0ull && (pass == 0 || (x >> (sh8 + 8)) == (prefix >> (sh8 + 8))))
+        atomicAdd(&hist[(x >> sh8) & 255], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane l owns bins 4 l .. 4 l + 3; count the keys in higher bins
+      uint32_t c[4], s4 = 0;
+#pragma unroll
+      for (int bq = 0; bq < 4; ++bq) { c[bq] = hist[4 * tid + bq]; s4 += c[bq]; }
+      uint32_t suf = s4;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_down(suf, o);
+        if (tid + o < 64) suf += t;
+      }
+      uint32_t above = suf - s4;
+      int bin = -1;
+      uint32_t left = 0, cnt = 0;
+#pragma unroll
+      for (int bq = 3; bq >= 0; --bq) {
+        if (bin < 0 && above < need && above + c[bq] >= need) {
+          bin = 4 * tid + bq; left = need - above; cnt = c[bq];
+        }
+        above += c[bq];
+      }
+      const uint64_t m = __ballot(bin >= 0);
+      if (m == 0ull) {
+        if (tid == 0) sh[0] = 0xffffffffu;
+      } else {
+        const int src = __ffsll((long long)m) - 1;
+        const int bb = __shfl(bin, src);
+        const uint32_t ll = __shfl(left, src), cc = __shfl(cnt, src);
+        if (tid == 0) { sh[0] = (uint32_t)bb; sh[1] = ll; sh[3] = cc; }
+      }
+    }
+    __syncthreads();
+    const uint32_t dd = sh[0];
+    need = sh[1];
+    const uint32_t bucket = sh[3];
+    __syncthreads();
+    if (dd == 0xffffffffu) { found = false; break; }
+    prefix |= (uint64_t)dd << sh8;
+    shift = sh8;
+    if (bucket == need) break;   // every key of the bucket is selected: the set is fixed
+  }
+  // Selected: the keys whose bits at and above `shift` reach the prefix (all
+  // nonzero keys when fewer than 64 exist).  T = the smallest selected key.
+  if (tid == 0) { sh[2] = 0; sh[4] = 0xffffffffu; sh[5] = 0xffffffffu; }
+  __syncthreads();
+  unsigned long long *tmin = reinterpret_cast<unsigned long long *>(sh + 4);
+#pragma unroll
+  for (int q = 0; q < K; ++q) {
+    const uint64_t x = k[q];
+    if (x != 0ull && (!found || (shift == 64 ? true : (x >> shift) >= (prefix >> shift)))) {
+      top[atomicAdd(&sh[2], 1u)] = x;
+      atomicMin(tmin, (unsigned long long)x);
+    }
+  }
+  __syncthreads();
+  const uint32_t cnt = sh[2];
+  const uint64_t T = found ? (uint64_t)*tmin : 0ull;
+  for (uint32_t i = cnt + tid; i < 64; i += 256) top[i] = 0ull;
+  __syncthreads();
+  return T;
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t u) {

@@ -249,15 +249,20 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
     for (int vs = 0; vs < 4; ++vs)
       f.a[vs] = *reinterpret_cast<const bf16x8 *>(sw + lane_off(true, slot_w, ks, vs & 1) + (vs >> 1) * (64 * CH * 16));
   };
+  // 16 MFMAs per K step.  Consecutive MFMAs share an operand: the two sides
+  // of one position group run back to back, and the (pg, sd) order reverses
+  // for odd vs, so only one operand changes at each step (slightly faster
+  // under the power limit this loop runs at than restarting at pg 0).
   auto mfma = [&](const Frags &f) {
 #pragma unroll
     for (int vs = 0; vs < 4; ++vs)
 #pragma unroll
-      for (int pg = 0; pg < 2; ++pg)
-#pragma unroll
-        for (int sd = 0; sd < 2; ++sd)
-          acc[vs][pg][sd] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[vs], f.b[pg][sd], acc[vs][pg][sd], 0, 0, 0);
+      for (int q = 0; q < 4; ++q) {
+        const int qq = (vs & 1) ? 3 - q : q;
+        const int pg = qq >> 1, sd = qq & 1;
+        acc[vs][pg][sd] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[vs], f.b[pg][sd], acc[vs][pg][sd], 0, 0, 0);
+      }
   };
   // Hidden elements past d (the last stage of a width that is not a multiple
   // of BK) hold zeros or data of the next row; zero both operands there.
@@ -684,97 +689,6 @@ __global__ __launch_bounds__(FP * FG) void fused_finalize_kernel(
 //  C. Write ids and fp16 log-probs lp = z - lse.
 constexpr int TK = 256;
 
-// Block-wide (TK threads) selection of the 64 largest nonzero keys among the
-// K keys each thread holds (0 = no key; nonzero keys are distinct).  Radix
-// select, 8 bits per pass from the top: a 256-bin LDS histogram of the keys
-// that match the digits fixed so far, and wave 0 finds the bin that holds the
-// wanted rank; the passes stop early once that bin holds exactly the keys
-// still wanted (then every key at or above it is selected and the smallest of
-// them is the 64th).  Returns the 64th largest key, or 0 when fewer than 64 keys are
-// nonzero; stores the selected keys (every nonzero key when fewer than 64) in
-// top[0..63], zero-filled, in no particular order.
-template <int K>
-__device__ uint64_t select64(const uint64_t (&k)[K], uint64_t *top, uint32_t *hist,
-                             uint32_t *sh) {
-  static_assert(TK == 256, "one histogram bin per thread");
-  const int tid = threadIdx.x;
-  uint64_t prefix = 0;
-  uint32_t need = 64;
-  int shift = 64;        // keys are selected by their bits at and above `shift`
-  bool found = true;
-  for (int pass = 0; pass < 8; ++pass) {
-    const int sh8 = 56 - 8 * pass;
-    hist[tid] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < K; ++q) {
-      const uint64_t x = k[q];
-      if (x != 0ull && (pass == 0 || (x >> (sh8 + 8)) == (prefix >> (sh8 + 8))))
-        atomicAdd(&hist[(x >> sh8) & 255], 1u);
-    }
-    __syncthreads();
-    if (tid < 64) {
-      // lane l owns bins 4 l .. 4 l + 3; count the keys in higher bins
-      uint32_t c[4], s4 = 0;
-#pragma unroll
-      for (int bq = 0; bq < 4; ++bq) { c[bq] = hist[4 * tid + bq]; s4 += c[bq]; }
-      uint32_t suf = s4;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t t = __shfl_down(suf, o);
-        if (tid + o < 64) suf += t;
-      }
-      uint32_t above = suf - s4;
-      int bin = -1;
-      uint32_t left = 0, cnt = 0;
-#pragma unroll
-      for (int bq = 3; bq >= 0; --bq) {
-        if (bin < 0 && above < need && above + c[bq] >= need) {
-          bin = 4 * tid + bq; left = need - above; cnt = c[bq];
-        }
-        above += c[bq];
-      }
-      const uint64_t m = __ballot(bin >= 0);
-      if (m == 0ull) {
-        if (tid == 0) sh[0] = 0xffffffffu;
-      } else {
-        const int src = __ffsll((long long)m) - 1;
-        const int bb = __shfl(bin, src);
-        const uint32_t ll = __shfl(left, src), cc = __shfl(cnt, src);
-        if (tid == 0) { sh[0] = (uint32_t)bb; sh[1] = ll; sh[3] = cc; }
-      }
-    }
-    __syncthreads();
-    const uint32_t dd = sh[0];
-    need = sh[1];
-    const uint32_t bucket = sh[3];
-    __syncthreads();
-    if (dd == 0xffffffffu) { found = false; break; }
-    prefix |= (uint64_t)dd << sh8;
-    shift = sh8;
-    if (bucket == need) break;   // every key of the bucket is selected: the set is fixed
-  }
-  // Selected: the keys whose bits at and above `shift` reach the prefix (all
-  // nonzero keys when fewer than 64 exist).  T = the smallest selected key.
-  if (tid == 0) { sh[2] = 0; sh[4] = 0xffffffffu; sh[5] = 0xffffffffu; }
-  __syncthreads();
-  unsigned long long *tmin = reinterpret_cast<unsigned long long *>(sh + 4);
-#pragma unroll
-  for (int q = 0; q < K; ++q) {
-    const uint64_t x = k[q];
-    if (x != 0ull && (!found || (shift == 64 ? true : (x >> shift) >= (prefix >> shift)))) {
-      top[atomicAdd(&sh[2], 1u)] = x;
-      atomicMin(tmin, (unsigned long long)x);
-    }
-  }
-  __syncthreads();
-  const uint32_t cnt = sh[2];
-  const uint64_t T = found ? (uint64_t)*tmin : 0ull;
-  for (uint32_t i = cnt + tid; i < 64; i += TK) top[i] = 0ull;
-  __syncthreads();
-  return T;
-}
-
 __global__ __launch_bounds__(TK) void fused_topk_kernel(
     const uint64_t *__restrict__ ckeys, const float *__restrict__ resid,
     const uint64_t *__restrict__ rinfo, const uint64_t *__restrict__ tkeys, int64_t nvt,
@@ -813,7 +727,7 @@ __global__ __launch_bounds__(TK) void fused_topk_kernel(
     }
     k4[3] = tid < 64 ? buf[tid] : 0ull;
     __syncthreads();
-    select64<4>(k4, buf, hist, sh);
+    block_select64<4>(k4, buf, hist, sh);
   }
   // ---- A2: the 64 largest of those tiles' 16 candidates each
   if (tid < 64) tiles[tid] = buf[tid] == 0ull ? -1 : (int)((uint32_t)key_id(buf[tid]) / BV);
@@ -827,7 +741,7 @@ __global__ __launch_bounds__(TK) void fused_topk_kernel(
       const int t = tiles[i >> 4];
       k4[q] = t < 0 ? 0ull : base[(int64_t)t * tstride + (i & 15)];
     }
-    T = select64<4>(k4, buf, hist, sh);
+    T = block_select64<4>(k4, buf, hist, sh);
   }
   const float tval = key_value(T);
 
@@ -916,7 +830,7 @@ __global__ __launch_bounds__(TK) void fused_topk_kernel(
       __syncthreads();
       uint64_t k2[2] = {buf[64 + tid], tid < 64 ? buf[tid] : 0ull};
       __syncthreads();
-      select64<2>(k2, buf, hist, sh);
+      block_select64<2>(k2, buf, hist, sh);
     }
     __syncthreads();
   }
@@ -924,15 +838,7 @@ __global__ __launch_bounds__(TK) void fused_topk_kernel(
   // ---- C: ids and log-probs, in descending key order (bitonic sort of the
   // 64 selected keys across the lanes of wave 0)
   if (tid < 64) {
-    uint64_t k = buf[tid];
-#pragma unroll
-    for (int kk = 2; kk <= 64; kk <<= 1)
-#pragma unroll
-      for (int j = kk >> 1; j > 0; j >>= 1) {
-        const uint64_t o = __shfl_xor(k, j);
-        const bool desc = (tid & kk) == 0, lower = (tid & j) == 0;
-        k = (desc == lower) ? (o > k ? o : k) : (o < k ? o : k);
-      }
+    const uint64_t k = wave_sort_desc(buf[tid]);
     const double l = lse_d[(int64_t)side * n + pos];
     if (ids) ids[pos * 64 + tid] = key_id(k);
     if (lp) lp[pos * 64 + tid] = f32_to_f16_bits((float)((double)key_value(k) - l));

@@ -50,6 +50,8 @@ hipError_t launch_logits_finalize(const LogitsArgs &a, const RowState *part, dou
 // ---- top-k merge and tail KLD -----------------------------------------------
 constexpr int kTopkMergeMax = 4096;   // splits * 64 candidate keys per row and side
 constexpr int kMaxSplits = kTopkMergeMax / 64;
+constexpr int64_t kMaxChunk = int64_t(1) << 28;   // ids per split, so 4-byte logits stay below 2^30 bytes
+static_assert((int64_t(0x7fffffff) + kMaxChunk - 1) / kMaxChunk <= kMaxSplits, "every v fits");
 hipError_t launch_topk_merge(const uint64_t *keys, int splits, int nsides, int64_t n,
                              const double *lse_d, const TopkOut &out, hipStream_t stream);
 hipError_t launch_topk_tail(const int32_t *ids_p, const uint16_t *lp_p, const int32_t *ids_q,

@@ -12,17 +12,19 @@
 // Top-64 export ("Qwopus3.8-27B-Coder-Flash: quality-eval reference",
 // "Files": top-64 ids and fp16 log-probs, sorted) rides the same pass.  Each
 // element is ranked by a 64-bit key (order-preserving f32 bits, then the
-// complemented id, so equal values rank the lower id first).  The block keeps
-// a candidate buffer per side in LDS and a threshold key: an element enters
-// the buffer only if its key beats the threshold.  The first batch seeds the
-// threshold just below the 64th largest of the 256 per-thread batch maxima (a
-// valid bound: they are 256 distinct elements); whenever the buffer passes a
-// high-water mark it is sorted (bitonic, in LDS), cut to its 64 best keys and
-// the threshold becomes the 64th.  An append that finds the buffer full is
-// remembered by its thread and retried after the compaction, so no candidate
-// is lost.  The block writes its sorted 64 best keys per side;
-// topk_merge_kernel (kld_topk.hip) merges the splits of a row and converts
-// them to ids and fp16 log-probs.
+// complemented id, so equal values rank the lower id first).  Per side, an
+// element becomes a candidate only if its value reaches a threshold that at
+// least 64 elements of the block's range are known to reach: at rounds 0, 1,
+// 3, 7, ... every wave sorts its 64 lanes' running maxima (distinct elements)
+// and publishes the 16th largest; the smallest of the four waves' values is
+// reached by 64 distinct elements.  Candidates are appended to a per-wave LDS
+// buffer (ballot + mbcnt offsets, no atomics, no block barrier); a wave whose
+// buffer fills sorts it in registers, keeps its 64 best keys and from then on
+// also requires keys above the 64th.  At the end the block radix-selects the
+// 64 best keys of the four buffers and wave 0 sorts them; topk_merge_kernel
+// (kld_topk.hip) merges the splits of a row and converts them to ids and fp16
+// log-probs.  On these inputs only a few hundred elements per row and side
+// pass the threshold, so the export costs little beyond the streaming pass.
 #include "kld_device.hpp"
 #include "kld_launch.hpp"
 
@@ -40,55 +42,115 @@ template <> struct Vec<uint16_t> { static constexpr int N = 8; };
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(uint16_t x) { return bf16_to_f32(x); }
 
-// Load VEC consecutive elements starting at element `pos` (< hi) of a row,
-// as f32; elements at or beyond `hi` read as -inf.  Fast path: one 16-byte
-// load when the whole vector is in range and the row is 16-byte aligned.
+// 16 bytes of a row as loaded: 4 f32 or 8 bf16 elements.
+constexpr int kNonTemporal = 2;   // buffer-load cache policy: streaming (nt)
+
+template <typename T> struct RawOf;
+template <> struct RawOf<float> { using type = f32x4; };
+template <> struct RawOf<uint16_t> { using type = u32x4; };
+
+// Load the VEC elements starting at element `pos` of a row; elements at or
+// beyond `hi` read as -inf.  Fast path: one 16-byte load when the whole
+// vector is in range and the row is 16-byte aligned.
 template <typename T, int VEC, bool ALIGNED>
-__device__ __forceinline__ void load_vec(const T *__restrict__ row, int64_t pos, int64_t hi,
-                                         float (&x)[VEC]) {
-  if (ALIGNED && pos + VEC <= hi) {
-    if constexpr (sizeof(T) == 4) {
-      f32x4 q = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + pos));
-      x[0] = q[0]; x[1] = q[1]; x[2] = q[2]; x[3] = q[3];
-    } else {
-      u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row + pos));
+__device__ __forceinline__ typename RawOf<T>::type load_raw(const T *__restrict__ row, int64_t pos,
+                                                           int64_t hi) {
+  using R = typename RawOf<T>::type;
+  if (ALIGNED && pos + VEC <= hi) return __builtin_nontemporal_load(reinterpret_cast<const R *>(row + pos));
+  R r;
+  if constexpr (sizeof(T) == 4) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[2 * i] = __uint_as_float(q[i] << 16);
-        x[2 * i + 1] = __uint_as_float(q[i] & 0xffff0000u);
-      }
-    }
+    for (int j = 0; j < 4; ++j) r[j] = pos + j < hi ? row[pos + j] : kNegInf;
   } else {
+    constexpr uint32_t kNegInfBf16 = 0xff80u;
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) x[j] = (pos + j < hi) ? to_f32(row[pos + j]) : kNegInf;
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t a = pos + 2 * i < hi ? row[pos + 2 * i] : kNegInfBf16;
+      const uint32_t b = pos + 2 * i + 1 < hi ? row[pos + 2 * i + 1] : kNegInfBf16;
+      r[i] = a | (b << 16);
+    }
   }
+  return r;
+}
+
+// Element j of a loaded vector, as f32.
+__device__ __forceinline__ float elem(const f32x4 &q, int j) { return q[j]; }
+__device__ __forceinline__ float elem(const u32x4 &q, int j) {
+  return __uint_as_float((j & 1) ? (q[j >> 1] & 0xffff0000u) : (q[j >> 1] << 16));
+}
+// Element j of a loaded vector set to -inf.
+__device__ __forceinline__ void set_neg_inf(f32x4 &q, int j) { q[j] = kNegInf; }
+__device__ __forceinline__ void set_neg_inf(u32x4 &q, int j) {
+  q[j >> 1] = (j & 1) ? ((q[j >> 1] & 0x0000ffffu) | 0xff800000u) : ((q[j >> 1] & 0xffff0000u) | 0xff80u);
+}
+__device__ __forceinline__ void set_elem(f32x4 &q, int j, float x) { q[j] = x; }
+__device__ __forceinline__ void set_elem(u32x4 &q, int j, uint16_t x) {
+  q[j >> 1] = (j & 1) ? ((q[j >> 1] & 0x0000ffffu) | ((uint32_t)x << 16))
+                      : ((q[j >> 1] & 0xffff0000u) | x);
 }
 
 constexpr int kThreads = 256;
-constexpr int kCap = 2048;            // candidate buffer entries per side
-constexpr int kHigh = kCap - 512;     // compact once the buffer holds more than this
+constexpr int kWaves = kThreads / 64;
+constexpr int kWCap = 256;            // candidate keys per wave and side
+static_assert(kWCap == kThreads, "the final selection reads entry threadIdx.x of each buffer");
 
 struct TopkShared {
-  uint64_t buf[2][kCap];
-  uint64_t seed[kThreads];
-  uint64_t thr[2];
-  int count[2];
+  uint64_t buf[2][kWaves][kWCap];     // per side and wave: appended candidates (make_entry)
+  float bound[2][2][kWaves];          // [update parity][side][wave] threshold bounds
+  uint64_t top[64];
+  uint32_t hist[256];
+  int cnt[2][kWaves];
+  __align__(8) uint32_t sel[6];
 };
 
-// Sort the filled part of one side's buffer, keep its 64 best keys and set
-// the threshold to the 64th (0 while fewer than 64 are known).  Block-wide.
-__device__ void compact(TopkShared &sh, int side) {
-  const int cnt = min(sh.count[side], kCap);
-  int n = 64;
-  while (n < cnt) n <<= 1;
-  for (int i = cnt + (int)threadIdx.x; i < n; i += kThreads) sh.buf[side][i] = 0ull;
-  __syncthreads();
-  bitonic_desc<kThreads>(sh.buf[side], n);
-  if (threadIdx.x == 0) {
-    sh.count[side] = min(cnt, 64);
-    sh.thr[side] = cnt >= 64 ? sh.buf[side][63] : 0ull;
-  }
-  __syncthreads();
+// Values that are equal in every lane, moved to scalar registers so that the
+// compiler treats them (and branches on them) as wave-uniform.
+__device__ __forceinline__ float uniform_f(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Candidate buffer entries hold (value bits, id) as they were appended; the
+// 64-bit ranking key is formed only when the entries are ranked.
+__device__ __forceinline__ uint64_t make_entry(float x, int id) {
+  return ((uint64_t)(uint32_t)id << 32) | __float_as_uint(x);
+}
+__device__ __forceinline__ uint64_t entry_key(uint64_t e) {
+  return topk_key(__uint_as_float((uint32_t)e), (int)(e >> 32));
+}
+
+// A wave's candidate buffer (its first cnt of kWCap entries, LDS) -> its 64
+// best, sorted by key, descending, in entries 0..63; returns the 64th key
+// (cnt >= 64).  Bitonic network over keys in LDS, two compare-exchanges per
+// lane and stage; the lanes of one wave share the buffer, so the stages are
+// separated by wave-scope fences (a wave's LDS accesses complete in order).
+// Rare: only inputs with very many equal values fill a buffer.
+__device__ __attribute__((noinline)) uint64_t wave_compact(uint64_t *buf, int cnt) {
+  const int lane = threadIdx.x & 63;
+  for (int e = lane; e < kWCap; e += 64) buf[e] = e < cnt ? entry_key(buf[e]) : 0ull;
+  for (int k = 2; k <= kWCap; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int i = lane; i < kWCap / 2; i += 64) {   // pair i: entries a, a + j
+        const int a = ((i & ~(j - 1)) << 1) | (i & (j - 1));
+        const bool desc = (a & k) == 0;
+        const uint64_t x = buf[a], y = buf[a + j];
+        if (desc ? x < y : x > y) { buf[a] = y; buf[a + j] = x; }
+      }
+    }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint64_t t64 = buf[63];
+  const uint64_t kl = buf[lane];
+  buf[lane] = make_entry(key_value(kl), key_id(kl));   // back to (value, id)
+  return t64;
 }
 
 template <typename T, int VEC, int U, bool ALIGNED, bool TWO, bool TOPK>
@@ -106,45 +168,86 @@ __global__ __launch_bounds__(kThreads) void logits_partial_kernel(
 
   __shared__ TopkShared sh_storage[1];
   TopkShared &sh = sh_storage[0];
-  if constexpr (TOPK) {
-    if (threadIdx.x < NS) { sh.count[threadIdx.x] = 0; sh.thr[threadIdx.x] = 0ull; }
-  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // per side, uniform over the wave: value threshold, key threshold (0 = none)
+  // and candidates in the wave's buffer
+  float thr[2] = {kNegInf, kNegInf};
+  uint64_t tkey[2] = {0ull, 0ull};
+  int cnt[2] = {0, 0};
+  int upd = 0;
 
   float ma = kNegInf, sa = 0.f, t = 0.f, mb = kNegInf, sb = 0.f;
   int ia = kNoId, ib = kNoId;
 
-  constexpr int64_t kStride = (int64_t)kThreads * VEC;
-  // every thread runs the same number of rounds so the block can synchronise
-  const int64_t rounds = (hi - lo + kStride * U - 1) / (kStride * U);
-  for (int64_t rd = 0; rd < rounds; ++rd) {
-    const int64_t base = lo + rd * kStride * U + (int64_t)threadIdx.x * VEC;
-    float xa[U][VEC], xb[U][VEC];
+  constexpr int kStride = kThreads * VEC;
+  constexpr int kRound = kStride * U;   // ids per round
+  // every thread runs the same number of rounds so the block can synchronise;
+  // offsets from lo fit 32 bits (a split spans at most 2^28 + 7 ids)
+  const int len = (int)(hi - lo);
+  const int rounds = (len + kRound - 1) / kRound;
+  const int tofs = (int)threadIdx.x * VEC;   // the thread's first offset in a round
+
+  // Round r + 1's rows are loaded while round r is processed.  Aligned rows
+  // are read through buffer resources over the whole vectors of [lo, hi):
+  // loads past them return zeros and touch no memory, so the loop carries no
+  // bounds checks; the last round masks offsets past hi to -inf and reads a
+  // vector that straddles hi element by element.
+  using Raw = typename RawOf<T>::type;
+  Raw qa[2][U], qb[2][U];   // two rounds in flight: round r in slot r % 2
+  const int nvec = len / VEC * VEC;   // ids in whole vectors
+  __amdgpu_buffer_rsrc_t rsa, rsb;
+  if constexpr (ALIGNED) {
+    rsa = __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(ra + lo), (short)0,
+                                            nvec * (int)sizeof(T), 0x00020000);
+    rsb = __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(rb + lo), (short)0,
+                                            nvec * (int)sizeof(T), 0x00020000);
+  }
+  // Load round r into slot sl.  Rounds past the last one load nothing (zeros
+  // from the buffer resources, -inf from the checked path), so the loop
+  // fetches two ahead without conditions.
+  auto fetch = [&](int r, int sl) {
+    const int e0 = r * kRound + tofs;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t pos = base + u * kStride;
-      if (pos < hi) {
-        load_vec<T, VEC, ALIGNED>(ra, pos, hi, xa[u]);
-        if (TWO) load_vec<T, VEC, ALIGNED>(rb, pos, hi, xb[u]);
+      if constexpr (ALIGNED) {
+        const int o = (e0 + u * kStride) * (int)sizeof(T);
+        qa[sl][u] = __builtin_bit_cast(Raw, __builtin_amdgcn_raw_buffer_load_b128(rsa, o, 0, kNonTemporal));
+        if (TWO) qb[sl][u] = __builtin_bit_cast(Raw, __builtin_amdgcn_raw_buffer_load_b128(rsb, o, 0, kNonTemporal));
       } else {
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) { xa[u][j] = kNegInf; xb[u][j] = kNegInf; }
+        qa[sl][u] = load_raw<T, VEC, false>(ra, lo + e0 + u * kStride, hi);
+        if (TWO) qb[sl][u] = load_raw<T, VEC, false>(rb, lo + e0 + u * kStride, hi);
       }
     }
+  };
+
+  // One round: elements lo + r * kRound + tofs + u * kStride + j of the
+  // vectors ca[u], cb[u].  Values are unpacked where they are used, one
+  // vector at a time, so that only the packed round stays in registers.
+  // `lim` is the number of valid offsets from the thread's first one (only
+  // the last round can have fewer than kRound).
+  auto process = [&](int r, const Raw (&ca)[U], const Raw (&cb)[U], bool ragged,
+                     int lim) __attribute__((always_inline)) {
+    const int id0 = (int)lo + r * kRound + tofs;   // id of element (0, 0)
+    float vma[U], vmb[U];   // per-vector maxima
     float bma = kNegInf, bmb = kNegInf;
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+      vma[u] = kNegInf; vmb[u] = kNegInf;
 #pragma unroll
       for (int j = 0; j < VEC; ++j) {
-        bma = fmaxf(bma, xa[u][j]);
-        if (TWO) bmb = fmaxf(bmb, xb[u][j]);
+        vma[u] = fmaxf(vma[u], elem(ca[u], j));
+        if (TWO) vmb[u] = fmaxf(vmb[u], elem(cb[u], j));
       }
+      bma = fmaxf(bma, vma[u]);
+      if (TWO) bmb = fmaxf(bmb, vmb[u]);
+    }
     if (bma > ma) {   // new maximum: locate its lowest id in this batch, rebase the sums
       int id = kNoId;
 #pragma unroll
       for (int u = U - 1; u >= 0; --u)
 #pragma unroll
         for (int j = VEC - 1; j >= 0; --j)
-          if (xa[u][j] == bma) id = (int)(base + u * kStride + j);
+          if (elem(ca[u], j) == bma) id = id0 + u * kStride + j;
       const float f = rescale(ma, bma);
       if (TWO && sa != 0.f) t = fmaf(-sa, bma - ref_of(ma), t);
       t *= f; sa *= f; ma = bma; ia = id;
@@ -155,121 +258,182 @@ __global__ __launch_bounds__(kThreads) void logits_partial_kernel(
       for (int u = U - 1; u >= 0; --u)
 #pragma unroll
         for (int j = VEC - 1; j >= 0; --j)
-          if (xb[u][j] == bmb) id = (int)(base + u * kStride + j);
+          if (elem(cb[u], j) == bmb) id = id0 + u * kStride + j;
       if (sa != 0.f) t = fmaf(sa, bmb - ref_of(mb), t);
       sb *= rescale(mb, bmb); mb = bmb; ib = id;
     }
+    if constexpr (TOPK) {
+      if (((r + 1) & r) == 0) {
+        // rounds 0, 1, 3, 7, ...: raise the value thresholds from the lanes'
+        // running maxima (the wave's 16th largest; the smallest over waves)
+        const int par = upd & 1;
+        ++upd;
+#pragma unroll
+        for (int side = 0; side < NS; ++side) {
+          const float srt = wave_sort_desc(side ? mb : ma);
+          const float b16 = __shfl(srt, 15);
+          if (lane == 0) sh.bound[par][side][wave] = b16;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int side = 0; side < NS; ++side) {
+          float b = sh.bound[par][side][0];
+#pragma unroll
+          for (int w = 1; w < kWaves; ++w) b = fminf(b, sh.bound[par][side][w]);
+          thr[side] = uniform_f(fmaxf(thr[side], b));
+        }
+      }
+    }
     const float rfa = ref_of(ma), rfb = ref_of(mb);
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+      float xa[VEC], xb[VEC];
 #pragma unroll
       for (int j = 0; j < VEC; ++j) {
-        const float x = xa[u][j] - rfa;
+        xa[j] = elem(ca[u], j);
+        if (TWO) xb[j] = elem(cb[u], j);
+      }
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) {
+        const float x = xa[j] - rfa;
         const float w = exp2_fast(x * kL2E);
         sa += w;
         if (TWO) {
-          const float y = xb[u][j] - rfb;
+          const float y = xb[j] - rfb;
           // x - y is clamped below so that a -inf reference id (w = 0) adds
           // exactly 0 even when the candidate id is -inf too.
           t = fmaf(w, fmaxf(x - y, -kFltMax), t);
           sb += exp2_fast(y * kL2E);
         }
       }
-
-    if constexpr (TOPK) {
-      if (rd == 0) {
-        // seed each side's threshold just below the 64th best per-thread maximum
+      if constexpr (TOPK) {
+        // append the vector's elements that reach the threshold, one element
+        // per lane at a time; a wave with no such element skips it all.
+        // Thresholds and counts are wave-uniform (scalar registers).
+#pragma unroll
         for (int side = 0; side < NS; ++side) {
-          uint64_t best = 0ull;
-#pragma unroll
-          for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int j = 0; j < VEC; ++j) {
-              const int64_t id = base + u * kStride + j;
-              if (id < hi) {
-                const uint64_t k = topk_key(side ? xb[u][j] : xa[u][j], (int)id);
-                best = k > best ? k : best;
-              }
-            }
-          sh.seed[threadIdx.x] = best;
-          __syncthreads();
-          bitonic_desc<kThreads>(sh.seed, kThreads);
-          if (threadIdx.x == 0) sh.thr[side] = sh.seed[63] == 0ull ? 0ull : sh.seed[63] - 1ull;
-          __syncthreads();
-        }
-      }
-      // append every element whose key beats the threshold; remember what did
-      // not fit and retry after compacting
-      uint32_t pending[2] = {0u, 0u};
-      for (int side = 0; side < NS; ++side) {
-        const uint64_t th = sh.thr[side];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
+          const float th = uniform_f(thr[side]);
+          if (__ballot((side ? vmb[u] : vma[u]) >= th) == 0ull) continue;
+          uint64_t *wbuf = sh.buf[side][wave];
 #pragma unroll
           for (int j = 0; j < VEC; ++j) {
-            const int64_t id = base + u * kStride + j;
-            const float x = side ? xb[u][j] : xa[u][j];
-            if (id < hi) {
-              const uint64_t k = topk_key(x, (int)id);
-              if (k > th) {
-                const int slot = atomicAdd(&sh.count[side], 1);
-                if (slot < kCap) sh.buf[side][slot] = k;
-                else pending[side] |= 1u << (u * VEC + j);
-              }
+            const int off = u * kStride + j;   // element offset from id0
+            const float x = side ? xb[j] : xa[j];
+            if (__ballot(x >= th) == 0ull) continue;
+            // rare: some lane holds a candidate
+            const int id = id0 + off;
+            bool p = x >= th && (!ragged || off < lim);
+            const uint64_t tk = tkey[side];
+            if (tk != 0ull) p = p && topk_key(x, id) > tk;
+            uint64_t m = __ballot(p);
+            if (m == 0ull) continue;
+            if (cnt[side] + 64 > kWCap) {
+              // buffer full: keep its 64 best, filter this element again
+              const uint64_t t64 = wave_compact(wbuf, cnt[side]);
+              tkey[side] = uniform_u64(t64);
+              cnt[side] = 64;
+              thr[side] = uniform_f(fmaxf(thr[side], key_value(tkey[side])));
+              p = p && topk_key(x, id) > tkey[side];
+              m = __ballot(p);
+              if (m == 0ull) continue;
             }
+            const int at = cnt[side] + (int)__builtin_amdgcn_mbcnt_hi(
+                (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (p) wbuf[at] = make_entry(x, id);
+            cnt[side] += __popcll(m);
           }
-      }
-      for (;;) {
-        __syncthreads();
-        bool any = false;
-        for (int side = 0; side < NS; ++side) any = any || sh.count[side] > kHigh;
-        if (!any) break;
-        for (int side = 0; side < NS; ++side)
-          if (sh.count[side] > kHigh) compact(sh, side);
-        // retry the elements that found the buffer full
-        for (int side = 0; side < NS; ++side) {
-          const uint64_t th = sh.thr[side];
-          uint32_t still = 0u;
-#pragma unroll
-          for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int j = 0; j < VEC; ++j) {
-              if (pending[side] & (1u << (u * VEC + j))) {
-                const uint64_t k =
-                    topk_key(side ? xb[u][j] : xa[u][j], (int)(base + u * kStride + j));
-                if (k > th) {
-                  const int slot = atomicAdd(&sh.count[side], 1);
-                  if (slot < kCap) sh.buf[side][slot] = k;
-                  else still |= 1u << (u * VEC + j);
-                }
-              }
-            }
-          pending[side] = still;
         }
       }
+    }
+  };
+
+  // Round r's packed vectors, with the range end applied in the last round
+  // (offsets past hi -> -inf; the vector that straddles hi read element by
+  // element), then processed.
+  auto run = [&](int r, int sl, bool last) __attribute__((always_inline)) {
+    Raw ca[U], cb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) { ca[u] = qa[sl][u]; cb[u] = qb[sl][u]; }
+    if (!last) {
+      fetch(r + 2, sl);
+      process(r, ca, cb, false, kRound);
+      return;
+    }
+    const int lim = len - (r * kRound + tofs);   // valid offsets from the thread's first
+    const bool ragged = len < (r + 1) * kRound;
+    if (ALIGNED && ragged) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int o = u * kStride;
+        if (o < lim && o + VEC > lim && r * kRound + tofs + o >= nvec) {
+          // the vector that straddles hi (past the buffer's whole vectors)
+          const int64_t pos = lo + r * kRound + tofs + o;
+#pragma unroll
+          for (int j = 0; j < VEC; ++j)
+            if (o + j < lim) {
+              set_elem(ca[u], j, ra[pos + j]);
+              if (TWO) set_elem(cb[u], j, rb[pos + j]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < VEC; ++j)
+          if (o + j >= lim) {
+            set_neg_inf(ca[u], j);
+            if (TWO) set_neg_inf(cb[u], j);
+          }
+      }
+    }
+    process(r, ca, cb, ragged, lim);
+  };
+
+  if (rounds > 0) {
+    fetch(0, 0);
+    fetch(1, 1);
+    int r = 0;
+    for (; r + 2 < rounds; r += 2) {   // rounds r, r + 1: neither is the last
+      run(r, 0, false);
+      run(r + 1, 1, false);
+    }
+    if (r + 1 < rounds) {
+      run(r, 0, false);
+      run(r + 1, 1, true);
+    } else {
+      run(r, 0, true);
     }
   }
 
   if constexpr (TOPK) {
+    // the 64 best keys of the four waves' buffers, sorted by wave 0
+    if (lane == 0) {
+      sh.cnt[0][wave] = cnt[0];
+      sh.cnt[1][wave] = cnt[1];
+    }
+    __syncthreads();
+#pragma unroll
     for (int side = 0; side < NS; ++side) {
-      compact(sh, side);
-      uint64_t *dst = topk_keys + ((row * splits + split) * 2 + side) * 64;
-      if (threadIdx.x < 64)
-        dst[threadIdx.x] = (int)threadIdx.x < sh.count[side] ? sh.buf[side][threadIdx.x] : 0ull;
+      uint64_t k[kWaves];
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w)
+        k[w] = (int)threadIdx.x < sh.cnt[side][w] ? entry_key(sh.buf[side][w][threadIdx.x]) : 0ull;
+      block_select64<kWaves>(k, sh.top, sh.hist, sh.sel);
+      if (wave == 0) {
+        const uint64_t key = wave_sort_desc(sh.top[lane]);
+        topk_keys[((row * splits + split) * 2 + side) * 64 + lane] = key;
+      }
+      __syncthreads();
     }
   }
 
   RowState s;
   s.ma = ma; s.sa = sa; s.t = t; s.mb = mb; s.sb = sb; s.ia = ia; s.ib = ib;
   s = wave_merge(s);
-  __shared__ RowState waves[kThreads / 64];
-  const int wave = threadIdx.x / 64;
-  if ((threadIdx.x & 63) == 0) waves[wave] = s;
+  __shared__ RowState waves[kWaves];
+  if (lane == 0) waves[wave] = s;
   __syncthreads();
   if (threadIdx.x == 0) {
     RowState r = waves[0];
 #pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) r = merge(r, waves[w]);
+    for (int w = 1; w < kWaves; ++w) r = merge(r, waves[w]);
     part[row * splits + split] = r;
   }
 }
