@@ -91,16 +91,16 @@ __device__ __forceinline__ void set_elem(u32x4 &q, int j, uint16_t x) {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kWCap = 256;            // candidate keys per wave and side
-static_assert(kWCap == kThreads, "the final selection reads entry threadIdx.x of each buffer");
+constexpr int kWCap = 256;            // candidate keys per wave and side (64 kept + room for batches)
 
+// SCAP staged vectors per wave and side.
+template <int SCAP>
 struct TopkShared {
   uint64_t buf[2][kWaves][kWCap];     // per side and wave: appended candidates (make_entry)
-  float bound[2][2][kWaves];          // [update parity][side][wave] threshold bounds
-  uint64_t top[64];
-  uint32_t hist[256];
-  int cnt[2][kWaves];
-  __align__(8) uint32_t sel[6];
+  u32x4 stage[2][kWaves][SCAP];       // per side and wave: staged vectors (as loaded)
+  int sid[2][kWaves][SCAP];           // id of each staged vector's first element
+  uint64_t top[2][kWaves][64];        // per side and wave: its 64 best keys, sorted
+  float bound[2][kWaves];             // per side and wave: threshold bound (nondecreasing)
 };
 
 // Values that are equal in every lane, moved to scalar registers so that the
@@ -153,6 +153,22 @@ __device__ __attribute__((noinline)) uint64_t wave_compact(uint64_t *buf, int cn
   return t64;
 }
 
+// Two key lists of 64, one key per lane, each sorted descending: a from
+// lane order, b given reversed (lane l holds b[63 - l]).  Returns the 64
+// largest keys of both, sorted descending: the lane-wise maximum of a and
+// reversed b holds them as a bitonic sequence, which a half-cleaner cascade
+// sorts.
+__device__ __forceinline__ uint64_t wave_merge_top64(uint64_t a, uint64_t b_rev) {
+  const int lane = threadIdx.x & 63;
+  uint64_t c = a > b_rev ? a : b_rev;
+#pragma unroll
+  for (int j = 32; j > 0; j >>= 1) {
+    const uint64_t o = __shfl_xor(c, j);
+    c = (lane & j) == 0 ? (o > c ? o : c) : (o < c ? o : c);
+  }
+  return c;
+}
+
 template <typename T, int VEC, int U, bool ALIGNED, bool TWO, bool TOPK>
 __global__ __launch_bounds__(kThreads) void logits_partial_kernel(
     const T *__restrict__ ref, const T *__restrict__ cand, int64_t ld_ref, int64_t ld_cand,
@@ -166,15 +182,23 @@ __global__ __launch_bounds__(kThreads) void logits_partial_kernel(
   const T *rb = TWO ? cand + row * ld_cand : ra;
   constexpr int NS = TWO ? 2 : 1;
 
-  __shared__ TopkShared sh_storage[1];
-  TopkShared &sh = sh_storage[0];
+  constexpr int kSCap = 128;
+  __shared__ TopkShared<kSCap> sh_storage[1];
+  TopkShared<kSCap> &sh = sh_storage[0];
+  __shared__ RowState waves[kWaves];
+  __shared__ int done;   // waves that have finished (the last one merges)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // per side, uniform over the wave: value threshold, key threshold (0 = none)
   // and candidates in the wave's buffer
   float thr[2] = {kNegInf, kNegInf};
   uint64_t tkey[2] = {0ull, 0ull};
-  int cnt[2] = {0, 0};
-  int upd = 0;
+  int cnt[2] = {0, 0};    // candidates in the wave's buffer
+  int scnt[2] = {0, 0};   // vectors staged by the wave
+  if constexpr (TOPK) {
+    if (threadIdx.x < 2 * kWaves) (&sh.bound[0][0])[threadIdx.x] = kNegInf;
+    if (threadIdx.x == 0) done = 0;
+    __syncthreads();
+  }
 
   float ma = kNegInf, sa = 0.f, t = 0.f, mb = kNegInf, sb = 0.f;
   int ia = kNoId, ib = kNoId;
@@ -220,6 +244,68 @@ __global__ __launch_bounds__(kThreads) void logits_partial_kernel(
     }
   };
 
+  // Raise the value thresholds from the lanes' running maxima: each wave
+  // publishes the 16th largest of its 64 (distinct elements, so at least 16
+  // of its elements reach it) and takes the smallest of the four waves'
+  // latest values, which at least 64 elements reach.  Published values only
+  // grow, so reading another wave's older value is still valid: no barrier.
+  auto update = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int side = 0; side < NS; ++side) {
+      const float srt = wave_sort_desc(side ? mb : ma);
+      const float b16 = __shfl(srt, 15);
+      if (lane == 0) sh.bound[side][wave] = b16;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+#pragma unroll
+    for (int side = 0; side < NS; ++side) {
+      const volatile float *bd = sh.bound[side];
+      float b = bd[0];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) b = fminf(b, bd[w]);
+      thr[side] = uniform_f(fmaxf(thr[side], b));
+    }
+  };
+
+  // Filter the wave's staged vectors against the current threshold (and key
+  // threshold, after a compaction) and append the elements that pass, one
+  // element per lane at a time.
+  auto flush = [&](int side) {
+    const float th = uniform_f(thr[side]);
+    uint64_t *wbuf = sh.buf[side][wave];
+    for (int b0 = 0; b0 < scnt[side]; b0 += 64) {
+      const int e = b0 + lane;
+      const bool ok = e < scnt[side];
+      const Raw q = __builtin_bit_cast(Raw, ok ? sh.stage[side][wave][e] : u32x4{0u, 0u, 0u, 0u});
+      const int bid = ok ? sh.sid[side][wave][e] : 0;
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) {
+        const float x = elem(q, j);
+        const int id = bid + j;
+        bool p = ok && x >= th && (int64_t)id < hi;
+        const uint64_t tk = tkey[side];
+        if (tk != 0ull) p = p && topk_key(x, id) > tk;
+        uint64_t m = __ballot(p);
+        if (m == 0ull) continue;
+        if (cnt[side] + 64 > kWCap) {
+          // buffer full: keep its 64 best, filter this element again
+          const uint64_t t64 = wave_compact(wbuf, cnt[side]);
+          tkey[side] = uniform_u64(t64);
+          cnt[side] = 64;
+          thr[side] = uniform_f(fmaxf(thr[side], key_value(tkey[side])));
+          p = p && topk_key(x, id) > tkey[side];
+          m = __ballot(p);
+          if (m == 0ull) continue;
+        }
+        const int at = cnt[side] + (int)__builtin_amdgcn_mbcnt_hi(
+            (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (p) wbuf[at] = make_entry(x, id);
+        cnt[side] += __popcll(m);
+      }
+    }
+    scnt[side] = 0;
+  };
+
   // One round: elements lo + r * kRound + tofs + u * kStride + j of the
   // vectors ca[u], cb[u].  Values are unpacked where they are used, one
   // vector at a time, so that only the packed round stays in registers.
@@ -263,24 +349,26 @@ __global__ __launch_bounds__(kThreads) void logits_partial_kernel(
       sb *= rescale(mb, bmb); mb = bmb; ib = id;
     }
     if constexpr (TOPK) {
-      if (((r + 1) & r) == 0) {
-        // rounds 0, 1, 3, 7, ...: raise the value thresholds from the lanes'
-        // running maxima (the wave's 16th largest; the smallest over waves)
-        const int par = upd & 1;
-        ++upd;
+      if (((r + 1) & r) == 0) update();   // rounds 0, 1, 3, 7, ...
+      // stage the vectors whose maximum reaches the threshold; their elements
+      // are filtered in batches (flush), so the common path has no
+      // per-element work and a single branch per vector and side
 #pragma unroll
-        for (int side = 0; side < NS; ++side) {
-          const float srt = wave_sort_desc(side ? mb : ma);
-          const float b16 = __shfl(srt, 15);
-          if (lane == 0) sh.bound[par][side][wave] = b16;
-        }
-        __syncthreads();
+      for (int side = 0; side < NS; ++side) {
+        const float th = uniform_f(thr[side]);
 #pragma unroll
-        for (int side = 0; side < NS; ++side) {
-          float b = sh.bound[par][side][0];
-#pragma unroll
-          for (int w = 1; w < kWaves; ++w) b = fminf(b, sh.bound[par][side][w]);
-          thr[side] = uniform_f(fmaxf(thr[side], b));
+        for (int u = 0; u < U; ++u) {
+          const bool c = (side ? vmb[u] : vma[u]) >= th;
+          const uint64_t m = __ballot(c);
+          if (m == 0ull) continue;
+          if (scnt[side] + 64 > kSCap) flush(side);
+          const int at = scnt[side] + (int)__builtin_amdgcn_mbcnt_hi(
+              (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          if (c) {
+            sh.stage[side][wave][at] = __builtin_bit_cast(u32x4, side ? cb[u] : ca[u]);
+            sh.sid[side][wave][at] = id0 + u * kStride;
+          }
+          scnt[side] += __popcll(m);
         }
       }
     }
@@ -304,44 +392,6 @@ __global__ __launch_bounds__(kThreads) void logits_partial_kernel(
           // exactly 0 even when the candidate id is -inf too.
           t = fmaf(w, fmaxf(x - y, -kFltMax), t);
           sb += exp2_fast(y * kL2E);
-        }
-      }
-      if constexpr (TOPK) {
-        // append the vector's elements that reach the threshold, one element
-        // per lane at a time; a wave with no such element skips it all.
-        // Thresholds and counts are wave-uniform (scalar registers).
-#pragma unroll
-        for (int side = 0; side < NS; ++side) {
-          const float th = uniform_f(thr[side]);
-          if (__ballot((side ? vmb[u] : vma[u]) >= th) == 0ull) continue;
-          uint64_t *wbuf = sh.buf[side][wave];
-#pragma unroll
-          for (int j = 0; j < VEC; ++j) {
-            const int off = u * kStride + j;   // element offset from id0
-            const float x = side ? xb[j] : xa[j];
-            if (__ballot(x >= th) == 0ull) continue;
-            // rare: some lane holds a candidate
-            const int id = id0 + off;
-            bool p = x >= th && (!ragged || off < lim);
-            const uint64_t tk = tkey[side];
-            if (tk != 0ull) p = p && topk_key(x, id) > tk;
-            uint64_t m = __ballot(p);
-            if (m == 0ull) continue;
-            if (cnt[side] + 64 > kWCap) {
-              // buffer full: keep its 64 best, filter this element again
-              const uint64_t t64 = wave_compact(wbuf, cnt[side]);
-              tkey[side] = uniform_u64(t64);
-              cnt[side] = 64;
-              thr[side] = uniform_f(fmaxf(thr[side], key_value(tkey[side])));
-              p = p && topk_key(x, id) > tkey[side];
-              m = __ballot(p);
-              if (m == 0ull) continue;
-            }
-            const int at = cnt[side] + (int)__builtin_amdgcn_mbcnt_hi(
-                (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-            if (p) wbuf[at] = make_entry(x, id);
-            cnt[side] += __popcll(m);
-          }
         }
       }
     }
@@ -403,38 +453,64 @@ __global__ __launch_bounds__(kThreads) void logits_partial_kernel(
   }
 
   if constexpr (TOPK) {
-    // the 64 best keys of the four waves' buffers, sorted by wave 0
-    if (lane == 0) {
-      sh.cnt[0][wave] = cnt[0];
-      sh.cnt[1][wave] = cnt[1];
-    }
-    __syncthreads();
+    // last threshold from the final maxima, remaining staged vectors, then
+    // each wave sorts its own 64 best
+    update();
 #pragma unroll
     for (int side = 0; side < NS; ++side) {
-      uint64_t k[kWaves];
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w)
-        k[w] = (int)threadIdx.x < sh.cnt[side][w] ? entry_key(sh.buf[side][w][threadIdx.x]) : 0ull;
-      block_select64<kWaves>(k, sh.top, sh.hist, sh.sel);
-      if (wave == 0) {
-        const uint64_t key = wave_sort_desc(sh.top[lane]);
-        topk_keys[((row * splits + split) * 2 + side) * 64 + lane] = key;
+      flush(side);
+      uint64_t *wbuf = sh.buf[side][wave];
+      uint64_t k;
+      if (cnt[side] <= 64) {
+        k = wave_sort_desc(lane < cnt[side] ? entry_key(wbuf[lane]) : (uint64_t)0);
+      } else {
+        wave_compact(wbuf, cnt[side]);   // entries 0..63 become its 64 best, sorted
+        k = entry_key(wbuf[lane]);
       }
-      __syncthreads();
+      sh.top[side][wave][lane] = k;
     }
   }
-
   RowState s;
   s.ma = ma; s.sa = sa; s.t = t; s.mb = mb; s.sb = sb; s.ia = ia; s.ib = ib;
   s = wave_merge(s);
-  __shared__ RowState waves[kWaves];
   if (lane == 0) waves[wave] = s;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    RowState r = waves[0];
+
+  // One wave merges the four waves' results, in wave order.  With top-k it
+  // is the wave that finishes last (the others leave without waiting);
+  // without, wave 0 after a barrier.
+  if constexpr (TOPK) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    int last = 0;
+    if (lane == 0) last = atomicAdd(&done, 1) == kWaves - 1;
+    if (__shfl(last, 0) == 0) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  } else {
+    __syncthreads();
+    if (wave != 0) return;
+  }
+  if (lane == 0) {
+    const volatile RowState *vw = waves;
+    RowState r;
+    r.ma = vw[0].ma; r.sa = vw[0].sa; r.t = vw[0].t; r.mb = vw[0].mb; r.sb = vw[0].sb;
+    r.ia = vw[0].ia; r.ib = vw[0].ib;
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) r = merge(r, waves[w]);
+    for (int w = 1; w < kWaves; ++w) {
+      RowState o;
+      o.ma = vw[w].ma; o.sa = vw[w].sa; o.t = vw[w].t; o.mb = vw[w].mb; o.sb = vw[w].sb;
+      o.ia = vw[w].ia; o.ib = vw[w].ib;
+      r = merge(r, o);
+    }
     part[row * splits + split] = r;
+  }
+  if constexpr (TOPK) {
+#pragma unroll
+    for (int side = 0; side < NS; ++side) {
+      const volatile uint64_t *tp = &sh.top[side][0][0];
+      uint64_t k = tp[lane];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) k = wave_merge_top64(k, tp[w * 64 + 63 - lane]);
+      topk_keys[((row * splits + split) * 2 + side) * 64 + lane] = k;
+    }
   }
 }
 
