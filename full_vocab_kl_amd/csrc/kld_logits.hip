@@ -99,7 +99,6 @@ struct TopkShared {
   uint64_t buf[2][kWaves][kWCap];     // per side and wave: appended candidates (make_entry)
   u32x4 stage[2][kWaves][SCAP];       // per side and wave: staged vectors (as loaded)
   int sid[2][kWaves][SCAP];           // id of each staged vector's first element
-  uint64_t top[2][kWaves][64];        // per side and wave: its 64 best keys, sorted
   float bound[2][kWaves];             // per side and wave: threshold bound (nondecreasing)
 };
 
@@ -467,7 +466,8 @@ __global__ __launch_bounds__(kThreads) void logits_partial_kernel(
         wave_compact(wbuf, cnt[side]);   // entries 0..63 become its 64 best, sorted
         k = entry_key(wbuf[lane]);
       }
-      sh.top[side][wave][lane] = k;
+      // the wave's staging area of this side is free now: it takes the list
+      reinterpret_cast<uint64_t *>(sh.stage[side][wave])[lane] = k;
     }
   }
   RowState s;
@@ -505,10 +505,10 @@ __global__ __launch_bounds__(kThreads) void logits_partial_kernel(
   if constexpr (TOPK) {
 #pragma unroll
     for (int side = 0; side < NS; ++side) {
-      const volatile uint64_t *tp = &sh.top[side][0][0];
-      uint64_t k = tp[lane];
+      auto list = [&](int w) { return reinterpret_cast<const volatile uint64_t *>(sh.stage[side][w]); };
+      uint64_t k = list(0)[lane];
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) k = wave_merge_top64(k, tp[w * 64 + 63 - lane]);
+      for (int w = 1; w < kWaves; ++w) k = wave_merge_top64(k, list(w)[63 - lane]);
       topk_keys[((row * splits + split) * 2 + side) * 64 + lane] = k;
     }
   }
