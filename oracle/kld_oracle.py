@@ -41,6 +41,14 @@ Readings where the pages are silent (each also listed in the design notes):
       +inf, has KL = NaN.
 * R7  NLL of a target id outside [0, V) is NaN.
 * R8  argmax ignores NaN entries; a row of only NaN reports id 0.
+* R9  the golden record's tail mass is the mass of the ids outside the
+      top-K, summed over those ids of the full row (equal to 1 - sum of the
+      listed probabilities in exact arithmetic, but free of its
+      cancellation when the tail is tiny).
+* R10 the 513-cell score takes p from the stored record (the f32 log-probs
+      of the listed ids and the stored tail mass) and q from the candidate's
+      full row: q of a listed id is its softmax probability, q's tail cell
+      the candidate mass of every unlisted id.
 
 Parity is pinned for every function here by the ``-m "not gpu"`` tests
 (tests/test_oracle_pins.py); no function is "parity unpinned".
@@ -278,6 +286,87 @@ def score_rows(a: np.ndarray, b: np.ndarray, target=None, k: int | None = None) 
                 out[f"ids_{s}"][i] = ids
                 out[f"lp_{s}"][i] = lp
     return out
+
+
+GOLDEN_TOPK = 512
+
+
+def golden_row(x: np.ndarray, target=None, k: int = GOLDEN_TOPK):
+    """The golden record of one reference position ([QC] "Golden
+    distributions": the k most likely tokens exactly, most likely first, as
+    {int32 id, f32 log p}, plus the NLL of the true next token, the entropy
+    in nats and the tail mass of the rest).
+
+    Ids follow O6 (ties to the lower id, reading R1); lp = x_j - lse(x) in f64,
+    rounded once to f32; entropy = -sum_j p_j ln p_j over every id with
+    p_j > 0; tail = sum of p_j over the ids outside the top k (reading R9);
+    nll per O4 (NaN without a target).  Returns (ids int32 [k], lp f32 [k],
+    rec f32 [3] = (nll, entropy, tail))."""
+    x = np.asarray(x, dtype=np.float64)
+    v = x.shape[0]
+    lse = logsumexp(x)
+    order = np.lexsort((np.arange(v), -x))
+    top, rest = order[:k], order[k:]
+    lp = (x[top] - lse).astype(np.float32)
+    pos = x > -np.inf
+    logp = x[pos] - lse
+    entropy = float(-np.sum(np.exp(logp) * logp))
+    tail = float(np.sum(np.exp(x[rest] - lse)))
+    nll = nll_row(x, int(target)) if target is not None else float("nan")
+    rec = np.array([nll, entropy, tail], dtype=np.float32)
+    return top.astype(np.int32), lp, rec
+
+
+def coarse_kl_row(ids, lp, tail, b: np.ndarray) -> float:
+    """The score of one position against a golden record ([QC] "The score"):
+    the candidate's distribution q is coarsened onto the record's cells --
+    its listed ids and one tail cell with the rest of q's mass -- and
+    KL(p || q) = sum over the cells of p_i (ln p_i - ln q_i).
+
+    p_i = exp(lp_i) for the listed ids and p_T = tail (the stored record,
+    reading R10); q_i = softmax(b)_i and q_T = the sum of softmax(b) over the
+    unlisted ids.  A cell with p = 0 adds 0; p > 0 against q = 0 gives +inf."""
+    b = np.asarray(b, dtype=np.float64)
+    ids = np.asarray(ids, dtype=np.int64)
+    lse_b = logsumexp(b)
+    lq = b - lse_b
+    listed = np.zeros(b.shape[0], dtype=bool)
+    listed[ids] = True
+    q_t = float(np.sum(np.exp(lq[~listed])))
+    lp = np.asarray(lp, dtype=np.float64)
+    p = np.exp(lp)
+    total = 0.0
+    for pi, lpi, lqi in zip(p, lp, lq[ids]):
+        if pi == 0.0:
+            continue
+        if lqi == -np.inf:
+            return math.inf
+        total += pi * (lpi - lqi)
+    p_t = float(tail)
+    if p_t > 0.0:
+        if q_t == 0.0:
+            return math.inf
+        total += p_t * (math.log(p_t) - math.log(q_t))
+    return float(total)
+
+
+def golden_rows(x: np.ndarray, target=None, k: int = GOLDEN_TOPK) -> dict:
+    """golden_row over the rows of x [n, V]: ids [n, k], lp [n, k], rec [n, 3]."""
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[0]
+    out = {"ids": np.empty((n, k), np.int32), "lp": np.empty((n, k), np.float32),
+           "rec": np.empty((n, 3), np.float32)}
+    for i in range(n):
+        t = None if target is None else int(target[i])
+        out["ids"][i], out["lp"][i], out["rec"][i] = golden_row(x[i], t, k)
+    return out
+
+
+def coarse_kl_rows(ids, lp, rec, b: np.ndarray) -> np.ndarray:
+    """coarse_kl_row over the rows of b [n, V] against records (ids, lp, rec)."""
+    b = np.asarray(b, dtype=np.float64)
+    return np.array([coarse_kl_row(ids[i], lp[i], float(rec[i][2]), b[i])
+                     for i in range(b.shape[0])])
 
 
 def percentile(x: np.ndarray, q: float) -> float:

@@ -311,3 +311,97 @@ def test_score_rows_consistency():
         assert s["kl"][i] == oracle.kl_row(a[i], b[i])
         assert s["nll_ref"][i] == oracle.nll_row(a[i], t[i])
         assert list(s["ids_cand"][i]) == _brute_topk(b[i], 8)
+
+
+# ---------------------------------------------------- golden record + score
+
+def _frac(s):
+    from fractions import Fraction
+    return float(Fraction(s))
+
+
+def test_golden_record_hand_example():
+    g = _gold("golden_record_example.json")
+    p = np.array([_frac(s) for s in g["full_p"]])
+    ids, lp, rec = oracle.golden_row(np.log(p), g["target"], k=g["k"])
+    assert list(ids) == g["expected_ids"]
+    assert np.array_equal(lp, np.log(p[:2]).astype(np.float32))
+    assert rec[0] == np.float32(float(g["expected_nll"]))
+    assert rec[1] == np.float32(float(g["expected_entropy"]))
+    assert rec[2] == np.float32(float(g["expected_tail"]))
+    # the score from the exact record (f64 log-probs and tail)
+    q = np.array(g["full_q"])
+    got = oracle.coarse_kl_row(ids, np.log(p[ids]), 0.25, np.log(q))
+    assert abs(got - float(g["expected_score"])) < 1e-15
+    # same cells as the top-K + tail rule of the quality-eval reference when q
+    # is uniform off its own list (the tail-rule example uses this p, q)
+    a = _gold("tail_example_a.json")
+    assert abs(got - float(a["expected_tail_kl"])) < 1e-15
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_golden_entropy_matches_scipy_and_uniform(seed):
+    g = np.random.default_rng(400 + seed)
+    x = g.normal(0, 2, 3000)
+    _, _, rec = oracle.golden_row(x, k=64)
+    p = np.exp(x - oracle.logsumexp(x))
+    assert abs(float(rec[1]) - scipy.stats.entropy(p)) <= 1e-6 * scipy.stats.entropy(p)
+    _, _, rec_u = oracle.golden_row(np.full(1000, 3.25), k=16)
+    assert abs(float(rec_u[1]) - math.log(1000)) < 1e-6
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_golden_ids_brute_force_and_mass(seed):
+    g = np.random.default_rng(500 + seed)
+    v, k = 2000, 512
+    x = np.round(g.normal(0, 1.5, v), 1)      # heavy ties
+    ids, lp, rec = oracle.golden_row(x, k=k)
+    want = [j for _, j in sorted((-x[j], j) for j in range(v))][:k]
+    assert list(ids) == want
+    lse = oracle.logsumexp(x)
+    assert np.allclose(lp, (x[want] - lse).astype(np.float32), rtol=0, atol=0)
+    listed = float(np.sum(np.exp(x[want] - lse)))
+    assert abs(listed + float(rec[2]) - 1.0) < 1e-6
+    _, _, rec_more = oracle.golden_row(x, k=k + 100)
+    assert rec_more[2] <= rec[2]
+
+
+def _exact_record(x, k):
+    lse = oracle.logsumexp(x)
+    ids = np.lexsort((np.arange(x.shape[0]), -x))[:k]
+    rest = np.setdiff1d(np.arange(x.shape[0]), ids)
+    return ids, x[ids] - lse, float(np.sum(np.exp(x[rest] - lse)))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_coarse_score_brute_force_and_lower_bound(seed):
+    g = np.random.default_rng(600 + seed)
+    v, k = 300, int(g.integers(1, 40))
+    a = g.normal(0, 2, v)
+    b = a + g.normal(0, 0.3, v)
+    ids, lp, tail = _exact_record(a, k)
+    got = oracle.coarse_kl_row(ids, lp, tail, b)
+    p = np.exp(a - oracle.logsumexp(a))
+    q = np.exp(b - oracle.logsumexp(b))
+    assert abs(got - _coarsened_kl(p, q, list(ids))) < 1e-12
+    assert got <= oracle.kl_row(a, b) + 1e-12       # coarsening lowers KL (log-sum inequality)
+
+
+def test_coarse_score_all_ids_listed_is_full_kl():
+    g = np.random.default_rng(7)
+    v = 500
+    a = g.normal(0, 2, v)
+    b = a + g.normal(0, 0.5, v)
+    ids, lp, tail = _exact_record(a, v)
+    assert tail == 0.0
+    assert abs(oracle.coarse_kl_row(ids, lp, tail, b) - oracle.kl_row(a, b)) < 1e-12
+
+
+def test_coarse_score_edges():
+    a = np.log(np.array([0.5, 0.3, 0.2]))
+    ids, lp, tail = _exact_record(a, 2)
+    assert abs(oracle.coarse_kl_row(ids, lp, tail, a)) < 1e-15       # q = p
+    b = np.array([0.0, -np.inf, 0.0])                                 # a listed id with q = 0
+    assert oracle.coarse_kl_row(ids, lp, tail, b) == math.inf
+    b2 = np.array([0.0, 0.0, -np.inf])                                # q's tail cell empty
+    assert oracle.coarse_kl_row(ids, lp, tail, b2) == math.inf
