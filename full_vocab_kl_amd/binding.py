@@ -61,6 +61,8 @@ _SIGS = {
     "topk_export": (_I, [_P, _I, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _SZ, _P]),
     "kld_topk_tail": (_I, [_P, _P, _P, _P, _I64, _I, _I64, _P, _P]),
     "kld_summary": (_I, [_P, _P, _P, _P, _P, _I64, _P, _I, _P, _P, _SZ, _P]),
+    "kld_golden_export": (_I, [_P, _I, _I64, _I64, _I64, _P, _I, _P, _P, _P, _P]),
+    "kld_coarse_kl": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P, _I, _P, _P]),
     "kld_status_str": (ctypes.c_char_p, [_I]),
     "kld_abi_version": (_I, []),
 }
@@ -263,6 +265,38 @@ def kld_topk_tail(ids_p, lp_p, ids_q, lp_q, v: int, k: int = TOPK, out=None, str
     code = lib().kld_topk_tail(_ptr(ids_p), _ptr(lp_p), _ptr(ids_q), _ptr(lp_q), n, k, v, _ptr(out),
                                _stream(stream))
     _check(code, "kld_topk_tail")
+    return out
+
+
+GOLDEN_TOPK = 512
+
+
+def kld_golden_export(logits: torch.Tensor, target: torch.Tensor | None = None, out: dict | None = None,
+                      stream=None) -> dict:
+    """Golden records of [n, v] reference logits: ids [n, 512] int32, lp
+    [n, 512] f32, rec [n, 3] f32 (NLL of target, entropy, tail mass)."""
+    n, v = logits.shape
+    dt = _dtype_code(logits)
+    if out is None:
+        dev = logits.device
+        out = {"ids": torch.empty((n, GOLDEN_TOPK), dtype=torch.int32, device=dev),
+               "lp": torch.empty((n, GOLDEN_TOPK), dtype=torch.float32, device=dev),
+               "rec": torch.empty((n, 3), dtype=torch.float32, device=dev)}
+    code = lib().kld_golden_export(_ptr(logits), dt, n, v, _rows_ld(logits), _ptr(target), GOLDEN_TOPK,
+                                   _ptr(out["ids"]), _ptr(out["lp"]), _ptr(out["rec"]), _stream(stream))
+    _check(code, "kld_golden_export")
+    return out
+
+
+def kld_coarse_kl(cand: torch.Tensor, ids: torch.Tensor, lp: torch.Tensor, rec: torch.Tensor,
+                  out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """513-cell coarsened KL of [n, v] candidate logits against golden records."""
+    n, v = cand.shape
+    dt = _dtype_code(cand)
+    out = out if out is not None else torch.empty(n, dtype=torch.float32, device=cand.device)
+    code = lib().kld_coarse_kl(_ptr(cand), dt, n, v, _rows_ld(cand), _ptr(ids), _ptr(lp), _ptr(rec),
+                               GOLDEN_TOPK, _ptr(out), _stream(stream))
+    _check(code, "kld_coarse_kl")
     return out
 
 

@@ -237,6 +237,41 @@ kld_status topk_export(const void *logits, int dtype, int64_t n, int64_t v, int6
   return KLD_OK;
 }
 
+kld_status kld_golden_export(const void *logits, int dtype, int64_t n, int64_t v, int64_t ld,
+                             const int32_t *target, int k, int32_t *ids, float *lp, float *rec,
+                             void *stream) {
+  if (dtype != KLD_F32 && dtype != KLD_BF16) return KLD_EDTYPE;
+  if (n < 0 || v < 0) return KLD_EINVAL;
+  if (k != KLD_GOLDEN_TOPK) return KLD_ESHAPE;
+  if (n == 0) return KLD_OK;
+  if (n > 0x7fffffffLL || v < KLD_GOLDEN_TOPK || v > 0x7fffffffLL || ld < v) return KLD_ESHAPE;
+  if (!logits || !ids || !lp || !rec) return KLD_EINVAL;
+  const size_t esize = dtype == KLD_F32 ? 4 : 2;
+  const bool aligned = aligned16(logits) && (ld * esize) % 16 == 0;
+  if (launch_golden_export(logits, dtype, n, v, ld, aligned, target, ids, lp, rec,
+                           as_stream(stream)) != hipSuccess)
+    return KLD_EHIP;
+  return KLD_OK;
+}
+
+kld_status kld_coarse_kl(const void *cand, int dtype, int64_t n, int64_t v, int64_t ld,
+                         const int32_t *ids, const float *lp, const float *rec, int k, float *kl,
+                         void *stream) {
+  if (dtype != KLD_F32 && dtype != KLD_BF16) return KLD_EDTYPE;
+  if (n < 0 || v < 0) return KLD_EINVAL;
+  if (k != KLD_GOLDEN_TOPK) return KLD_ESHAPE;
+  if (n == 0) return KLD_OK;
+  if (n > 0x7fffffffLL || v < KLD_GOLDEN_TOPK || ld < v) return KLD_ESHAPE;
+  if (v > (int64_t(1) << 20)) return KLD_EUNSUPPORTED;
+  if (!cand || !ids || !lp || !rec || !kl) return KLD_EINVAL;
+  const size_t esize = dtype == KLD_F32 ? 4 : 2;
+  const bool aligned = aligned16(cand) && (ld * esize) % 16 == 0;
+  if (launch_coarse_kl(cand, dtype, n, v, ld, aligned, ids, lp, rec, kl, as_stream(stream)) !=
+      hipSuccess)
+    return KLD_EHIP;
+  return KLD_OK;
+}
+
 kld_status kld_topk_tail(const int32_t *ids_p, const uint16_t *lp_p, const int32_t *ids_q,
                          const uint16_t *lp_q, int64_t n, int k, int64_t v, float *kl_tail,
                          void *stream) {

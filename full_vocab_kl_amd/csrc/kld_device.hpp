@@ -278,22 +278,22 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x) {
   return x;
 }
 
-// Block-wide (256 threads) selection of the 64 largest nonzero keys among the
+// Block-wide (256 threads) selection of the R largest nonzero keys among the
 // K keys each thread holds (0 = no key; nonzero keys are distinct).  Radix
 // select, 8 bits per pass from the top: a 256-bin LDS histogram of the keys
 // that match the digits fixed so far, and wave 0 finds the bin that holds the
 // wanted rank; the passes stop early once that bin holds exactly the keys
 // still wanted (then every key at or above it is selected and the smallest of
-// them is the 64th).  Returns the 64th largest key, or 0 when fewer than 64 keys are
-// nonzero; stores the selected keys (every nonzero key when fewer than 64) in
-// top[0..63], zero-filled, in no particular order.  LDS scratch: hist[256],
+// them is the R-th).  Returns the R-th largest key, or 0 when fewer than R keys
+// are nonzero; stores the selected keys (every nonzero key when fewer than R)
+// in top[0..R-1], zero-filled, in no particular order.  LDS scratch: hist[256],
 // sh[6] 8-byte aligned; every thread of the block must call it.
-template <int K>
-__device__ __forceinline__ uint64_t block_select64(const uint64_t (&k)[K], uint64_t *top, uint32_t *hist,
-                                   uint32_t *sh) {
+template <int K, int R = 64>
+__device__ __forceinline__ uint64_t block_select_top(const uint64_t (&k)[K], uint64_t *top,
+                                                     uint32_t *hist, uint32_t *sh) {
   const int tid = threadIdx.x;
   uint64_t prefix = 0;
-  uint32_t need = 64;
+  uint32_t need = R;
   int shift = 64;        // keys are selected by their bits at and above `shift`
   bool found = true;
   for (int pass = 0; pass < 8; ++pass) {
@@ -349,7 +349,7 @@ __device__ __forceinline__ uint64_t block_select64(const uint64_t (&k)[K], uint6
     if (bucket == need) break;   // every key of the bucket is selected: the set is fixed
   }
   // Selected: the keys whose bits at and above `shift` reach the prefix (all
-  // nonzero keys when fewer than 64 exist).  T = the smallest selected key.
+  // nonzero keys when fewer than R exist).  T = the smallest selected key.
   if (tid == 0) { sh[2] = 0; sh[4] = 0xffffffffu; sh[5] = 0xffffffffu; }
   __syncthreads();
   unsigned long long *tmin = reinterpret_cast<unsigned long long *>(sh + 4);
@@ -364,9 +364,15 @@ __device__ __forceinline__ uint64_t block_select64(const uint64_t (&k)[K], uint6
   __syncthreads();
   const uint32_t cnt = sh[2];
   const uint64_t T = found ? (uint64_t)*tmin : 0ull;
-  for (uint32_t i = cnt + tid; i < 64; i += 256) top[i] = 0ull;
+  for (uint32_t i = cnt + tid; i < R; i += 256) top[i] = 0ull;
   __syncthreads();
   return T;
+}
+
+template <int K>
+__device__ __forceinline__ uint64_t block_select64(const uint64_t (&k)[K], uint64_t *top,
+                                                   uint32_t *hist, uint32_t *sh) {
+  return block_select_top<K, 64>(k, top, hist, sh);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t u) {

@@ -1,0 +1,387 @@
+// Golden records and the 513-cell score ("Qwen3.8-27B Quantization
+// Challenge": "Golden distributions", "The score").
+//
+// golden_export_kernel: one block per reference row.  One streaming pass keeps
+// the online log-sum-exp state and the entropy sum (f32 per round, f64 across
+// rounds) and filters the 512 largest (value, id) keys through an LDS
+// candidate buffer behind a threshold key (the 512th best so far, raised by a
+// block radix select whenever the buffer nears full).  The 512 are sorted by
+// a block bitonic network and written with their f32 log-probs.  A second
+// pass over the (cache-resident) row sums the probability of every id outside
+// the 512 directly, so a tiny tail mass keeps its relative accuracy instead
+// of coming out of 1 - sum of the listed probabilities.
+//
+// coarse_kl_kernel: one block per candidate row.  The record's 512 ids are
+// set in an LDS bitmap of the vocabulary; one streaming pass keeps the
+// candidate's log-sum-exp state and, separately, the mass of the unlisted
+// ids (the candidate's tail cell); then the 512 listed logits are gathered
+// and the cells summed in f64 in a fixed order.
+#include "kld.h"
+#include "kld_device.hpp"
+#include "kld_launch.hpp"
+
+namespace kld {
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int GT = 256;                  // threads per block
+constexpr int GE = 8;                    // consecutive elements per thread and round
+constexpr int GROUND = GT * GE;          // elements per round
+constexpr int GK = KLD_GOLDEN_TOPK;      // listed ids per record
+constexpr int GCAP = 4096;               // candidate keys per block
+static_assert(GCAP % GT == 0 && GCAP - GROUND >= GK, "buffer holds the kept keys plus a round");
+
+__device__ __forceinline__ float ld_f32(const float *r, int64_t j) { return r[j]; }
+__device__ __forceinline__ float ld_f32(const uint16_t *r, int64_t j) { return bf16_to_f32(r[j]); }
+
+// The GE elements at pos (a multiple of GE) of a row; elements at or past hi
+// read as -inf.  Aligned rows take 16-byte loads when the run is in range.
+template <typename T, bool ALIGNED>
+__device__ __forceinline__ void load_run(const T *__restrict__ row, int64_t pos, int64_t hi,
+                                         float (&x)[GE]) {
+  if (ALIGNED && pos + GE <= hi) {
+    if constexpr (sizeof(T) == 4) {
+      const f32x4 a = *reinterpret_cast<const f32x4 *>(row + pos);
+      const f32x4 b = *reinterpret_cast<const f32x4 *>(row + pos + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = b[e]; }
+    } else {
+      const u32x4 q = *reinterpret_cast<const u32x4 *>(row + pos);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = __uint_as_float(q[e] << 16);
+        x[2 * e + 1] = __uint_as_float(q[e] & 0xffff0000u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < GE; ++e) x[e] = pos + e < hi ? ld_f32(row, pos + e) : kNegInf;
+  }
+}
+
+// Online state of one thread: maximum m, S = sum e^(z - m), U = sum e^(z - m) (z - m)
+// (the entropy sum), W = sum e^(z - m) over a subset (the unlisted ids).
+struct LseState {
+  float m;
+  double s, u, w;
+};
+
+__device__ __forceinline__ LseState lse_merge(const LseState &a, const LseState &b) {
+  if (b.m == kNegInf) return a;
+  if (a.m == kNegInf) return b;
+  const float m = fmaxf(a.m, b.m);
+  const double fa = exp((double)a.m - (double)m), fb = exp((double)b.m - (double)m);
+  LseState r;
+  r.m = m;
+  r.s = a.s * fa + b.s * fb;
+  // (z - m) = (z - a.m) + (a.m - m)
+  r.u = fa * (a.u + ((double)a.m - (double)m) * a.s) + fb * (b.u + ((double)b.m - (double)m) * b.s);
+  r.w = a.w * fa + b.w * fb;
+  return r;
+}
+
+// Block-wide merge (fixed butterfly, then the four waves in order); every
+// thread gets the result.
+__device__ LseState lse_block(LseState st, LseState *xw) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    LseState q;
+    q.m = __shfl_xor(st.m, o);
+    q.s = __shfl_xor(st.s, o);
+    q.u = __shfl_xor(st.u, o);
+    q.w = __shfl_xor(st.w, o);
+    st = (threadIdx.x & o) ? lse_merge(q, st) : lse_merge(st, q);
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) xw[wave] = st;
+  __syncthreads();
+  LseState r = xw[0];
+#pragma unroll
+  for (int w = 1; w < GT / 64; ++w) r = lse_merge(r, xw[w]);
+  __syncthreads();
+  return r;
+}
+
+// Fixed-order block sum of one double per thread; every thread gets it.
+__device__ double sum_block(double x, double *red) {
+  red[threadIdx.x] = x;
+  __syncthreads();
+  for (int h = GT / 2; h > 0; h >>= 1) {
+    if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+    __syncthreads();
+  }
+  const double r = red[0];
+  __syncthreads();
+  return r;
+}
+
+// Fold one round's f32 partial sums (relative to m) into the thread's state,
+// after raising m to the round maximum bm when it grew.
+__device__ __forceinline__ void raise_max(LseState &st, float bm) {
+  if (bm > st.m) {
+    if (st.m != kNegInf) {
+      const double f = exp((double)st.m - (double)bm);
+      st.u = f * (st.u + ((double)st.m - (double)bm) * st.s);
+      st.s *= f;
+      st.w *= f;
+    }
+    st.m = bm;
+  }
+}
+
+struct GoldenShared {
+  uint64_t buf[GCAP];
+  uint64_t top[GK];
+  uint32_t hist[256];
+  double red[GT];
+  LseState xw[GT / 64];
+  uint64_t thr;
+  int cnt;
+  __align__(8) uint32_t sel[6];
+};
+
+// Keep the GK best keys of the buffer (sorted order is not needed here).
+__device__ void golden_compact(GoldenShared &sh) {
+  uint64_t k[GCAP / GT];
+  const int cnt = sh.cnt;
+#pragma unroll
+  for (int q = 0; q < GCAP / GT; ++q) {
+    const int e = q * GT + (int)threadIdx.x;
+    k[q] = e < cnt ? sh.buf[e] : 0ull;
+  }
+  __syncthreads();
+  const uint64_t t = block_select_top<GCAP / GT, GK>(k, sh.top, sh.hist, sh.sel);
+  // top holds the selected keys first, then zeros
+  for (int i = (int)threadIdx.x; i < GK; i += GT) sh.buf[i] = sh.top[i];
+  if (threadIdx.x == 0) {
+    int kept = 0;
+    while (kept < GK && sh.top[kept] != 0ull) ++kept;
+    sh.cnt = kept;
+    // GK keys at or above t exist, so no other key below or at t can be
+    // among the GK best (keys are distinct)
+    if (t != 0ull) sh.thr = t;
+  }
+  __syncthreads();
+}
+
+template <typename T, bool ALIGNED>
+__global__ __launch_bounds__(GT) void golden_export_kernel(
+    const T *__restrict__ logits, int64_t ld, int64_t v, const int32_t *__restrict__ target,
+    int32_t *__restrict__ ids, float *__restrict__ lp, float *__restrict__ rec) {
+  __shared__ GoldenShared sh;
+  const int64_t row = blockIdx.x;
+  const T *r = logits + row * ld;
+  if (threadIdx.x == 0) { sh.cnt = 0; sh.thr = 0ull; }
+  __syncthreads();
+
+  LseState st{kNegInf, 0.0, 0.0, 0.0};
+  const int64_t rounds = (v + GROUND - 1) / GROUND;
+  for (int64_t rd = 0; rd < rounds; ++rd) {
+    const int64_t pos = rd * GROUND + (int64_t)threadIdx.x * GE;
+    float x[GE];
+    load_run<T, ALIGNED>(r, pos, v, x);
+    float bm = kNegInf;
+#pragma unroll
+    for (int e = 0; e < GE; ++e) bm = fmaxf(bm, x[e]);
+    raise_max(st, bm);
+    float ps = 0.f, pu = 0.f;
+    if (st.m != kNegInf) {
+#pragma unroll
+      for (int e = 0; e < GE; ++e) {
+        const float d = x[e] - st.m;
+        const float w = exp2_fast(d * kL2E);
+        ps += w;
+        pu = fmaf(w, fmaxf(d, -kFltMax), pu);   // a -inf logit (w = 0) adds exactly 0
+      }
+    }
+    st.s += (double)ps;
+    st.u += (double)pu;
+    // candidates: keys above the threshold (NaN logits are never listed)
+    const uint64_t th = sh.thr;
+#pragma unroll
+    for (int e = 0; e < GE; ++e) {
+      if (pos + e < v && x[e] == x[e]) {
+        const uint64_t key = topk_key(x[e], (int)(pos + e));
+        if (key > th) sh.buf[atomicAdd(&sh.cnt, 1)] = key;
+      }
+    }
+    __syncthreads();
+    if (sh.cnt > GCAP - GROUND) golden_compact(sh);
+  }
+  golden_compact(sh);
+  // the GK best keys, sorted descending (zero keys -- fewer than GK valid
+  // ids -- sort last)
+  __syncthreads();
+  bitonic_desc<GT>(sh.top, GK);
+  const LseState tot = lse_block(st, sh.xw);
+  const double ls = log(tot.s);
+  const double lse = (double)tot.m + ls;
+  const uint64_t t512 = sh.top[GK - 1];
+  for (int i = (int)threadIdx.x; i < GK; i += GT) {
+    const uint64_t key = sh.top[i];
+    ids[row * GK + i] = key ? key_id(key) : 0;
+    lp[row * GK + i] = key ? (float)((double)key_value(key) - lse) : kNegInf;
+  }
+  // second pass: the mass of every id outside the GK listed ones
+  double tail = 0.0;
+  for (int64_t rd = 0; rd < rounds; ++rd) {
+    const int64_t pos = rd * GROUND + (int64_t)threadIdx.x * GE;
+    float x[GE];
+    load_run<T, ALIGNED>(r, pos, v, x);
+    float pt = 0.f;
+#pragma unroll
+    for (int e = 0; e < GE; ++e) {
+      if (pos + e < v && x[e] == x[e] && topk_key(x[e], (int)(pos + e)) < t512)
+        pt += exp2_fast((float)(((double)x[e] - lse) * kL2E));
+    }
+    tail += (double)pt;
+  }
+  tail = sum_block(tail, sh.red);
+  if (threadIdx.x == 0) {
+    float nll = __builtin_nanf("");
+    if (target) {
+      const int32_t tg = target[row];
+      if (tg >= 0 && (int64_t)tg < v) nll = (float)(lse - (double)ld_f32(r, tg));
+    }
+    rec[row * 3 + 0] = nll;
+    rec[row * 3 + 1] = (float)(ls - tot.u / tot.s);   // H = ln S - U / S
+    rec[row * 3 + 2] = (float)tail;
+  }
+}
+
+template <typename T, bool ALIGNED>
+__global__ __launch_bounds__(GT) void coarse_kl_kernel(
+    const T *__restrict__ cand, int64_t ld, int64_t v, const int32_t *__restrict__ ids,
+    const float *__restrict__ lp, const float *__restrict__ rec, float *__restrict__ kl) {
+  extern __shared__ uint32_t listed[];   // bitmap of the record's ids, ceil(v / 32) words
+  __shared__ double red[GT];
+  __shared__ LseState xw[GT / 64];
+  __shared__ int bad;
+  const int64_t row = blockIdx.x;
+  const T *r = cand + row * ld;
+  const int64_t words = (v + 31) / 32;
+  for (int64_t w = threadIdx.x; w < words; w += GT) listed[w] = 0u;
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
+  for (int i = (int)threadIdx.x; i < GK; i += GT) {
+    const int32_t id = ids[row * GK + i];
+    if (id < 0 || (int64_t)id >= v) bad = 1;
+    else atomicOr(&listed[id >> 5], 1u << (id & 31));
+  }
+  __syncthreads();
+
+  LseState st{kNegInf, 0.0, 0.0, 0.0};
+  const int64_t rounds = (v + GROUND - 1) / GROUND;
+  for (int64_t rd = 0; rd < rounds; ++rd) {
+    const int64_t pos = rd * GROUND + (int64_t)threadIdx.x * GE;
+    float x[GE];
+    load_run<T, ALIGNED>(r, pos, v, x);
+    float bm = kNegInf;
+#pragma unroll
+    for (int e = 0; e < GE; ++e) bm = fmaxf(bm, x[e]);
+    raise_max(st, bm);
+    // pos is a multiple of 8: its 8 flags sit in one bitmap word
+    const uint32_t flags = pos < v ? (listed[pos >> 5] >> (pos & 31)) & 0xffu : 0u;
+    float ps = 0.f, pw = 0.f;
+    if (st.m != kNegInf) {
+#pragma unroll
+      for (int e = 0; e < GE; ++e) {
+        const float w = exp2_fast((x[e] - st.m) * kL2E);
+        ps += w;
+        if (!((flags >> e) & 1u)) pw += w;
+      }
+    }
+    st.s += (double)ps;
+    st.w += (double)pw;
+  }
+  const LseState tot = lse_block(st, xw);
+  const double lse = (double)tot.m + log(tot.s);
+  const double q_t = tot.w / tot.s;
+  // listed cells, then the tail cell; +inf when p > 0 meets q = 0
+  double part = 0.0;
+  int inf = 0;
+  for (int i = (int)threadIdx.x; i < GK; i += GT) {
+    const int32_t id = ids[row * GK + i];
+    if (id < 0 || (int64_t)id >= v) continue;
+    const double l = (double)lp[row * GK + i];
+    const double p = exp(l);
+    if (p == 0.0) continue;
+    const float z = ld_f32(r, id);
+    if (z == kNegInf) { inf = 1; continue; }
+    part += p * (l - ((double)z - lse));
+  }
+  if (inf) atomicOr(&bad, 2);
+  double total = sum_block(part, red);
+  if (threadIdx.x == 0) {
+    const double p_t = (double)rec[row * 3 + 2];
+    int b = bad;
+    if (p_t > 0.0) {
+      if (q_t == 0.0) b |= 2;
+      else total += p_t * (log(p_t) - log(q_t));
+    }
+    const bool nan_in = !(tot.s > 0.0) || tot.m != tot.m || tot.m == __builtin_huge_valf();
+    kl[row] = (b & 1) || nan_in ? __builtin_nanf("") : (b & 2) ? __builtin_huge_valf() : (float)total;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_golden_export(const void *logits, int dtype, int64_t n, int64_t v, int64_t ld,
+                                bool aligned, const int32_t *target, int32_t *ids, float *lp,
+                                float *rec, hipStream_t stream) {
+  const dim3 grid((unsigned)n), block(GT);
+  if (dtype == 0) {
+    if (aligned)
+      hipLaunchKernelGGL((golden_export_kernel<float, true>), grid, block, 0, stream,
+                         (const float *)logits, ld, v, target, ids, lp, rec);
+    else
+      hipLaunchKernelGGL((golden_export_kernel<float, false>), grid, block, 0, stream,
+                         (const float *)logits, ld, v, target, ids, lp, rec);
+  } else {
+    if (aligned)
+      hipLaunchKernelGGL((golden_export_kernel<uint16_t, true>), grid, block, 0, stream,
+                         (const uint16_t *)logits, ld, v, target, ids, lp, rec);
+    else
+      hipLaunchKernelGGL((golden_export_kernel<uint16_t, false>), grid, block, 0, stream,
+                         (const uint16_t *)logits, ld, v, target, ids, lp, rec);
+  }
+  return hipGetLastError();
+}
+
+size_t coarse_kl_lds_bytes(int64_t v) { return (size_t)((v + 31) / 32) * 4; }
+
+hipError_t launch_coarse_kl(const void *cand, int dtype, int64_t n, int64_t v, int64_t ld,
+                            bool aligned, const int32_t *ids, const float *lp, const float *rec,
+                            float *kl, hipStream_t stream) {
+  const dim3 grid((unsigned)n), block(GT);
+  const size_t lds = coarse_kl_lds_bytes(v);
+  const void *kern = dtype == 0 ? (aligned ? (const void *)coarse_kl_kernel<float, true>
+                                           : (const void *)coarse_kl_kernel<float, false>)
+                                : (aligned ? (const void *)coarse_kl_kernel<uint16_t, true>
+                                           : (const void *)coarse_kl_kernel<uint16_t, false>);
+  // the bitmap is dynamic LDS: allow more than the 64 KB default (set on every
+  // call, host-side and cheap, so no library state is kept)
+  hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  if (dtype == 0) {
+    if (aligned)
+      hipLaunchKernelGGL((coarse_kl_kernel<float, true>), grid, block, lds, stream,
+                         (const float *)cand, ld, v, ids, lp, rec, kl);
+    else
+      hipLaunchKernelGGL((coarse_kl_kernel<float, false>), grid, block, lds, stream,
+                         (const float *)cand, ld, v, ids, lp, rec, kl);
+  } else {
+    if (aligned)
+      hipLaunchKernelGGL((coarse_kl_kernel<uint16_t, true>), grid, block, lds, stream,
+                         (const uint16_t *)cand, ld, v, ids, lp, rec, kl);
+    else
+      hipLaunchKernelGGL((coarse_kl_kernel<uint16_t, false>), grid, block, lds, stream,
+                         (const uint16_t *)cand, ld, v, ids, lp, rec, kl);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kld

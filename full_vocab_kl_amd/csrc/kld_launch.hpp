@@ -106,4 +106,13 @@ struct SummaryArgs {
 size_t summary_workspace_bytes(int64_t n);
 hipError_t launch_summary(const SummaryArgs &a, void *ws);
 
+// golden records and the 513-cell score (kld_golden.hip)
+hipError_t launch_golden_export(const void *logits, int dtype, int64_t n, int64_t v, int64_t ld,
+                                bool aligned, const int32_t *target, int32_t *ids, float *lp,
+                                float *rec, hipStream_t stream);
+size_t coarse_kl_lds_bytes(int64_t v);
+hipError_t launch_coarse_kl(const void *cand, int dtype, int64_t n, int64_t v, int64_t ld,
+                            bool aligned, const int32_t *ids, const float *lp, const float *rec,
+                            float *kl, hipStream_t stream);
+
 }  // namespace kld

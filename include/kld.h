@@ -21,6 +21,10 @@
  *    "Files", "Method".)
  *  - Mean / median / p99 / p99.9 KLD, top-1 rate and perplexities.
  *    ("The score"; "Qwen3.8-27B IQ8R": "Quality".)
+ *  - Golden records (the 512 most likely ids with f32 log-probs, the NLL of
+ *    the true next token, the entropy and the tail mass) and the 513-cell
+ *    coarsened KL of a candidate against them.  ("Qwen3.8-27B Quantization
+ *    Challenge": "Golden distributions", "The score".)
  *
  * Conventions shared by every entry point:
  *
@@ -52,6 +56,7 @@ extern "C" {
 
 #define KLD_ABI_VERSION 1
 #define KLD_TOPK 64           /* the export width the quality-eval reference uses */
+#define KLD_GOLDEN_TOPK 512   /* ids listed per golden record (the challenge's references) */
 #define KLD_MAX_QUANTILES 16
 
 typedef enum kld_status {
@@ -202,6 +207,52 @@ kld_status kld_summary(const float *kl, const int32_t *argmax_ref, const int32_t
                        const float *nll_ref, const float *nll_cand, int64_t n,
                        const double *quantiles, int nq, double *out, void *ws, size_t ws_bytes,
                        void *stream);
+
+/*
+ * kld_golden_export -- the golden record of each reference row ("Qwen3.8-27B
+ * Quantization Challenge", "Golden distributions": the 512 most likely
+ * tokens exactly, most likely first, as {int32 id, float32 log p}, plus the
+ * reference's NLL of the true next token, its entropy in nats and the tail
+ * mass of the rest).
+ *
+ * logits : [n, v] reference logits (dtype f32 or bf16 bits), leading
+ *          dimension ld >= v, v >= 512.
+ * target : [n] true next-token ids, or NULL (then rec[i][0] = NaN).
+ * k      : must be KLD_GOLDEN_TOPK (512).
+ * ids    : [n, 512] int32 output: ids by probability, descending, ties to the
+ *          lower id.
+ * lp     : [n, 512] f32 output: log p = logit - lse of the listed ids.
+ * rec    : [n, 3] f32 output: NLL of target (lse - logit[target]), entropy
+ *          -sum_j p_j ln p_j over every id, and the tail mass: the sum of p
+ *          over the ids outside the 512, summed directly (not 1 - the listed
+ *          mass, which would drown a tiny tail in rounding).
+ * Needs no workspace.  Rows holding NaN logits give unspecified records.
+ * Pointers need 4-byte alignment (logits: its element size).
+ */
+kld_status kld_golden_export(const void *logits, int dtype, int64_t n, int64_t v, int64_t ld,
+                             const int32_t *target, int k, int32_t *ids, float *lp, float *rec,
+                             void *stream);
+
+/*
+ * kld_coarse_kl -- the 513-cell score of candidate rows against golden
+ * records ("Qwen3.8-27B Quantization Challenge", "The score"): the
+ * candidate's distribution q is coarsened onto the record's cells -- its 512
+ * listed ids and one tail cell holding the rest of q's mass -- and
+ * KL(p || q) = sum over the cells of p_i (ln p_i - ln q_i), with p_i =
+ * exp(lp_i) and p_tail = rec[i][2] as stored.
+ *
+ * cand   : [n, v] candidate logits (dtype f32 or bf16 bits), ld >= v,
+ *          512 <= v <= 2^20 (the listed ids live in an LDS bitmap of v bits).
+ * ids, lp, rec : the records as kld_golden_export writes them; ids distinct.
+ * k      : must be KLD_GOLDEN_TOPK.
+ * kl     : [n] f32 output.  A cell with p = 0 adds 0; p > 0 against q = 0
+ *          gives +inf; a listed id outside [0, v) or a candidate row with a
+ *          NaN or +inf logit gives NaN.
+ * Needs no workspace.  Pointers need 4-byte alignment (cand: its element size).
+ */
+kld_status kld_coarse_kl(const void *cand, int dtype, int64_t n, int64_t v, int64_t ld,
+                         const int32_t *ids, const float *lp, const float *rec, int k, float *kl,
+                         void *stream);
 
 /* Human-readable name of a status code (static string). */
 const char *kld_status_str(int status);

@@ -117,3 +117,21 @@ def test_topk_and_tail_validation_fails_closed():
     assert lib.kld_topk_tail(16, 16, 16, 16, 4, 64, 64, 16, None) == 2
     assert lib.kld_topk_tail(None, 16, 16, 16, 4, 64, 1000, 16, None) == 1
     assert lib.kld_topk_tail(16, 16, 16, 16, 0, 64, 1000, 16, None) == 0
+
+
+def test_golden_and_coarse_validation_fails_closed():
+    lib = kld.lib()
+    # kld_golden_export(logits, dtype, n, v, ld, target, k, ids, lp, rec, stream)
+    assert lib.kld_golden_export(16, 5, 4, 1000, 1000, None, 512, 16, 16, 16, None) == 3
+    assert lib.kld_golden_export(16, 0, -1, 1000, 1000, None, 512, 16, 16, 16, None) == 1
+    assert lib.kld_golden_export(16, 0, 4, 1000, 1000, None, 64, 16, 16, 16, None) == 2
+    assert lib.kld_golden_export(16, 0, 4, 511, 511, None, 512, 16, 16, 16, None) == 2
+    assert lib.kld_golden_export(16, 0, 4, 1000, 999, None, 512, 16, 16, 16, None) == 2
+    assert lib.kld_golden_export(None, 0, 4, 1000, 1000, None, 512, 16, 16, 16, None) == 1
+    assert lib.kld_golden_export(16, 0, 0, 1000, 1000, None, 512, None, None, None, None) == 0
+    # kld_coarse_kl(cand, dtype, n, v, ld, ids, lp, rec, k, kl, stream)
+    assert lib.kld_coarse_kl(16, 9, 4, 1000, 1000, 16, 16, 16, 512, 16, None) == 3
+    assert lib.kld_coarse_kl(16, 1, 4, 1000, 1000, 16, 16, 16, 100, 16, None) == 2
+    assert lib.kld_coarse_kl(16, 1, 4, 1000, 1000, 16, None, 16, 512, 16, None) == 1
+    assert lib.kld_coarse_kl(16, 1, 4, (1 << 20) + 1, (1 << 20) + 1, 16, 16, 16, 512, 16, None) == 5
+    assert lib.kld_coarse_kl(16, 1, 0, 1000, 1000, None, None, None, 512, None, None) == 0
