@@ -14,7 +14,7 @@ import torch
 
 TOPK = 64
 KLD_F32, KLD_BF16 = 0, 1
-OP_FROM_LOGITS, OP_FUSED_HEAD, OP_TOPK_EXPORT, OP_SUMMARY = 0, 1, 2, 3
+OP_FROM_LOGITS, OP_FUSED_HEAD, OP_TOPK_EXPORT, OP_SUMMARY, OP_COARSE_KL = 0, 1, 2, 3, 4
 FLAG_TOPK = 1
 N_SUMMARY_FIXED = 8
 
@@ -62,7 +62,7 @@ _SIGS = {
     "kld_topk_tail": (_I, [_P, _P, _P, _P, _I64, _I, _I64, _P, _P]),
     "kld_summary": (_I, [_P, _P, _P, _P, _P, _I64, _P, _I, _P, _P, _SZ, _P]),
     "kld_golden_export": (_I, [_P, _I, _I64, _I64, _I64, _P, _I, _P, _P, _P, _P]),
-    "kld_coarse_kl": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P, _I, _P, _P]),
+    "kld_coarse_kl": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P, _I, _P, _P, _SZ, _P]),
     "kld_status_str": (ctypes.c_char_p, [_I]),
     "kld_abi_version": (_I, []),
 }
@@ -289,13 +289,15 @@ def kld_golden_export(logits: torch.Tensor, target: torch.Tensor | None = None, 
 
 
 def kld_coarse_kl(cand: torch.Tensor, ids: torch.Tensor, lp: torch.Tensor, rec: torch.Tensor,
-                  out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                  out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                  stream=None) -> torch.Tensor:
     """513-cell coarsened KL of [n, v] candidate logits against golden records."""
     n, v = cand.shape
     dt = _dtype_code(cand)
     out = out if out is not None else torch.empty(n, dtype=torch.float32, device=cand.device)
+    ws, need = _workspace(OP_COARSE_KL, n, v, 0, 0, cand.device, ws)
     code = lib().kld_coarse_kl(_ptr(cand), dt, n, v, _rows_ld(cand), _ptr(ids), _ptr(lp), _ptr(rec),
-                               GOLDEN_TOPK, _ptr(out), _stream(stream))
+                               GOLDEN_TOPK, _ptr(out), _ptr(ws), ws.numel(), _stream(stream))
     _check(code, "kld_coarse_kl")
     return out
 

@@ -130,6 +130,11 @@ size_t kld_workspace_size(int op, int64_t n, int64_t v, int64_t d, int flags) {
     case KLD_OP_TOPK_EXPORT: return logits_workspace(n, v, KLD_FLAG_TOPK, &c);
     case KLD_OP_FUSED_HEAD: return fused_workspace(n, v, flags, &c);
     case KLD_OP_SUMMARY: return round_up(summary_workspace_bytes(n), kAlign);
+    case KLD_OP_COARSE_KL: {
+      if (n == 0 || v == 0) return 0;
+      const CoarseGeom g = coarse_geom(n, v);
+      return round_up((size_t)n * g.splits * coarse_state_bytes(), kAlign);
+    }
     default: return 0;
   }
 }
@@ -256,17 +261,17 @@ kld_status kld_golden_export(const void *logits, int dtype, int64_t n, int64_t v
 
 kld_status kld_coarse_kl(const void *cand, int dtype, int64_t n, int64_t v, int64_t ld,
                          const int32_t *ids, const float *lp, const float *rec, int k, float *kl,
-                         void *stream) {
+                         void *ws, size_t ws_bytes, void *stream) {
   if (dtype != KLD_F32 && dtype != KLD_BF16) return KLD_EDTYPE;
   if (n < 0 || v < 0) return KLD_EINVAL;
   if (k != KLD_GOLDEN_TOPK) return KLD_ESHAPE;
   if (n == 0) return KLD_OK;
-  if (n > 0x7fffffffLL || v < KLD_GOLDEN_TOPK || ld < v) return KLD_ESHAPE;
-  if (v > (int64_t(1) << 20)) return KLD_EUNSUPPORTED;
+  if (n > 0x7fffffffLL || v < KLD_GOLDEN_TOPK || v > 0x7fffffffLL || ld < v) return KLD_ESHAPE;
   if (!cand || !ids || !lp || !rec || !kl) return KLD_EINVAL;
+  if (!ws || ws_bytes < kld_workspace_size(KLD_OP_COARSE_KL, n, v, 0, 0)) return KLD_EWORKSPACE;
   const size_t esize = dtype == KLD_F32 ? 4 : 2;
   const bool aligned = aligned16(cand) && (ld * esize) % 16 == 0;
-  if (launch_coarse_kl(cand, dtype, n, v, ld, aligned, ids, lp, rec, kl, as_stream(stream)) !=
+  if (launch_coarse_kl(cand, dtype, n, v, ld, aligned, ids, lp, rec, kl, ws, as_stream(stream)) !=
       hipSuccess)
     return KLD_EHIP;
   return KLD_OK;

@@ -11,11 +11,14 @@
 // the 512 directly, so a tiny tail mass keeps its relative accuracy instead
 // of coming out of 1 - sum of the listed probabilities.
 //
-// coarse_kl_kernel: one block per candidate row.  The record's 512 ids are
-// set in an LDS bitmap of the vocabulary; one streaming pass keeps the
-// candidate's log-sum-exp state and, separately, the mass of the unlisted
-// ids (the candidate's tail cell); then the 512 listed logits are gathered
-// and the cells summed in f64 in a fixed order.
+// coarse_partial_kernel + coarse_finalize_kernel: a candidate row is split
+// into ranges of at most 131,072 ids, one block each.  A block sets the
+// record's listed ids of its range in an LDS bitmap and streams the range
+// once, keeping the online log-sum-exp state and, separately, the mass of the
+// unlisted ids (the candidate's tail cell, summed directly so that a tiny
+// tail keeps its relative accuracy).  The finalize kernel merges a row's
+// ranges in order (f64), gathers the 512 listed logits and sums the cells in
+// f64 in a fixed order, one wave per row.
 #include "kld.h"
 #include "kld_device.hpp"
 #include "kld_launch.hpp"
@@ -252,78 +255,128 @@ __global__ __launch_bounds__(GT) void golden_export_kernel(
   }
 }
 
-template <typename T, bool ALIGNED>
-__global__ __launch_bounds__(GT) void coarse_kl_kernel(
-    const T *__restrict__ cand, int64_t ld, int64_t v, const int32_t *__restrict__ ids,
-    const float *__restrict__ lp, const float *__restrict__ rec, float *__restrict__ kl) {
-  extern __shared__ uint32_t listed[];   // bitmap of the record's ids, ceil(v / 32) words
-  __shared__ double red[GT];
+constexpr int CMAXW = 4096;              // bitmap words per range: 131,072 ids (16 KB)
+
+// The VEC elements at pos of a row (pos a multiple of VEC); past hi: -inf.
+template <typename T, int VEC, bool ALIGNED>
+__device__ __forceinline__ void load_vecn(const T *__restrict__ row, int64_t pos, int64_t hi,
+                                          float (&x)[VEC]) {
+  if (ALIGNED && pos + VEC <= hi) {
+    if constexpr (sizeof(T) == 4) {
+      const f32x4 q = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + pos));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = q[e];
+    } else {
+      const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row + pos));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = __uint_as_float(q[e] << 16);
+        x[2 * e + 1] = __uint_as_float(q[e] & 0xffff0000u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) x[e] = pos + e < hi ? ld_f32(row, pos + e) : kNegInf;
+  }
+}
+
+template <typename T, int VEC, int U, bool ALIGNED>
+__global__ __launch_bounds__(GT) void coarse_partial_kernel(
+    const T *__restrict__ cand, int64_t ld, int64_t v, int64_t chunk, int splits,
+    const int32_t *__restrict__ ids, LseState *__restrict__ part) {
+  __shared__ uint32_t listed[CMAXW];   // the record's ids in [lo, hi), bit (id - lo)
   __shared__ LseState xw[GT / 64];
-  __shared__ int bad;
-  const int64_t row = blockIdx.x;
+  const int64_t row = blockIdx.x / splits;
+  const int split = (int)(blockIdx.x % splits);
+  const int64_t lo = (int64_t)split * chunk;
+  const int64_t hi = lo + chunk < v ? lo + chunk : v;
   const T *r = cand + row * ld;
-  const int64_t words = (v + 31) / 32;
-  for (int64_t w = threadIdx.x; w < words; w += GT) listed[w] = 0u;
-  if (threadIdx.x == 0) bad = 0;
+  for (int w = (int)threadIdx.x; w < CMAXW; w += GT) listed[w] = 0u;
   __syncthreads();
   for (int i = (int)threadIdx.x; i < GK; i += GT) {
     const int32_t id = ids[row * GK + i];
-    if (id < 0 || (int64_t)id >= v) bad = 1;
-    else atomicOr(&listed[id >> 5], 1u << (id & 31));
+    if ((int64_t)id >= lo && (int64_t)id < hi) {
+      const int64_t o = id - lo;
+      atomicOr(&listed[o >> 5], 1u << (o & 31));
+    }
   }
   __syncthreads();
 
+  constexpr int64_t kStride = (int64_t)GT * VEC;
   LseState st{kNegInf, 0.0, 0.0, 0.0};
-  const int64_t rounds = (v + GROUND - 1) / GROUND;
+  const int64_t rounds = (hi - lo + kStride * U - 1) / (kStride * U);
   for (int64_t rd = 0; rd < rounds; ++rd) {
-    const int64_t pos = rd * GROUND + (int64_t)threadIdx.x * GE;
-    float x[GE];
-    load_run<T, ALIGNED>(r, pos, v, x);
+    const int64_t base = lo + rd * kStride * U + (int64_t)threadIdx.x * VEC;
+    float x[U][VEC];
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_vecn<T, VEC, ALIGNED>(r, base + u * kStride, hi, x[u]);
     float bm = kNegInf;
 #pragma unroll
-    for (int e = 0; e < GE; ++e) bm = fmaxf(bm, x[e]);
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) bm = fmaxf(bm, x[u][e]);
     raise_max(st, bm);
-    // pos is a multiple of 8: its 8 flags sit in one bitmap word
-    const uint32_t flags = pos < v ? (listed[pos >> 5] >> (pos & 31)) & 0xffu : 0u;
     float ps = 0.f, pw = 0.f;
     if (st.m != kNegInf) {
 #pragma unroll
-      for (int e = 0; e < GE; ++e) {
-        const float w = exp2_fast((x[e] - st.m) * kL2E);
-        ps += w;
-        if (!((flags >> e) & 1u)) pw += w;
+      for (int u = 0; u < U; ++u) {
+        // offsets from lo are multiples of VEC, so the vector's flags sit in one word
+        const int64_t o = base + u * kStride - lo;
+        const uint32_t flags = o < hi - lo ? listed[o >> 5] >> (o & 31) : 0u;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float w = exp2_fast((x[u][e] - st.m) * kL2E);
+          ps += w;
+          if (!((flags >> e) & 1u)) pw += w;
+        }
       }
     }
     st.s += (double)ps;
     st.w += (double)pw;
   }
   const LseState tot = lse_block(st, xw);
+  if (threadIdx.x == 0) part[row * splits + split] = tot;
+}
+
+__global__ __launch_bounds__(GT) void coarse_finalize_kernel(
+    const LseState *__restrict__ part, int splits, int64_t n, const void *__restrict__ cand,
+    int dtype, int64_t ld, int64_t v, const int32_t *__restrict__ ids,
+    const float *__restrict__ lp, const float *__restrict__ rec, float *__restrict__ kl) {
+  const int64_t row = (int64_t)blockIdx.x * (GT / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n) return;
+  LseState tot = part[row * splits];
+  for (int i = 1; i < splits; ++i) tot = lse_merge(tot, part[row * splits + i]);
   const double lse = (double)tot.m + log(tot.s);
   const double q_t = tot.w / tot.s;
-  // listed cells, then the tail cell; +inf when p > 0 meets q = 0
-  double part = 0.0;
-  int inf = 0;
-  for (int i = (int)threadIdx.x; i < GK; i += GT) {
+  double acc = 0.0;
+  int flags = 0;   // 1: an id outside [0, v); 2: p > 0 against q = 0
+  for (int i = lane; i < GK; i += 64) {
     const int32_t id = ids[row * GK + i];
-    if (id < 0 || (int64_t)id >= v) continue;
+    if (id < 0 || (int64_t)id >= v) { flags |= 1; continue; }
     const double l = (double)lp[row * GK + i];
     const double p = exp(l);
     if (p == 0.0) continue;
-    const float z = ld_f32(r, id);
-    if (z == kNegInf) { inf = 1; continue; }
-    part += p * (l - ((double)z - lse));
+    const float z = dtype == 0 ? reinterpret_cast<const float *>(cand)[row * ld + id]
+                               : bf16_to_f32(reinterpret_cast<const uint16_t *>(cand)[row * ld + id]);
+    if (z == kNegInf) { flags |= 2; continue; }
+    acc += p * (l - ((double)z - lse));
   }
-  if (inf) atomicOr(&bad, 2);
-  double total = sum_block(part, red);
-  if (threadIdx.x == 0) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    acc += __shfl_xor(acc, o);
+    flags |= __shfl_xor(flags, o);
+  }
+  if (lane == 0) {
     const double p_t = (double)rec[row * 3 + 2];
-    int b = bad;
     if (p_t > 0.0) {
-      if (q_t == 0.0) b |= 2;
-      else total += p_t * (log(p_t) - log(q_t));
+      if (q_t == 0.0) flags |= 2;
+      else acc += p_t * (log(p_t) - log(q_t));
     }
-    const bool nan_in = !(tot.s > 0.0) || tot.m != tot.m || tot.m == __builtin_huge_valf();
-    kl[row] = (b & 1) || nan_in ? __builtin_nanf("") : (b & 2) ? __builtin_huge_valf() : (float)total;
+    const bool nan_in = !(tot.s > 0.0) || tot.s != tot.s || tot.m != tot.m ||
+                        tot.m == __builtin_huge_valf();
+    kl[row] = (flags & 1) || nan_in ? __builtin_nanf("") : (flags & 2) ? __builtin_huge_valf()
+                                                                     : (float)acc;
   }
 }
 
@@ -351,36 +404,49 @@ hipError_t launch_golden_export(const void *logits, int dtype, int64_t n, int64_
   return hipGetLastError();
 }
 
-size_t coarse_kl_lds_bytes(int64_t v) { return (size_t)((v + 31) / 32) * 4; }
+CoarseGeom coarse_geom(int64_t n, int64_t v) {
+  // ranges of at most 131,072 ids, a multiple of 256, and about 2048 blocks
+  int64_t want = n > 0 ? (2048 + n - 1) / n : 1;
+  const int64_t min_splits = (v + 131071) / 131072;
+  const int64_t max_splits = (v + 4095) / 4096;
+  if (want > max_splits) want = max_splits;
+  if (want < min_splits) want = min_splits;
+  if (want < 1) want = 1;
+  int64_t chunk = (v + want - 1) / want;
+  chunk = (chunk + 255) / 256 * 256;
+  CoarseGeom g;
+  g.chunk = chunk;
+  g.splits = (int)((v + chunk - 1) / chunk);
+  return g;
+}
+
+size_t coarse_state_bytes() { return sizeof(LseState); }
 
 hipError_t launch_coarse_kl(const void *cand, int dtype, int64_t n, int64_t v, int64_t ld,
                             bool aligned, const int32_t *ids, const float *lp, const float *rec,
-                            float *kl, hipStream_t stream) {
-  const dim3 grid((unsigned)n), block(GT);
-  const size_t lds = coarse_kl_lds_bytes(v);
-  const void *kern = dtype == 0 ? (aligned ? (const void *)coarse_kl_kernel<float, true>
-                                           : (const void *)coarse_kl_kernel<float, false>)
-                                : (aligned ? (const void *)coarse_kl_kernel<uint16_t, true>
-                                           : (const void *)coarse_kl_kernel<uint16_t, false>);
-  // the bitmap is dynamic LDS: allow more than the 64 KB default (set on every
-  // call, host-side and cheap, so no library state is kept)
-  hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
+                            float *kl, void *part_ws, hipStream_t stream) {
+  const CoarseGeom g = coarse_geom(n, v);
+  LseState *part = static_cast<LseState *>(part_ws);
+  const dim3 grid((unsigned)(n * g.splits)), block(GT);
   if (dtype == 0) {
     if (aligned)
-      hipLaunchKernelGGL((coarse_kl_kernel<float, true>), grid, block, lds, stream,
-                         (const float *)cand, ld, v, ids, lp, rec, kl);
+      hipLaunchKernelGGL((coarse_partial_kernel<float, 4, 4, true>), grid, block, 0, stream,
+                         (const float *)cand, ld, v, g.chunk, g.splits, ids, part);
     else
-      hipLaunchKernelGGL((coarse_kl_kernel<float, false>), grid, block, lds, stream,
-                         (const float *)cand, ld, v, ids, lp, rec, kl);
+      hipLaunchKernelGGL((coarse_partial_kernel<float, 4, 4, false>), grid, block, 0, stream,
+                         (const float *)cand, ld, v, g.chunk, g.splits, ids, part);
   } else {
     if (aligned)
-      hipLaunchKernelGGL((coarse_kl_kernel<uint16_t, true>), grid, block, lds, stream,
-                         (const uint16_t *)cand, ld, v, ids, lp, rec, kl);
+      hipLaunchKernelGGL((coarse_partial_kernel<uint16_t, 8, 2, true>), grid, block, 0, stream,
+                         (const uint16_t *)cand, ld, v, g.chunk, g.splits, ids, part);
     else
-      hipLaunchKernelGGL((coarse_kl_kernel<uint16_t, false>), grid, block, lds, stream,
-                         (const uint16_t *)cand, ld, v, ids, lp, rec, kl);
+      hipLaunchKernelGGL((coarse_partial_kernel<uint16_t, 8, 2, false>), grid, block, 0, stream,
+                         (const uint16_t *)cand, ld, v, g.chunk, g.splits, ids, part);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(coarse_finalize_kernel, dim3((unsigned)((n + 3) / 4)), block, 0, stream, part,
+                     g.splits, n, cand, dtype, ld, v, ids, lp, rec, kl);
   return hipGetLastError();
 }
 

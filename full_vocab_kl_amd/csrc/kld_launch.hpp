@@ -110,9 +110,14 @@ hipError_t launch_summary(const SummaryArgs &a, void *ws);
 hipError_t launch_golden_export(const void *logits, int dtype, int64_t n, int64_t v, int64_t ld,
                                 bool aligned, const int32_t *target, int32_t *ids, float *lp,
                                 float *rec, hipStream_t stream);
-size_t coarse_kl_lds_bytes(int64_t v);
+struct CoarseGeom {
+  int splits;
+  int64_t chunk;
+};
+CoarseGeom coarse_geom(int64_t n, int64_t v);
+size_t coarse_state_bytes();   // per (row, range) partial state in the workspace
 hipError_t launch_coarse_kl(const void *cand, int dtype, int64_t n, int64_t v, int64_t ld,
                             bool aligned, const int32_t *ids, const float *lp, const float *rec,
-                            float *kl, hipStream_t stream);
+                            float *kl, void *part_ws, hipStream_t stream);
 
 }  // namespace kld

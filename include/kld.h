@@ -79,7 +79,8 @@ enum {
   KLD_OP_FROM_LOGITS = 0,
   KLD_OP_FUSED_HEAD = 1,
   KLD_OP_TOPK_EXPORT = 2,
-  KLD_OP_SUMMARY = 3
+  KLD_OP_SUMMARY = 3,
+  KLD_OP_COARSE_KL = 4
 };
 #define KLD_FLAG_TOPK 1       /* the call will also export top-64 lists */
 
@@ -241,18 +242,18 @@ kld_status kld_golden_export(const void *logits, int dtype, int64_t n, int64_t v
  * KL(p || q) = sum over the cells of p_i (ln p_i - ln q_i), with p_i =
  * exp(lp_i) and p_tail = rec[i][2] as stored.
  *
- * cand   : [n, v] candidate logits (dtype f32 or bf16 bits), ld >= v,
- *          512 <= v <= 2^20 (the listed ids live in an LDS bitmap of v bits).
+ * cand   : [n, v] candidate logits (dtype f32 or bf16 bits), ld >= v >= 512.
  * ids, lp, rec : the records as kld_golden_export writes them; ids distinct.
  * k      : must be KLD_GOLDEN_TOPK.
  * kl     : [n] f32 output.  A cell with p = 0 adds 0; p > 0 against q = 0
  *          gives +inf; a listed id outside [0, v) or a candidate row with a
  *          NaN or +inf logit gives NaN.
- * Needs no workspace.  Pointers need 4-byte alignment (cand: its element size).
+ * ws     : workspace of kld_workspace_size(KLD_OP_COARSE_KL, n, v, 0, 0) bytes.
+ * Pointers need 4-byte alignment (cand: its element size; ws: 16 bytes).
  */
 kld_status kld_coarse_kl(const void *cand, int dtype, int64_t n, int64_t v, int64_t ld,
                          const int32_t *ids, const float *lp, const float *rec, int k, float *kl,
-                         void *stream);
+                         void *ws, size_t ws_bytes, void *stream);
 
 /* Human-readable name of a status code (static string). */
 const char *kld_status_str(int status);

@@ -130,8 +130,11 @@ def test_golden_and_coarse_validation_fails_closed():
     assert lib.kld_golden_export(None, 0, 4, 1000, 1000, None, 512, 16, 16, 16, None) == 1
     assert lib.kld_golden_export(16, 0, 0, 1000, 1000, None, 512, None, None, None, None) == 0
     # kld_coarse_kl(cand, dtype, n, v, ld, ids, lp, rec, k, kl, stream)
-    assert lib.kld_coarse_kl(16, 9, 4, 1000, 1000, 16, 16, 16, 512, 16, None) == 3
-    assert lib.kld_coarse_kl(16, 1, 4, 1000, 1000, 16, 16, 16, 100, 16, None) == 2
-    assert lib.kld_coarse_kl(16, 1, 4, 1000, 1000, 16, None, 16, 512, 16, None) == 1
-    assert lib.kld_coarse_kl(16, 1, 4, (1 << 20) + 1, (1 << 20) + 1, 16, 16, 16, 512, 16, None) == 5
-    assert lib.kld_coarse_kl(16, 1, 0, 1000, 1000, None, None, None, 512, None, None) == 0
+    big = 1 << 30
+    assert lib.kld_coarse_kl(16, 9, 4, 1000, 1000, 16, 16, 16, 512, 16, 16, big, None) == 3
+    assert lib.kld_coarse_kl(16, 1, 4, 1000, 1000, 16, 16, 16, 100, 16, 16, big, None) == 2
+    assert lib.kld_coarse_kl(16, 1, 4, 1000, 1000, 16, None, 16, 512, 16, 16, big, None) == 1
+    assert lib.kld_coarse_kl(16, 1, 4, 1000, 1000, 16, 16, 16, 512, 16, None, 0, None) == 4
+    assert lib.kld_coarse_kl(16, 1, 4, 1000, 1000, 16, 16, 16, 512, 16, 16, 8, None) == 4
+    assert lib.kld_coarse_kl(16, 1, 0, 1000, 1000, None, None, None, 512, None, None, 0, None) == 0
+    assert kld.kld_workspace_size(4, 512, 248_320) > 0
