@@ -369,6 +369,40 @@ def coarse_kl_rows(ids, lp, rec, b: np.ndarray) -> np.ndarray:
                      for i in range(b.shape[0])])
 
 
+def window_summary(kl, offsets, score_from: int, thresholds=()) -> dict:
+    """Scored-window statistics over segments (windows or documents) of a
+    per-position score array.
+
+    Segment i covers positions offsets[i] .. offsets[i+1] - 1; its first
+    score_from positions are not scored ([QC] "Golden distributions": a
+    document of T tokens has T - 1 - score_from scored rows, row j predicting
+    token score_from + j + 1; [FS] "What these inputs measured": the
+    scored-window control with score_from 0 / 256 / 1024).  Per segment: the
+    sum and count of the scored values (its mean is sum / count); overall:
+    the mean over every scored position, weighted equally ([QC] "The score":
+    the mean over all positions, and the mean over a subset of them such as
+    the 256K-token traces), and for each threshold the exact count of scored
+    positions whose score exceeds it ([FS] "What is in here": percentiles and
+    exact exceedance counts)."""
+    kl = np.asarray(kl, dtype=np.float64)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    nseg = offsets.shape[0] - 1
+    seg_sum = np.zeros(nseg)
+    seg_count = np.zeros(nseg, np.int64)
+    seg_exceed = np.zeros((nseg, len(thresholds)), np.int64)
+    for i in range(nseg):
+        x = kl[offsets[i] + score_from: offsets[i + 1]] if offsets[i] + score_from < offsets[i + 1] \
+            else kl[0:0]
+        seg_sum[i] = float(np.sum(x))
+        seg_count[i] = x.shape[0]
+        for t, thr in enumerate(thresholds):
+            seg_exceed[i, t] = int(np.sum(x > thr))
+    total = int(seg_count.sum())
+    return {"seg_sum": seg_sum, "seg_count": seg_count, "seg_exceed": seg_exceed,
+            "mean": float(seg_sum.sum() / total) if total else float("nan"), "count": total,
+            "exceed": seg_exceed.sum(axis=0)}
+
+
 def percentile(x: np.ndarray, q: float) -> float:
     """O5 percentile by reading R2 (linear interpolation, type 7): sort
     ascending, h = q (N - 1), value = x_(floor h) + (h - floor h) *

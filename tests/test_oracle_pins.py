@@ -405,3 +405,36 @@ def test_coarse_score_edges():
     assert oracle.coarse_kl_row(ids, lp, tail, b) == math.inf
     b2 = np.array([0.0, 0.0, -np.inf])                                # q's tail cell empty
     assert oracle.coarse_kl_row(ids, lp, tail, b2) == math.inf
+
+
+# ---------------------------------------------------- scored windows
+
+def test_window_summary_hand_example():
+    # two windows of 5 and 3 positions, score_from 2: scored values are
+    # (0.3, 0.4, 0.5) and (0.8,): sums 1.2 and 0.8, mean 2.0 / 4 = 0.5,
+    # exceedances of 0.35: 2 + 1 = 3, of 0.8: 0 (strictly greater)
+    kl = [0.1, 0.2, 0.3, 0.4, 0.5, 0.6, 0.7, 0.8]
+    w = oracle.window_summary(kl, [0, 5, 8], 2, thresholds=(0.35, 0.8))
+    assert np.allclose(w["seg_sum"], [1.2, 0.8]) and list(w["seg_count"]) == [3, 1]
+    assert abs(w["mean"] - 0.5) < 1e-15 and w["count"] == 4
+    assert list(w["exceed"]) == [3, 0]
+
+
+def test_window_summary_reduces_to_plain_mean_and_brute_force():
+    g = np.random.default_rng(31)
+    kl = g.exponential(1e-3, 5000)
+    offs = np.concatenate([[0], np.sort(g.choice(np.arange(1, 5000), 12, replace=False)), [5000]])
+    w0 = oracle.window_summary(kl, offs, 0, thresholds=(1e-3,))
+    assert abs(w0["mean"] - oracle.summarize(kl)["mean_kl"]) < 1e-15
+    assert w0["exceed"][0] == int(np.sum(kl > 1e-3))
+    sf = 37
+    w = oracle.window_summary(kl, offs, sf, thresholds=(1e-3, 5e-3))
+    mask = np.zeros(5000, bool)
+    for i in range(len(offs) - 1):
+        mask[min(offs[i] + sf, offs[i + 1]):offs[i + 1]] = True
+    assert w["count"] == int(mask.sum())
+    assert abs(w["mean"] - kl[mask].mean()) < 1e-15
+    assert list(w["exceed"]) == [int(np.sum(kl[mask] > 1e-3)), int(np.sum(kl[mask] > 5e-3))]
+    # a segment shorter than score_from contributes nothing
+    w_short = oracle.window_summary(kl, [0, 10, 5000], 20)
+    assert w_short["seg_count"][0] == 0 and w_short["count"] == 4990 - 20
