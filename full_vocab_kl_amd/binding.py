@@ -14,7 +14,7 @@ import torch
 
 TOPK = 64
 KLD_F32, KLD_BF16 = 0, 1
-OP_FROM_LOGITS, OP_FUSED_HEAD, OP_TOPK_EXPORT, OP_SUMMARY, OP_COARSE_KL = 0, 1, 2, 3, 4
+OP_FROM_LOGITS, OP_FUSED_HEAD, OP_TOPK_EXPORT, OP_SUMMARY, OP_COARSE_KL, OP_WINDOWS = 0, 1, 2, 3, 4, 5
 FLAG_TOPK = 1
 N_SUMMARY_FIXED = 8
 
@@ -63,6 +63,7 @@ _SIGS = {
     "kld_summary": (_I, [_P, _P, _P, _P, _P, _I64, _P, _I, _P, _P, _SZ, _P]),
     "kld_golden_export": (_I, [_P, _I, _I64, _I64, _I64, _P, _I, _P, _P, _P, _P]),
     "kld_coarse_kl": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P, _I, _P, _P, _SZ, _P]),
+    "kld_window_summary": (_I, [_P, _I64, _P, _I64, _I64, _P, _I, _P, _P, _P, _P, _SZ, _P]),
     "kld_status_str": (ctypes.c_char_p, [_I]),
     "kld_abi_version": (_I, []),
 }
@@ -300,6 +301,25 @@ def kld_coarse_kl(cand: torch.Tensor, ids: torch.Tensor, lp: torch.Tensor, rec: 
                                GOLDEN_TOPK, _ptr(out), _ptr(ws), ws.numel(), _stream(stream))
     _check(code, "kld_coarse_kl")
     return out
+
+
+def kld_window_summary(kl: torch.Tensor, offsets: torch.Tensor, score_from: int = 0,
+                       thresholds=(), ws: torch.Tensor | None = None, stream=None) -> dict:
+    """Scored-window statistics: per-segment sums and counts past score_from,
+    the mean over every scored position and exact exceedance counts."""
+    n = kl.shape[0]
+    nseg = offsets.shape[0] - 1
+    dev = kl.device
+    seg_sum = torch.empty(max(nseg, 0), dtype=torch.float64, device=dev)
+    seg_count = torch.empty(max(nseg, 0), dtype=torch.int64, device=dev)
+    totals = torch.empty(2 + len(thresholds), dtype=torch.float64, device=dev)
+    th = (ctypes.c_float * max(len(thresholds), 1))(*thresholds)
+    ws, need = _workspace(OP_WINDOWS, 0, 0, 0, 0, dev, ws)
+    code = lib().kld_window_summary(_ptr(kl), n, _ptr(offsets), nseg, int(score_from), th,
+                                    len(thresholds), _ptr(seg_sum), _ptr(seg_count), _ptr(totals),
+                                    _ptr(ws), ws.numel(), _stream(stream))
+    _check(code, "kld_window_summary")
+    return {"seg_sum": seg_sum, "seg_count": seg_count, "totals": totals}
 
 
 def kld_summary(kl, argmax_ref=None, argmax_cand=None, nll_ref=None, nll_cand=None,

@@ -106,6 +106,15 @@ struct SummaryArgs {
 size_t summary_workspace_bytes(int64_t n);
 hipError_t launch_summary(const SummaryArgs &a, void *ws);
 
+// scored-window statistics (kld_window.hip)
+struct WindowThresholds {
+  float value[16];
+  int count;
+};
+hipError_t launch_window_summary(const float *kl, int64_t n, const int64_t *offsets, int64_t nseg,
+                                 int64_t score_from, const WindowThresholds &thr, double *seg_sum,
+                                 int64_t *seg_count, double *totals, void *ws, hipStream_t stream);
+
 // golden records and the 513-cell score (kld_golden.hip)
 hipError_t launch_golden_export(const void *logits, int dtype, int64_t n, int64_t v, int64_t ld,
                                 bool aligned, const int32_t *target, int32_t *ids, float *lp,

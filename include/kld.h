@@ -58,6 +58,7 @@ extern "C" {
 #define KLD_TOPK 64           /* the export width the quality-eval reference uses */
 #define KLD_GOLDEN_TOPK 512   /* ids listed per golden record (the challenge's references) */
 #define KLD_MAX_QUANTILES 16
+#define KLD_MAX_THRESHOLDS 16
 
 typedef enum kld_status {
   KLD_OK = 0,
@@ -80,7 +81,8 @@ enum {
   KLD_OP_FUSED_HEAD = 1,
   KLD_OP_TOPK_EXPORT = 2,
   KLD_OP_SUMMARY = 3,
-  KLD_OP_COARSE_KL = 4
+  KLD_OP_COARSE_KL = 4,
+  KLD_OP_WINDOWS = 5
 };
 #define KLD_FLAG_TOPK 1       /* the call will also export top-64 lists */
 
@@ -254,6 +256,37 @@ kld_status kld_golden_export(const void *logits, int dtype, int64_t n, int64_t v
 kld_status kld_coarse_kl(const void *cand, int dtype, int64_t n, int64_t v, int64_t ld,
                          const int32_t *ids, const float *lp, const float *rec, int k, float *kl,
                          void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * kld_window_summary -- scored-window statistics of a per-position score
+ * ("Qwen3.8-27B Quantization Challenge", "Golden distributions": the first
+ * score_from positions of a document are not scored; "The score": the mean
+ * over all positions and over a subset such as the long traces; "Qwen3.8-27B
+ * fidelity suite v5": exact exceedance counts and the score_from 0 / 256 /
+ * 1024 window control).
+ *
+ * kl         : [n] per-position scores (device).
+ * offsets    : [nseg + 1] int64 (device): segment i (a window or document)
+ *              covers positions offsets[i] .. offsets[i+1] - 1, nondecreasing
+ *              within [0, n].
+ * score_from : the first score_from positions of every segment are skipped.
+ * thresholds : HOST array of nthr <= KLD_MAX_THRESHOLDS values.
+ * seg_sum    : [nseg] f64 output, the sum of each segment's scored values
+ *              (its mean is seg_sum / seg_count; the mean over a subset of
+ *              segments is the sum of their sums over the sum of their counts).
+ * seg_count  : [nseg] int64 output, scored positions per segment.
+ * totals     : [2 + nthr] f64 output: [0] mean over every scored position
+ *              (each weighted equally), [1] their count, [2 + t] how many
+ *              exceed thresholds[t] (strictly).
+ * ws         : kld_workspace_size(KLD_OP_WINDOWS, 0, 0, 0, 0) bytes.
+ * A segment whose offsets break the rules gets seg_sum NaN and count 0, and
+ * totals[0] is NaN.  Sums are taken in a fixed order: results are bitwise
+ * reproducible.
+ */
+kld_status kld_window_summary(const float *kl, int64_t n, const int64_t *offsets, int64_t nseg,
+                              int64_t score_from, const float *thresholds, int nthr,
+                              double *seg_sum, int64_t *seg_count, double *totals, void *ws,
+                              size_t ws_bytes, void *stream);
 
 /* Human-readable name of a status code (static string). */
 const char *kld_status_str(int status);

@@ -28,6 +28,7 @@ HIDDEN = 5120
 WINDOW_POSITIONS = 2047
 
 STREAM_BASE, STREAM_NOISE, STREAM_BOOST, STREAM_TARGET, STREAM_HEAD, STREAM_SUBSET = range(6)
+STREAM_SCORES = 6
 HEAD_BLOCK = 2048
 HIDDEN_BLOCK = 256
 
@@ -173,3 +174,21 @@ def subset(workload: int, n: int, m: int) -> np.ndarray:
     """A seeded sorted subset of m distinct row indices out of n."""
     g = rng(workload, STREAM_SUBSET, 0)
     return np.sort(g.choice(n, size=min(m, n), replace=False)).astype(np.int64)
+
+
+def kl_scores(workload: int, n: int, median: float = 0.02, sigma: float = 1.6) -> np.ndarray:
+    """n seeded per-position scores (float32), lognormal with the given
+    median: mostly small values with a heavy upper tail, the shape of a
+    per-position KL stream; about one value in a thousand is exactly zero."""
+    g = rng(workload, STREAM_SCORES, 0)
+    x = (median * np.exp(sigma * g.standard_normal(n))).astype(np.float32)
+    x[g.random(n) < 1e-3] = 0.0
+    return x
+
+
+def doc_offsets(workload: int, lengths) -> np.ndarray:
+    """Segment offsets [len(lengths) + 1] (int64) for segments of the given
+    lengths laid end to end, in a seeded shuffled order."""
+    g = rng(workload, STREAM_SCORES, 1)
+    lens = np.asarray(lengths, np.int64)[g.permutation(len(lengths))]
+    return np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)

@@ -138,3 +138,21 @@ def test_golden_and_coarse_validation_fails_closed():
     assert lib.kld_coarse_kl(16, 1, 4, 1000, 1000, 16, 16, 16, 512, 16, 16, 8, None) == 4
     assert lib.kld_coarse_kl(16, 1, 0, 1000, 1000, None, None, None, 512, None, None, 0, None) == 0
     assert kld.kld_workspace_size(4, 512, 248_320) > 0
+
+
+def test_window_summary_validation_fails_closed():
+    lib = kld.lib()
+    thr = (ctypes.c_float * 17)(*range(17))
+    ws = 1 << 20
+    # kld_window_summary(kl, n, offsets, nseg, score_from, thr, nthr, seg_sum, seg_count,
+    #                    totals, ws, ws_bytes, stream)
+    assert lib.kld_window_summary(16, 10, 16, 2, 0, thr, 17, 16, 16, 16, 16, ws, None) == 2
+    assert lib.kld_window_summary(16, 10, 16, 2, -1, thr, 1, 16, 16, 16, 16, ws, None) == 1
+    assert lib.kld_window_summary(16, -1, 16, 2, 0, thr, 1, 16, 16, 16, 16, ws, None) == 1
+    assert lib.kld_window_summary(16, 10, None, 2, 0, thr, 1, 16, 16, 16, 16, ws, None) == 1
+    assert lib.kld_window_summary(16, 10, 16, 2, 0, None, 1, 16, 16, 16, 16, ws, None) == 1
+    assert lib.kld_window_summary(16, 10, 16, 2, 0, thr, 1, None, 16, 16, 16, ws, None) == 1
+    assert lib.kld_window_summary(None, 10, 16, 2, 0, thr, 1, 16, 16, 16, 16, ws, None) == 1
+    assert lib.kld_window_summary(16, 10, 16, 2, 0, thr, 1, 16, 16, 16, None, 0, None) == 4
+    assert lib.kld_window_summary(16, 10, 16, 2, 0, thr, 1, 16, 16, 16, 16, 8, None) == 4
+    assert kld.kld_workspace_size(5, 0, 0) >= 17 * 8
