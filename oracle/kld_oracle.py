@@ -41,14 +41,29 @@ Readings where the pages are silent (each also listed in the design notes):
       +inf, has KL = NaN.
 * R7  NLL of a target id outside [0, V) is NaN.
 * R8  argmax ignores NaN entries; a row of only NaN reports id 0.
-* R9  the golden record's tail mass is the mass of the ids outside the
+* R14 the golden record's tail mass is the mass of the ids outside the
       top-K, summed over those ids of the full row (equal to 1 - sum of the
       listed probabilities in exact arithmetic, but free of its
       cancellation when the tail is tiny).
-* R10 the 513-cell score takes p from the stored record (the f32 log-probs
+* R15 the 513-cell score takes p from the stored record (the f32 log-probs
       of the listed ids and the stored tail mass) and q from the candidate's
       full row: q of a listed id is its softmax probability, q's tail cell
       the candidate mass of every unlisted id.
+* R16 score_from skips the first score_from positions of every segment
+      (window or document); a segment shorter than that scores nothing; an
+      exceedance is a score strictly above the threshold.
+* R17 the paired difference of two candidates is position-weighted, mean(a)
+      - mean(b) over the scored positions of the contexts both were scored
+      on (with equal scored positions per context, as in the pages' shard,
+      this is also the mean of the per-context differences); a context is
+      won by the candidate with the strictly lower per-context mean.
+* R18 the source-cluster bootstrap resamples clusters: each replicate draws
+      as many cluster ids as there are clusters, uniformly with replacement,
+      and recomputes R17's statistic over the drawn clusters' contexts (a
+      cluster drawn twice counts twice); the interval is the percentile
+      interval of the replicates by R2 (2.5 % and 97.5 % for a 95 %
+      interval).  The draws are an input: the pages give neither the
+      generator nor the replicate count (10,000 is used here).
 
 Parity is pinned for every function here by the ``-m "not gpu"`` tests
 (tests/test_oracle_pins.py); no function is "parity unpinned".
@@ -299,7 +314,7 @@ def golden_row(x: np.ndarray, target=None, k: int = GOLDEN_TOPK):
 
     Ids follow O6 (ties to the lower id, reading R1); lp = x_j - lse(x) in f64,
     rounded once to f32; entropy = -sum_j p_j ln p_j over every id with
-    p_j > 0; tail = sum of p_j over the ids outside the top k (reading R9);
+    p_j > 0; tail = sum of p_j over the ids outside the top k (reading R14);
     nll per O4 (NaN without a target).  Returns (ids int32 [k], lp f32 [k],
     rec f32 [3] = (nll, entropy, tail))."""
     x = np.asarray(x, dtype=np.float64)
@@ -324,7 +339,7 @@ def coarse_kl_row(ids, lp, tail, b: np.ndarray) -> float:
     KL(p || q) = sum over the cells of p_i (ln p_i - ln q_i).
 
     p_i = exp(lp_i) for the listed ids and p_T = tail (the stored record,
-    reading R10); q_i = softmax(b)_i and q_T = the sum of softmax(b) over the
+    reading R15); q_i = softmax(b)_i and q_T = the sum of softmax(b) over the
     unlisted ids.  A cell with p = 0 adds 0; p > 0 against q = 0 gives +inf."""
     b = np.asarray(b, dtype=np.float64)
     ids = np.asarray(ids, dtype=np.int64)
@@ -374,7 +389,7 @@ def window_summary(kl, offsets, score_from: int, thresholds=()) -> dict:
     per-position score array.
 
     Segment i covers positions offsets[i] .. offsets[i+1] - 1; its first
-    score_from positions are not scored ([QC] "Golden distributions": a
+    score_from positions are not scored (reading R16; [QC] "Golden distributions": a
     document of T tokens has T - 1 - score_from scored rows, row j predicting
     token score_from + j + 1; [FS] "What these inputs measured": the
     scored-window control with score_from 0 / 256 / 1024).  Per segment: the
@@ -402,6 +417,62 @@ def window_summary(kl, offsets, score_from: int, thresholds=()) -> dict:
             "mean": float(seg_sum.sum() / total) if total else float("nan"), "count": total,
             "exceed": seg_exceed.sum(axis=0)}
 
+
+
+def paired_bootstrap(sum_a, sum_b, count, cluster, draws, quantiles=(0.025, 0.975)) -> dict:
+    """Paired per-context comparison of two candidates with a source-cluster
+    bootstrap interval ([FS] "Replay: score your own checkpoint against the
+    published BF16 reference": two reports compared per context give the
+    difference of their means, a 95 % bootstrap interval over source
+    clusters and how many contexts each side wins, with ties; "What these
+    inputs measured": bootstrap intervals over clusters).
+
+    Context c has sum_a[c] and sum_b[c], the sums of the two candidates'
+    per-position scores over its count[c] scored positions, and belongs to
+    source cluster cluster[c] in [0, K).  Reading R17: the difference is
+    sum_c (sum_a[c] - sum_b[c]) / sum_c count[c]; context c is won by a when
+    sum_a[c] / count[c] < sum_b[c] / count[c], by b when the reverse holds,
+    and tied when the two means are equal.  Reading R18: replicate r takes
+    the clusters draws[r, 0..K-1] (ids drawn with replacement) and computes
+    the same difference over the contexts of those clusters, each cluster
+    as often as it was drawn; the interval is percentile(replicates, q)
+    by R2 for each q.  Returns diff, a_wins, b_wins, ties, replicates and
+    the list of quantiles."""
+    sum_a = np.asarray(sum_a, dtype=np.float64)
+    sum_b = np.asarray(sum_b, dtype=np.float64)
+    count = np.asarray(count, dtype=np.int64)
+    cluster = np.asarray(cluster, dtype=np.int64)
+    draws = np.asarray(draws, dtype=np.int64)
+    nctx = sum_a.shape[0]
+    n_clusters = draws.shape[1] if draws.ndim == 2 else 0
+    total = int(count.sum())
+    diff = float(np.sum(sum_a - sum_b) / total) if total else float("nan")
+    mean_a = sum_a / np.where(count > 0, count, 1)
+    mean_b = sum_b / np.where(count > 0, count, 1)
+    scored = count > 0
+    a_wins = int(np.sum(scored & (mean_a < mean_b)))
+    b_wins = int(np.sum(scored & (mean_b < mean_a)))
+    ties = int(np.sum(scored & (mean_a == mean_b)))
+    # each cluster's summed difference and scored positions
+    clus_diff = np.zeros(n_clusters)
+    clus_count = np.zeros(n_clusters, np.int64)
+    for c in range(nctx):
+        clus_diff[cluster[c]] += sum_a[c] - sum_b[c]
+        clus_count[cluster[c]] += count[c]
+    reps = np.empty(draws.shape[0])
+    for r in range(draws.shape[0]):
+        num = 0.0
+        den = 0
+        for k in draws[r]:
+            num += clus_diff[k]
+            den += clus_count[k]
+        reps[r] = num / den if den else float("nan")
+    if reps.shape[0] and not np.isnan(reps).any():
+        qs = [percentile(reps, q) for q in quantiles]
+    else:
+        qs = [float("nan")] * len(quantiles)
+    return {"diff": diff, "a_wins": a_wins, "b_wins": b_wins, "ties": ties,
+            "replicates": reps, "quantiles": qs}
 
 def percentile(x: np.ndarray, q: float) -> float:
     """O5 percentile by reading R2 (linear interpolation, type 7): sort

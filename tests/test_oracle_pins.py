@@ -438,3 +438,84 @@ def test_window_summary_reduces_to_plain_mean_and_brute_force():
     # a segment shorter than score_from contributes nothing
     w_short = oracle.window_summary(kl, [0, 10, 5000], 20)
     assert w_short["seg_count"][0] == 0 and w_short["count"] == 4990 - 20
+
+
+# ---------------------------------------------------- paired bootstrap
+
+def test_paired_bootstrap_hand_example():
+    ex = _gold("paired_bootstrap_example.json")
+    r = oracle.paired_bootstrap(ex["sum_a"], ex["sum_b"], ex["count"], ex["cluster"], ex["draws"],
+                                ex["quantiles"])
+    assert abs(r["diff"] - float(ex["expected_diff"])) < 1e-16
+    assert (r["a_wins"], r["b_wins"], r["ties"]) == (ex["expected_a_wins"], ex["expected_b_wins"],
+                                                     ex["expected_ties"])
+    assert np.allclose(r["replicates"], [float(x) for x in ex["expected_replicates"]], rtol=1e-15,
+                       atol=0)
+    assert np.allclose(r["quantiles"], [float(x) for x in ex["expected_quantiles"]], rtol=1e-15,
+                       atol=0)
+
+
+def _paired_inputs(seed, nctx, k, equal_counts=True):
+    g = np.random.default_rng(seed)
+    count = np.full(nctx, 2047) if equal_counts else g.integers(0, 3000, nctx)
+    sum_a = g.integers(0, 10 ** 6, nctx).astype(np.float64)       # integer sums: exact in f64
+    sum_b = sum_a + g.integers(-5000, 5000, nctx)
+    cluster = np.concatenate([np.arange(k), g.integers(0, k, nctx - k)])
+    g.shuffle(cluster)
+    return sum_a, sum_b, count, cluster
+
+
+def test_paired_bootstrap_brute_force_over_every_draw():
+    # K = 3 clusters, all 27 draw sequences: each replicate recomputed by
+    # expanding the drawn clusters into their contexts, in exact rationals
+    from fractions import Fraction
+    sum_a, sum_b, count, cluster = _paired_inputs(41, 7, 3, equal_counts=False)
+    draws = np.array(list(itertools.product(range(3), repeat=3)))
+    r = oracle.paired_bootstrap(sum_a, sum_b, count, cluster, draws, (0.5,))
+    for d, got in zip(draws, r["replicates"]):
+        ctx = [c for k in d for c in range(7) if cluster[c] == k]
+        num = sum(Fraction(int(sum_a[c]) - int(sum_b[c])) for c in ctx)
+        den = sum(int(count[c]) for c in ctx)
+        assert got == float(num / den)
+    assert r["quantiles"][0] == np.percentile(r["replicates"], 50.0)
+    # the point estimate over all contexts, and the win counts by brute force
+    assert r["diff"] == float(Fraction(int(np.sum(sum_a - sum_b)), int(np.sum(count))))
+    ma, mb = sum_a / np.maximum(count, 1), sum_b / np.maximum(count, 1)
+    wins = [0, 0, 0]
+    for c in range(7):
+        if count[c]:
+            wins[0 if ma[c] < mb[c] else 1 if mb[c] < ma[c] else 2] += 1
+    assert [r["a_wins"], r["b_wins"], r["ties"]] == wins
+
+
+def test_paired_bootstrap_invariants():
+    sum_a, sum_b, count, cluster = _paired_inputs(42, 512, 330)
+    g = np.random.default_rng(43)
+    draws = np.vstack([np.arange(330), g.integers(0, 330, (999, 330))])
+    r = oracle.paired_bootstrap(sum_a, sum_b, count, cluster, draws, (0.025, 0.5, 0.975))
+    # every cluster drawn once reproduces the point estimate (integer inputs: exact)
+    assert r["replicates"][0] == r["diff"]
+    # equal counts per context: the position-weighted difference is the
+    # mean of the per-context differences
+    assert abs(r["diff"] - np.mean(sum_a / 2047 - sum_b / 2047)) < 1e-12
+    # percentile interval: numpy's type-7 percentiles of the replicates
+    for q, v in zip((0.025, 0.5, 0.975), r["quantiles"]):
+        assert v == np.percentile(r["replicates"], 100 * q)
+    # swapping the candidates negates the difference, the replicates and the interval
+    s = oracle.paired_bootstrap(sum_b, sum_a, count, cluster, draws, (0.025, 0.975))
+    assert s["diff"] == -r["diff"] and np.array_equal(s["replicates"], -r["replicates"])
+    assert (s["a_wins"], s["b_wins"], s["ties"]) == (r["b_wins"], r["a_wins"], r["ties"])
+    assert abs(s["quantiles"][0] + r["quantiles"][2]) <= 1e-12 * abs(r["quantiles"][2])
+    assert r["a_wins"] + r["b_wins"] + r["ties"] == 512
+    # an interval of a real bootstrap brackets the point estimate here
+    assert r["quantiles"][0] < r["diff"] < r["quantiles"][2]
+
+
+def test_paired_bootstrap_edges():
+    # no scored position: NaN difference and NaN replicates
+    r = oracle.paired_bootstrap([0.0, 0.0], [0.0, 0.0], [0, 0], [0, 1], [[0, 1]], (0.5,))
+    assert math.isnan(r["diff"]) and math.isnan(r["quantiles"][0])
+    assert (r["a_wins"], r["b_wins"], r["ties"]) == (0, 0, 0)
+    # identical candidates: zero difference, every context tied
+    r = oracle.paired_bootstrap([1.0, 2.0], [1.0, 2.0], [3, 4], [0, 1], [[0, 1], [1, 1]], (0.5,))
+    assert r["diff"] == 0.0 and r["ties"] == 2 and r["quantiles"][0] == 0.0
