@@ -14,7 +14,8 @@ import torch
 
 TOPK = 64
 KLD_F32, KLD_BF16 = 0, 1
-OP_FROM_LOGITS, OP_FUSED_HEAD, OP_TOPK_EXPORT, OP_SUMMARY, OP_COARSE_KL, OP_WINDOWS = 0, 1, 2, 3, 4, 5
+(OP_FROM_LOGITS, OP_FUSED_HEAD, OP_TOPK_EXPORT, OP_SUMMARY, OP_COARSE_KL, OP_WINDOWS,
+ OP_PAIRED) = range(7)
 FLAG_TOPK = 1
 N_SUMMARY_FIXED = 8
 
@@ -64,6 +65,8 @@ _SIGS = {
     "kld_golden_export": (_I, [_P, _I, _I64, _I64, _I64, _P, _I, _P, _P, _P, _P]),
     "kld_coarse_kl": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P, _I, _P, _P, _SZ, _P]),
     "kld_window_summary": (_I, [_P, _I64, _P, _I64, _I64, _P, _I, _P, _P, _P, _P, _SZ, _P]),
+    "kld_paired_bootstrap": (_I, [_P, _P, _P, _I64, _P, _I64, _P, _I64, _P, _I, _P, _P, _P, _SZ,
+                                  _P]),
     "kld_status_str": (ctypes.c_char_p, [_I]),
     "kld_abi_version": (_I, []),
 }
@@ -320,6 +323,28 @@ def kld_window_summary(kl: torch.Tensor, offsets: torch.Tensor, score_from: int 
                                     _ptr(ws), ws.numel(), _stream(stream))
     _check(code, "kld_window_summary")
     return {"seg_sum": seg_sum, "seg_count": seg_count, "totals": totals}
+
+
+def kld_paired_bootstrap(sum_a: torch.Tensor, sum_b: torch.Tensor, count: torch.Tensor,
+                         cluster: torch.Tensor, draws: torch.Tensor,
+                         quantiles=(0.025, 0.975), ws: torch.Tensor | None = None,
+                         stream=None) -> dict:
+    """Paired per-context comparison of two candidates with a source-cluster
+    bootstrap: the position-weighted difference, contexts won and tied, the
+    replicates and their percentiles."""
+    nctx = sum_a.shape[0]
+    nrep, nclust = draws.shape
+    dev = sum_a.device
+    reps = torch.empty(nrep, dtype=torch.float64, device=dev)
+    out = torch.empty(4 + len(quantiles), dtype=torch.float64, device=dev)
+    qs = (ctypes.c_double * max(len(quantiles), 1))(*quantiles)
+    ws, need = _workspace(OP_PAIRED, nclust, 0, 0, 0, dev, ws)
+    code = lib().kld_paired_bootstrap(_ptr(sum_a), _ptr(sum_b), _ptr(count), nctx, _ptr(cluster),
+                                      nclust, _ptr(draws), nrep, qs, len(quantiles), _ptr(reps),
+                                      _ptr(out), _ptr(ws), ws.numel(), _stream(stream))
+    _check(code, "kld_paired_bootstrap")
+    return {"diff": out[0], "a_wins": out[1], "b_wins": out[2], "ties": out[3],
+            "quantiles": out[4:], "replicates": reps, "out": out}
 
 
 def kld_summary(kl, argmax_ref=None, argmax_cand=None, nll_ref=None, nll_cand=None,

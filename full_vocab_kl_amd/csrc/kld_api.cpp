@@ -131,6 +131,7 @@ size_t kld_workspace_size(int op, int64_t n, int64_t v, int64_t d, int flags) {
     case KLD_OP_FUSED_HEAD: return fused_workspace(n, v, flags, &c);
     case KLD_OP_SUMMARY: return round_up(summary_workspace_bytes(n), kAlign);
     case KLD_OP_WINDOWS: return round_up((KLD_MAX_THRESHOLDS + 1) * sizeof(unsigned long long), kAlign);
+    case KLD_OP_PAIRED: return round_up(paired_workspace_bytes(n), kAlign);
     case KLD_OP_COARSE_KL: {
       if (n == 0 || v == 0) return 0;
       const CoarseGeom g = coarse_geom(n, v);
@@ -274,6 +275,33 @@ kld_status kld_coarse_kl(const void *cand, int dtype, int64_t n, int64_t v, int6
   const bool aligned = aligned16(cand) && (ld * esize) % 16 == 0;
   if (launch_coarse_kl(cand, dtype, n, v, ld, aligned, ids, lp, rec, kl, ws, as_stream(stream)) !=
       hipSuccess)
+    return KLD_EHIP;
+  return KLD_OK;
+}
+
+kld_status kld_paired_bootstrap(const double *sum_a, const double *sum_b, const int64_t *count,
+                                int64_t nctx, const int32_t *cluster, int64_t nclust,
+                                const int32_t *draws, int64_t nrep, const double *quantiles,
+                                int nq, double *replicates, double *out, void *ws,
+                                size_t ws_bytes, void *stream) {
+  if (nctx < 0 || nclust < 0 || nrep < 0 || nq < 0) return KLD_EINVAL;
+  if (nq > KLD_MAX_QUANTILES || nrep > KLD_MAX_REPLICATES || nclust > (1LL << 30))
+    return KLD_ESHAPE;
+  if (nrep > 0 && nclust == 0) return KLD_ESHAPE;
+  if (!out || (nctx > 0 && (!sum_a || !sum_b || !count || !cluster)) ||
+      (nrep > 0 && (!draws || !replicates)) || (nq > 0 && !quantiles))
+    return KLD_EINVAL;
+  PairedQuantiles qs;
+  qs.count = nq;
+  for (int i = 0; i < KLD_MAX_QUANTILES; ++i) {
+    const double q = i < nq ? quantiles[i] : 0.0;
+    if (!(q >= 0.0 && q <= 1.0)) return KLD_EINVAL;
+    qs.q[i] = q;
+  }
+  if (nclust > 0 && (!ws || ws_bytes < kld_workspace_size(KLD_OP_PAIRED, nclust, 0, 0, 0)))
+    return KLD_EWORKSPACE;
+  if (launch_paired_bootstrap(sum_a, sum_b, count, nctx, cluster, nclust, draws, nrep, qs,
+                              replicates, out, ws, as_stream(stream)) != hipSuccess)
     return KLD_EHIP;
   return KLD_OK;
 }

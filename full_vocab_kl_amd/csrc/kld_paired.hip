@@ -1,0 +1,203 @@
+// Paired per-context comparison of two candidates with a source-cluster
+// bootstrap interval ("Qwen3.8-27B fidelity suite v5": "Replay: score your
+// own checkpoint against the published BF16 reference" -- the difference of
+// two reports' means paired per context, a 95 % bootstrap interval over
+// source clusters and the contexts each side wins or ties; "What these inputs
+// measured" -- bootstrap intervals over clusters).
+//
+// The difference is position-weighted: sum_c (sum_a - sum_b) / sum_c count.
+// A bootstrap replicate draws as many clusters as there are, with
+// replacement (the draws are an input), and recomputes that difference over
+// the drawn clusters' contexts; the interval is the type-7 percentile of the
+// replicates (linear interpolation, h = q (n - 1)).
+//
+//   paired_cluster_kernel   one block per cluster: its summed difference and
+//                           scored positions; one extra block: the overall
+//                           difference, wins, ties and a label check
+//   paired_replicate_kernel one wave per replicate: gather-sum over its draws
+//   paired_quantile_kernel  one block: bitonic sort of the replicates in LDS
+//                           and the interpolated percentiles
+// Every sum runs in a fixed order, so results are bitwise reproducible.
+#include "kld.h"
+#include "kld_device.hpp"
+#include "kld_launch.hpp"
+
+namespace kld {
+
+namespace {
+
+constexpr int PT = 256;
+
+template <typename T>
+__device__ __forceinline__ T block_sum(T x, T *red) {
+  red[threadIdx.x] = x;
+  __syncthreads();
+  for (int h = PT / 2; h > 0; h >>= 1) {
+    if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+    __syncthreads();
+  }
+  const T r = red[0];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(PT) void paired_cluster_kernel(
+    const double *__restrict__ sum_a, const double *__restrict__ sum_b,
+    const int64_t *__restrict__ count, int64_t nctx, const int32_t *__restrict__ cluster,
+    int64_t nclust, double *__restrict__ clus_diff, int64_t *__restrict__ clus_count,
+    double *__restrict__ out) {
+  __shared__ double rd[PT];
+  __shared__ long long ri[PT];
+  const int64_t k = blockIdx.x;
+  if (k < nclust) {
+    double d = 0.0;
+    long long c = 0;
+    for (int64_t i = threadIdx.x; i < nctx; i += PT) {
+      if (cluster[i] == k) {
+        d += sum_a[i] - sum_b[i];
+        c += count[i];
+      }
+    }
+    d = block_sum(d, rd);
+    c = block_sum(c, ri);
+    if (threadIdx.x == 0) {
+      clus_diff[k] = d;
+      clus_count[k] = c;
+    }
+    return;
+  }
+  // the overall difference, wins and ties, and a check of the labels
+  double d = 0.0;
+  long long c = 0, wa = 0, wb = 0, ti = 0, bad = 0;
+  for (int64_t i = threadIdx.x; i < nctx; i += PT) {
+    const double a = sum_a[i], b = sum_b[i];
+    const int64_t n = count[i];
+    d += a - b;
+    c += n;
+    bad += (cluster[i] < 0 || cluster[i] >= nclust || n < 0) ? 1 : 0;
+    if (n > 0) {
+      const double ma = a / (double)n, mb = b / (double)n;
+      wa += ma < mb;
+      wb += mb < ma;
+      ti += ma == mb;
+    }
+  }
+  d = block_sum(d, rd);
+  c = block_sum(c, ri);
+  wa = block_sum(wa, ri);
+  wb = block_sum(wb, ri);
+  ti = block_sum(ti, ri);
+  bad = block_sum(bad, ri);
+  if (threadIdx.x == 0) {
+    out[0] = (bad || c == 0) ? __builtin_nan("") : d / (double)c;
+    out[1] = (double)wa;
+    out[2] = (double)wb;
+    out[3] = (double)ti;
+  }
+}
+
+constexpr int RW = 4;   // waves (replicates) per block
+
+__global__ __launch_bounds__(RW * 64) void paired_replicate_kernel(
+    const double *__restrict__ clus_diff, const int64_t *__restrict__ clus_count, int64_t nclust,
+    const int32_t *__restrict__ draws, int64_t nrep, double *__restrict__ reps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * RW + (threadIdx.x >> 6);
+  if (r >= nrep) return;
+  const int32_t *dr = draws + r * nclust;
+  double num = 0.0;
+  long long den = 0;
+  int bad = 0;
+  for (int64_t i = lane; i < nclust; i += 64) {
+    const int32_t k = dr[i];
+    if (k < 0 || k >= nclust) {
+      bad = 1;
+    } else {
+      num += clus_diff[k];
+      den += clus_count[k];
+    }
+  }
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) {
+    num += __shfl_xor(num, m);
+    den += __shfl_xor(den, m);
+    bad |= __shfl_xor(bad, m);
+  }
+  if (lane == 0) reps[r] = (bad || den == 0) ? __builtin_nan("") : num / (double)den;
+}
+
+constexpr int QT = 1024;
+
+__global__ __launch_bounds__(QT) void paired_quantile_kernel(const double *__restrict__ reps,
+                                                             int64_t nrep, PairedQuantiles qs,
+                                                             double *__restrict__ out) {
+  __shared__ double x[KLD_MAX_REPLICATES];
+  __shared__ int any_nan;
+  int m = 1;
+  while (m < nrep) m <<= 1;
+  if (threadIdx.x == 0) any_nan = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < m; i += QT) {
+    double v = i < nrep ? reps[i] : __builtin_inf();
+    if (v != v) {
+      any_nan = 1;
+      v = __builtin_inf();
+    }
+    x[i] = v;
+  }
+  __syncthreads();
+  // bitonic sort, ascending
+  for (int size = 2; size <= m; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int t = threadIdx.x; t < (m >> 1); t += QT) {
+        const int i = 2 * t - (t & (stride - 1));
+        const int j = i + stride;
+        const bool up = (i & size) == 0;
+        const double a = x[i], b = x[j];
+        if ((a > b) == up) {
+          x[i] = b;
+          x[j] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if ((int)threadIdx.x < qs.count) {
+    double v = __builtin_nan("");
+    if (nrep > 0 && !any_nan) {
+      const double h = qs.q[threadIdx.x] * (double)(nrep - 1);
+      const int64_t lo = (int64_t)floor(h);
+      const int64_t hi = lo + 1 < nrep ? lo + 1 : nrep - 1;
+      v = x[lo] + (h - (double)lo) * (x[hi] - x[lo]);
+    }
+    out[4 + threadIdx.x] = v;
+  }
+}
+
+}  // namespace
+
+size_t paired_workspace_bytes(int64_t nclust) {
+  return (size_t)(nclust > 0 ? nclust : 0) * (sizeof(double) + sizeof(int64_t));
+}
+
+hipError_t launch_paired_bootstrap(const double *sum_a, const double *sum_b, const int64_t *count,
+                                   int64_t nctx, const int32_t *cluster, int64_t nclust,
+                                   const int32_t *draws, int64_t nrep, const PairedQuantiles &qs,
+                                   double *reps, double *out, void *ws, hipStream_t stream) {
+  double *clus_diff = static_cast<double *>(ws);
+  int64_t *clus_count = reinterpret_cast<int64_t *>(clus_diff + nclust);
+  hipLaunchKernelGGL(paired_cluster_kernel, dim3((unsigned)(nclust + 1)), dim3(PT), 0, stream,
+                     sum_a, sum_b, count, nctx, cluster, nclust, clus_diff, clus_count, out);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (nrep > 0) {
+    hipLaunchKernelGGL(paired_replicate_kernel, dim3((unsigned)((nrep + RW - 1) / RW)),
+                       dim3(RW * 64), 0, stream, clus_diff, clus_count, nclust, draws, nrep, reps);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(paired_quantile_kernel, dim3(1), dim3(QT), 0, stream, reps, nrep, qs, out);
+  return hipGetLastError();
+}
+
+}  // namespace kld

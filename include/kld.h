@@ -59,6 +59,7 @@ extern "C" {
 #define KLD_GOLDEN_TOPK 512   /* ids listed per golden record (the challenge's references) */
 #define KLD_MAX_QUANTILES 16
 #define KLD_MAX_THRESHOLDS 16
+#define KLD_MAX_REPLICATES 16384
 
 typedef enum kld_status {
   KLD_OK = 0,
@@ -82,7 +83,8 @@ enum {
   KLD_OP_TOPK_EXPORT = 2,
   KLD_OP_SUMMARY = 3,
   KLD_OP_COARSE_KL = 4,
-  KLD_OP_WINDOWS = 5
+  KLD_OP_WINDOWS = 5,
+  KLD_OP_PAIRED = 6
 };
 #define KLD_FLAG_TOPK 1       /* the call will also export top-64 lists */
 
@@ -287,6 +289,45 @@ kld_status kld_window_summary(const float *kl, int64_t n, const int64_t *offsets
                               int64_t score_from, const float *thresholds, int nthr,
                               double *seg_sum, int64_t *seg_count, double *totals, void *ws,
                               size_t ws_bytes, void *stream);
+
+/*
+ * kld_paired_bootstrap -- paired per-context comparison of two candidates
+ * with a source-cluster bootstrap interval ("Qwen3.8-27B fidelity suite v5",
+ * "Replay: score your own checkpoint against the published BF16 reference":
+ * the difference of two reports' means paired per context, a 95 % interval
+ * from a bootstrap over source clusters, the contexts each side wins and
+ * the ties; "What these inputs measured": intervals over clusters).
+ *
+ * sum_a, sum_b : [nctx] f64 (device): per-context sums of the two
+ *                candidates' per-position scores (seg_sum of
+ *                kld_window_summary on each candidate's scores).
+ * count        : [nctx] int64 (device): scored positions per context.
+ * cluster      : [nctx] int32 (device): source cluster of each context,
+ *                in [0, nclust).
+ * draws        : [nrep, nclust] int32 (device), row-major: replicate r uses
+ *                the clusters draws[r][0..nclust-1], drawn by the caller
+ *                uniformly with replacement.
+ * quantiles    : HOST array of nq <= KLD_MAX_QUANTILES levels in [0, 1]
+ *                (0.025 and 0.975 give a 95 % interval).
+ * replicates   : [nrep] f64 output (device), nrep <= KLD_MAX_REPLICATES:
+ *                sum over the drawn clusters of (sum_a - sum_b) over the
+ *                sum of their counts.
+ * out          : [4 + nq] f64 output (device): [0] the difference
+ *                sum_c (sum_a - sum_b) / sum_c count, [1] contexts where
+ *                a's mean is lower, [2] where b's is lower, [3] ties
+ *                (contexts with count 0 are in none), [4 + i] the type-7
+ *                percentile of the replicates at quantiles[i].
+ * ws           : kld_workspace_size(KLD_OP_PAIRED, nclust, 0, 0, 0) bytes.
+ * A cluster label outside [0, nclust) or a negative count makes out[0] NaN;
+ * a draw outside it makes that replicate NaN; any NaN replicate (or none)
+ * makes every percentile NaN.  Sums run in a fixed order: results are
+ * bitwise reproducible.
+ */
+kld_status kld_paired_bootstrap(const double *sum_a, const double *sum_b, const int64_t *count,
+                                int64_t nctx, const int32_t *cluster, int64_t nclust,
+                                const int32_t *draws, int64_t nrep, const double *quantiles,
+                                int nq, double *replicates, double *out, void *ws,
+                                size_t ws_bytes, void *stream);
 
 /* Human-readable name of a status code (static string). */
 const char *kld_status_str(int status);

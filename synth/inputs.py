@@ -192,3 +192,28 @@ def doc_offsets(workload: int, lengths) -> np.ndarray:
     g = rng(workload, STREAM_SCORES, 1)
     lens = np.asarray(lengths, np.int64)[g.permutation(len(lengths))]
     return np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+
+
+def kl_score_pair(workload: int, n: int, spread: float = 0.1) -> tuple:
+    """Two candidates' per-position scores over the same n positions: the
+    first as kl_scores, the second the first times exp(spread * N(0, 1))
+    (two close candidates, paired by position)."""
+    a = kl_scores(workload, n)
+    g = rng(workload, STREAM_SCORES, 2)
+    b = (a * np.exp(spread * g.standard_normal(n))).astype(np.float32)
+    return a, b
+
+
+def cluster_labels(workload: int, nctx: int, nclust: int) -> np.ndarray:
+    """Source-cluster label (int32) of each of nctx contexts: every one of the
+    nclust clusters holds at least one context, the rest are uniform."""
+    g = rng(workload, STREAM_SCORES, 3)
+    lab = np.concatenate([np.arange(nclust), g.integers(0, nclust, max(nctx - nclust, 0))])
+    return g.permutation(lab)[:nctx].astype(np.int32)
+
+
+def bootstrap_draws(workload: int, nrep: int, nclust: int) -> np.ndarray:
+    """Bootstrap draws [nrep, nclust] (int32): each row nclust cluster ids
+    drawn uniformly with replacement."""
+    g = rng(workload, STREAM_SCORES, 4)
+    return g.integers(0, nclust, (nrep, nclust)).astype(np.int32)

@@ -156,3 +156,29 @@ def test_window_summary_validation_fails_closed():
     assert lib.kld_window_summary(16, 10, 16, 2, 0, thr, 1, 16, 16, 16, None, 0, None) == 4
     assert lib.kld_window_summary(16, 10, 16, 2, 0, thr, 1, 16, 16, 16, 16, 8, None) == 4
     assert kld.kld_workspace_size(5, 0, 0) >= 17 * 8
+
+
+def test_paired_bootstrap_validation_fails_closed():
+    lib = kld.lib()
+    q = (ctypes.c_double * 17)(*([0.5] * 17))
+    bad_q = (ctypes.c_double * 1)(1.5)
+    ws = 1 << 20
+    # kld_paired_bootstrap(sum_a, sum_b, count, nctx, cluster, nclust, draws, nrep, q, nq,
+    #                      replicates, out, ws, ws_bytes, stream)
+    assert lib.kld_paired_bootstrap(16, 16, 16, 8, 16, 3, 16, 10, q, 17, 16, 16, 16, ws, None) == 2
+    assert lib.kld_paired_bootstrap(16, 16, 16, 8, 16, 3, 16, 16385, q, 2, 16, 16, 16, ws,
+                                    None) == 2
+    assert lib.kld_paired_bootstrap(16, 16, 16, 8, 16, 0, 16, 10, q, 2, 16, 16, 16, ws, None) == 2
+    assert lib.kld_paired_bootstrap(16, 16, 16, -1, 16, 3, 16, 10, q, 2, 16, 16, 16, ws, None) == 1
+    assert lib.kld_paired_bootstrap(16, 16, 16, 8, 16, 3, 16, 10, bad_q, 1, 16, 16, 16, ws,
+                                    None) == 1
+    assert lib.kld_paired_bootstrap(16, None, 16, 8, 16, 3, 16, 10, q, 2, 16, 16, 16, ws,
+                                    None) == 1
+    assert lib.kld_paired_bootstrap(16, 16, 16, 8, 16, 3, None, 10, q, 2, 16, 16, 16, ws,
+                                    None) == 1
+    assert lib.kld_paired_bootstrap(16, 16, 16, 8, 16, 3, 16, 10, q, 2, 16, None, 16, ws,
+                                    None) == 1
+    assert lib.kld_paired_bootstrap(16, 16, 16, 8, 16, 3, 16, 10, q, 2, 16, 16, None, 0,
+                                    None) == 4
+    assert lib.kld_paired_bootstrap(16, 16, 16, 8, 16, 3, 16, 10, q, 2, 16, 16, 16, 8, None) == 4
+    assert kld.kld_workspace_size(6, 842, 0) >= 842 * 16
