@@ -38,7 +38,8 @@ def _args():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="fused_window",
-                   choices=["fused_window", "logits_f32", "logits_bf16_topk", "golden_f32"])
+                   choices=["fused_window", "logits_f32", "logits_bf16_topk", "golden_f32",
+                            "windows_paired"])
     p.add_argument("--cpu-sample", type=int, default=None,
                    help="positions the CPU oracle scores for the baseline (0 = skip)")
     p.add_argument("--no-secondary", action="store_true",
@@ -394,6 +395,101 @@ def golden_f32(steps, warmup, cpu_sample):
     return res
 
 
+
+def windows_paired(steps, warmup, cpu_sample):
+    """The ten-shard ladder's aggregation: 10,480,640 scored positions as
+    5,120 contexts of 2,047 positions in 842 source clusters.  One step is
+    kld_window_summary over each of two candidates' per-position scores
+    (per-context sums and counts, overall mean, exceedance counts against
+    seven thresholds) and kld_paired_bootstrap (the paired difference, wins
+    and ties, 10,000 cluster-bootstrap replicates and their 2.5 / 50 / 97.5 %
+    percentiles)."""
+    import numpy as np
+    import torch
+
+    import full_vocab_kl_amd as kld
+    import synth
+
+    nctx, per, nclust, nrep = 5120, 2047, 842, 10_000
+    n = nctx * per
+    thr = (0.0, 0.01, 0.1, 0.5, 1.0, 2.0, 5.0)
+    qs = (0.025, 0.5, 0.975)
+    a_np, b_np = synth.kl_score_pair(synth.LOGITS_F32, n)
+    lab_np = synth.cluster_labels(synth.LOGITS_F32, nctx, nclust)
+    dr_np = synth.bootstrap_draws(synth.LOGITS_F32, nrep, nclust)
+    off_np = np.arange(0, n + 1, per, dtype=np.int64)
+    dev = torch.device("cuda:0")
+    a, b = torch.from_numpy(a_np).to(dev), torch.from_numpy(b_np).to(dev)
+    off, lab, dr = (torch.from_numpy(x).to(dev) for x in (off_np, lab_np, dr_np))
+    def wout():
+        return {"seg_sum": torch.empty(nctx, dtype=torch.float64, device=dev),
+                "seg_count": torch.empty(nctx, dtype=torch.int64, device=dev),
+                "seg_exceed": torch.empty((nctx, len(thr)), dtype=torch.int64, device=dev),
+                "totals": torch.empty(2 + len(thr), dtype=torch.float64, device=dev)}
+    wa, wb = wout(), wout()
+    ws_p = torch.empty(kld.kld_workspace_size(5, nclust, nrep), dtype=torch.uint8, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * steps)]
+    res_box = {}
+
+    def step(i=None):
+        if i is not None:
+            ev[3 * i].record()
+        kld.kld_window_summary(a, off, 0, thr, out=wa)
+        kld.kld_window_summary(b, off, 0, thr, out=wb)
+        if i is not None:
+            ev[3 * i + 1].record()
+        res_box["p"] = kld.kld_paired_bootstrap(wa["seg_sum"], wb["seg_sum"], wa["seg_count"], lab,
+                                                dr, qs, ws=ws_p)
+        if i is not None:
+            ev[3 * i + 2].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    w_ms = sum(ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(steps)) / steps
+    p_ms = sum(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(steps)) / steps
+    nbytes = 2 * (4.0 * n + 8.0 * (nctx + 1) + (16.0 + 8.0 * len(thr)) * nctx)
+    achieved = nbytes / (w_ms * 1e-3) / 1e9
+    out = res_box["p"]["out"].cpu().numpy()
+    res = {
+        "value": n * steps / elapsed, "unit": "positions/s", "ms_per_step": elapsed * 1e3 / steps,
+        "dtype": "f64",
+        "config": {"workload": "kld_window_summary x 2 + kld_paired_bootstrap: 10,480,640 scored "
+                               "positions = 5,120 contexts x 2,047, 842 clusters, 10,000 replicates",
+                   "positions": n, "contexts": nctx, "clusters": nclust, "replicates": nrep},
+        "roofline": {"bound": "hbm", "kernel": "window_seg_kernel (two candidates)",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel_ms": round(w_ms, 4),
+                     "algorithmic": "2 x (4 B per position + 8 B per offset + 16 B + 8 B per "
+                                    f"threshold per context of output) = {nbytes:.4e} bytes"},
+        "paired_ms": round(p_ms, 4),
+        "result": {"diff": float(out[0]), "a_wins": int(out[1]), "b_wins": int(out[2]),
+                   "interval_95": [float(out[4]), float(out[6])]},
+    }
+    if cpu_sample:
+        import oracle
+        sub = min(cpu_sample, nrep)
+        t0 = time.perf_counter()
+        oa = oracle.window_summary(a_np, off_np, 0, thr)
+        ob = oracle.window_summary(b_np, off_np, 0, thr)
+        t1 = time.perf_counter()
+        oracle.paired_bootstrap(oa["seg_sum"], ob["seg_sum"], oa["seg_count"], lab_np,
+                                dr_np[:sub], qs)
+        t2 = time.perf_counter()
+        per_step = (t1 - t0) + (t2 - t1) * nrep / sub
+        res["cpu_baseline"] = {"value": n / per_step, "unit": "positions/s", "cores": _cores(),
+                               "kind": "oracle",
+                               "sample": f"both window summaries in full ({t1 - t0:.1f} s) and "
+                                         f"{sub} of the {nrep} replicates ({t2 - t1:.1f} s), "
+                                         "scaled to the full step"}
+    return res
+
 def _cores():
     try:
         import numpy  # noqa: F401
@@ -429,6 +525,9 @@ def main():
     elif args.workload == "golden_f32":
         cpu = 64 if args.cpu_sample is None else args.cpu_sample
         res = golden_f32(args.steps, args.warmup, cpu)
+    elif args.workload == "windows_paired":
+        cpu = 10_000 if args.cpu_sample is None else args.cpu_sample
+        res = windows_paired(args.steps, args.warmup, cpu)
     else:
         cpu = 64 if args.cpu_sample is None else args.cpu_sample
         res = logits_f32(args.steps, args.warmup, cpu)
@@ -441,17 +540,19 @@ def main():
         line["cpu_baseline"] = res["cpu_baseline"]
     if "result" in res:
         line["result"] = res["result"]
-    if "export_ms" in res:
-        line["export_ms"] = res["export_ms"]
+    for k in ("export_ms", "paired_ms"):
+        if k in res:
+            line[k] = res[k]
     if args.workload == "fused_window" and not args.no_secondary:
         line["secondary"] = []
-        for fn in (logits_f32, logits_bf16_topk, golden_f32):
+        for fn in (logits_f32, logits_bf16_topk, golden_f32, windows_paired):
             sec = fn(max(5, args.steps), args.warmup, 0)
             entry = {"workload": sec["config"]["workload"], "value": round(sec["value"], 1),
                      "unit": sec["unit"], "ms_per_step": round(sec["ms_per_step"], 4),
                      "roofline": sec["roofline"]}
-            if "export_ms" in sec:
-                entry["export_ms"] = sec["export_ms"]
+            for k in ("export_ms", "paired_ms"):
+                if k in sec:
+                    entry[k] = sec[k]
             line["secondary"].append(entry)
     print(json.dumps(line), flush=True)
 

@@ -14,8 +14,7 @@ import torch
 
 TOPK = 64
 KLD_F32, KLD_BF16 = 0, 1
-(OP_FROM_LOGITS, OP_FUSED_HEAD, OP_TOPK_EXPORT, OP_SUMMARY, OP_COARSE_KL, OP_WINDOWS,
- OP_PAIRED) = range(7)
+OP_FROM_LOGITS, OP_FUSED_HEAD, OP_TOPK_EXPORT, OP_SUMMARY, OP_COARSE_KL, OP_PAIRED = range(6)
 FLAG_TOPK = 1
 N_SUMMARY_FIXED = 8
 
@@ -64,7 +63,7 @@ _SIGS = {
     "kld_summary": (_I, [_P, _P, _P, _P, _P, _I64, _P, _I, _P, _P, _SZ, _P]),
     "kld_golden_export": (_I, [_P, _I, _I64, _I64, _I64, _P, _I, _P, _P, _P, _P]),
     "kld_coarse_kl": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P, _I, _P, _P, _SZ, _P]),
-    "kld_window_summary": (_I, [_P, _I64, _P, _I64, _I64, _P, _I, _P, _P, _P, _P, _SZ, _P]),
+    "kld_window_summary": (_I, [_P, _I64, _P, _I64, _I64, _P, _I, _P, _P, _P, _P, _P]),
     "kld_paired_bootstrap": (_I, [_P, _P, _P, _I64, _P, _I64, _P, _I64, _P, _I, _P, _P, _P, _SZ,
                                   _P]),
     "kld_status_str": (ctypes.c_char_p, [_I]),
@@ -307,22 +306,25 @@ def kld_coarse_kl(cand: torch.Tensor, ids: torch.Tensor, lp: torch.Tensor, rec: 
 
 
 def kld_window_summary(kl: torch.Tensor, offsets: torch.Tensor, score_from: int = 0,
-                       thresholds=(), ws: torch.Tensor | None = None, stream=None) -> dict:
-    """Scored-window statistics: per-segment sums and counts past score_from,
-    the mean over every scored position and exact exceedance counts."""
+                       thresholds=(), out: dict | None = None, stream=None) -> dict:
+    """Scored-window statistics: per-segment sums, counts and exceedance
+    counts past score_from, the mean over every scored position and the
+    exact exceedance counts over all of them."""
     n = kl.shape[0]
-    nseg = offsets.shape[0] - 1
+    nseg = max(offsets.shape[0] - 1, 0)
+    nthr = len(thresholds)
     dev = kl.device
-    seg_sum = torch.empty(max(nseg, 0), dtype=torch.float64, device=dev)
-    seg_count = torch.empty(max(nseg, 0), dtype=torch.int64, device=dev)
-    totals = torch.empty(2 + len(thresholds), dtype=torch.float64, device=dev)
-    th = (ctypes.c_float * max(len(thresholds), 1))(*thresholds)
-    ws, need = _workspace(OP_WINDOWS, 0, 0, 0, 0, dev, ws)
-    code = lib().kld_window_summary(_ptr(kl), n, _ptr(offsets), nseg, int(score_from), th,
-                                    len(thresholds), _ptr(seg_sum), _ptr(seg_count), _ptr(totals),
-                                    _ptr(ws), ws.numel(), _stream(stream))
+    if out is None:
+        out = {"seg_sum": torch.empty(nseg, dtype=torch.float64, device=dev),
+               "seg_count": torch.empty(nseg, dtype=torch.int64, device=dev),
+               "seg_exceed": torch.empty((nseg, nthr), dtype=torch.int64, device=dev),
+               "totals": torch.empty(2 + nthr, dtype=torch.float64, device=dev)}
+    th = (ctypes.c_float * max(nthr, 1))(*thresholds)
+    code = lib().kld_window_summary(_ptr(kl), n, _ptr(offsets), nseg, int(score_from), th, nthr,
+                                    _ptr(out["seg_sum"]), _ptr(out["seg_count"]),
+                                    _ptr(out["seg_exceed"]), _ptr(out["totals"]), _stream(stream))
     _check(code, "kld_window_summary")
-    return {"seg_sum": seg_sum, "seg_count": seg_count, "totals": totals}
+    return out
 
 
 def kld_paired_bootstrap(sum_a: torch.Tensor, sum_b: torch.Tensor, count: torch.Tensor,
@@ -338,7 +340,7 @@ def kld_paired_bootstrap(sum_a: torch.Tensor, sum_b: torch.Tensor, count: torch.
     reps = torch.empty(nrep, dtype=torch.float64, device=dev)
     out = torch.empty(4 + len(quantiles), dtype=torch.float64, device=dev)
     qs = (ctypes.c_double * max(len(quantiles), 1))(*quantiles)
-    ws, need = _workspace(OP_PAIRED, nclust, 0, 0, 0, dev, ws)
+    ws, need = _workspace(OP_PAIRED, nclust, nrep, 0, 0, dev, ws)
     code = lib().kld_paired_bootstrap(_ptr(sum_a), _ptr(sum_b), _ptr(count), nctx, _ptr(cluster),
                                       nclust, _ptr(draws), nrep, qs, len(quantiles), _ptr(reps),
                                       _ptr(out), _ptr(ws), ws.numel(), _stream(stream))

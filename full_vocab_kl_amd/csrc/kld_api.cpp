@@ -130,8 +130,7 @@ size_t kld_workspace_size(int op, int64_t n, int64_t v, int64_t d, int flags) {
     case KLD_OP_TOPK_EXPORT: return logits_workspace(n, v, KLD_FLAG_TOPK, &c);
     case KLD_OP_FUSED_HEAD: return fused_workspace(n, v, flags, &c);
     case KLD_OP_SUMMARY: return round_up(summary_workspace_bytes(n), kAlign);
-    case KLD_OP_WINDOWS: return round_up((KLD_MAX_THRESHOLDS + 1) * sizeof(unsigned long long), kAlign);
-    case KLD_OP_PAIRED: return round_up(paired_workspace_bytes(n), kAlign);
+    case KLD_OP_PAIRED: return round_up(paired_workspace_bytes(n, v), kAlign);
     case KLD_OP_COARSE_KL: {
       if (n == 0 || v == 0) return 0;
       const CoarseGeom g = coarse_geom(n, v);
@@ -298,7 +297,8 @@ kld_status kld_paired_bootstrap(const double *sum_a, const double *sum_b, const 
     if (!(q >= 0.0 && q <= 1.0)) return KLD_EINVAL;
     qs.q[i] = q;
   }
-  if (nclust > 0 && (!ws || ws_bytes < kld_workspace_size(KLD_OP_PAIRED, nclust, 0, 0, 0)))
+  if ((nclust > 0 || nrep > 0) &&
+      (!ws || ws_bytes < kld_workspace_size(KLD_OP_PAIRED, nclust, nrep, 0, 0)))
     return KLD_EWORKSPACE;
   if (launch_paired_bootstrap(sum_a, sum_b, count, nctx, cluster, nclust, draws, nrep, qs,
                               replicates, out, ws, as_stream(stream)) != hipSuccess)
@@ -308,19 +308,19 @@ kld_status kld_paired_bootstrap(const double *sum_a, const double *sum_b, const 
 
 kld_status kld_window_summary(const float *kl, int64_t n, const int64_t *offsets, int64_t nseg,
                               int64_t score_from, const float *thresholds, int nthr,
-                              double *seg_sum, int64_t *seg_count, double *totals, void *ws,
-                              size_t ws_bytes, void *stream) {
+                              double *seg_sum, int64_t *seg_count, int64_t *seg_exceed,
+                              double *totals, void *stream) {
   if (n < 0 || nseg < 0 || score_from < 0 || nthr < 0) return KLD_EINVAL;
   if (nthr > KLD_MAX_THRESHOLDS || nseg > 0x7fffffffLL) return KLD_ESHAPE;
-  if (!offsets || !totals || (nseg > 0 && (!seg_sum || !seg_count)) || (nthr > 0 && !thresholds))
+  if (!offsets || !totals || (nseg > 0 && (!seg_sum || !seg_count)) ||
+      (nthr > 0 && (!thresholds || (nseg > 0 && !seg_exceed))))
     return KLD_EINVAL;
   if (n > 0 && !kl) return KLD_EINVAL;
-  if (!ws || ws_bytes < kld_workspace_size(KLD_OP_WINDOWS, 0, 0, 0, 0)) return KLD_EWORKSPACE;
   WindowThresholds thr;
   thr.count = nthr;
   for (int t = 0; t < KLD_MAX_THRESHOLDS; ++t) thr.value[t] = t < nthr ? thresholds[t] : 0.f;
-  if (launch_window_summary(kl, n, offsets, nseg, score_from, thr, seg_sum, seg_count, totals, ws,
-                            as_stream(stream)) != hipSuccess)
+  if (launch_window_summary(kl, n, offsets, nseg, score_from, thr, seg_sum, seg_count, seg_exceed,
+                            totals, as_stream(stream)) != hipSuccess)
     return KLD_EHIP;
   return KLD_OK;
 }

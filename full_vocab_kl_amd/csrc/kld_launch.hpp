@@ -116,14 +116,15 @@ struct PairedQuantiles {
   double q[16];
   int count;
 };
-size_t paired_workspace_bytes(int64_t nclust);
+size_t paired_workspace_bytes(int64_t nclust, int64_t nrep);
 hipError_t launch_paired_bootstrap(const double *sum_a, const double *sum_b, const int64_t *count,
                                    int64_t nctx, const int32_t *cluster, int64_t nclust,
                                    const int32_t *draws, int64_t nrep, const PairedQuantiles &qs,
                                    double *reps, double *out, void *ws, hipStream_t stream);
 hipError_t launch_window_summary(const float *kl, int64_t n, const int64_t *offsets, int64_t nseg,
                                  int64_t score_from, const WindowThresholds &thr, double *seg_sum,
-                                 int64_t *seg_count, double *totals, void *ws, hipStream_t stream);
+                                 int64_t *seg_count, int64_t *seg_exceed, double *totals,
+                                 hipStream_t stream);
 
 // golden records and the 513-cell score (kld_golden.hip)
 hipError_t launch_golden_export(const void *logits, int dtype, int64_t n, int64_t v, int64_t ld,

@@ -15,8 +15,14 @@
 //                           scored positions; one extra block: the overall
 //                           difference, wins, ties and a label check
 //   paired_replicate_kernel one wave per replicate: gather-sum over its draws
-//   paired_quantile_kernel  one block: bitonic sort of the replicates in LDS
-//                           and the interpolated percentiles
+//   paired_runsort_kernel   one block per run of 1,024 replicates: bitonic
+//                           sort of the run in LDS
+//   paired_rank_kernel      every replicate's rank among all of them (its
+//                           place in its own run plus a binary search in
+//                           each other run; ties ordered by run), scattered
+//                           into the sorted array
+//   paired_quantile_kernel  one block: NaN check and the interpolated
+//                           percentiles
 // Every sum runs in a fixed order, so results are bitwise reproducible.
 #include "kld.h"
 #include "kld_device.hpp"
@@ -52,6 +58,7 @@ __global__ __launch_bounds__(PT) void paired_cluster_kernel(
   if (k < nclust) {
     double d = 0.0;
     long long c = 0;
+#pragma unroll 4
     for (int64_t i = threadIdx.x; i < nctx; i += PT) {
       if (cluster[i] == k) {
         d += sum_a[i] - sum_b[i];
@@ -108,13 +115,19 @@ __global__ __launch_bounds__(RW * 64) void paired_replicate_kernel(
   double num = 0.0;
   long long den = 0;
   int bad = 0;
-  for (int64_t i = lane; i < nclust; i += 64) {
-    const int32_t k = dr[i];
-    if (k < 0 || k >= nclust) {
-      bad = 1;
-    } else {
-      num += clus_diff[k];
-      den += clus_count[k];
+  for (int64_t i0 = lane; i0 < nclust; i0 += 64 * 4) {
+    int32_t k[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) k[u] = i0 + 64 * u < nclust ? dr[i0 + 64 * u] : 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (i0 + 64 * u >= nclust) continue;
+      if (k[u] < 0 || k[u] >= nclust) {
+        bad = 1;
+      } else {
+        num += clus_diff[k[u]];
+        den += clus_count[k[u]];
+      }
     }
   }
 #pragma unroll
@@ -126,35 +139,34 @@ __global__ __launch_bounds__(RW * 64) void paired_replicate_kernel(
   if (lane == 0) reps[r] = (bad || den == 0) ? __builtin_nan("") : num / (double)den;
 }
 
-constexpr int QT = 1024;
+// Sorting the replicates: runs of RUN values are sorted one block each,
+// then every value's rank among all of them is its place in its own run plus,
+// for each other run, how many of that run's values precede it (values of
+// earlier runs that are <= it, of later runs that are < it), found by binary
+// search.  The ranks are a permutation, so each value lands in its own slot.
+// NaN replicates sort as +inf here; the quantile kernel reports NaN for them.
+constexpr int RUN = 1024;
+constexpr int MAXRUNS = KLD_MAX_REPLICATES / RUN;
+static_assert(MAXRUNS * RUN == KLD_MAX_REPLICATES, "replicate capacity");
 
-__global__ __launch_bounds__(QT) void paired_quantile_kernel(const double *__restrict__ reps,
-                                                             int64_t nrep, PairedQuantiles qs,
-                                                             double *__restrict__ out) {
-  __shared__ double x[KLD_MAX_REPLICATES];
-  __shared__ int any_nan;
-  int m = 1;
-  while (m < nrep) m <<= 1;
-  if (threadIdx.x == 0) any_nan = 0;
+__device__ __forceinline__ double sort_key(double v) { return v != v ? __builtin_inf() : v; }
+
+__global__ __launch_bounds__(RUN) void paired_runsort_kernel(const double *__restrict__ reps,
+                                                             int64_t nrep,
+                                                             double *__restrict__ runs) {
+  __shared__ double x[RUN];
+  const int t = threadIdx.x;
+  const int64_t g = (int64_t)blockIdx.x * RUN + t;
+  x[t] = g < nrep ? sort_key(reps[g]) : __builtin_inf();
   __syncthreads();
-  for (int i = threadIdx.x; i < m; i += QT) {
-    double v = i < nrep ? reps[i] : __builtin_inf();
-    if (v != v) {
-      any_nan = 1;
-      v = __builtin_inf();
-    }
-    x[i] = v;
-  }
-  __syncthreads();
-  // bitonic sort, ascending
-  for (int size = 2; size <= m; size <<= 1) {
+  for (int size = 2; size <= RUN; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = threadIdx.x; t < (m >> 1); t += QT) {
+      if (t < RUN / 2) {
         const int i = 2 * t - (t & (stride - 1));
         const int j = i + stride;
         const bool up = (i & size) == 0;
         const double a = x[i], b = x[j];
-        if ((a > b) == up) {
+        if ((b < a) == up) {
           x[i] = b;
           x[j] = a;
         }
@@ -162,13 +174,63 @@ __global__ __launch_bounds__(QT) void paired_quantile_kernel(const double *__res
       __syncthreads();
     }
   }
+  runs[(int64_t)blockIdx.x * RUN + t] = x[t];
+}
+
+constexpr int RT = 256;
+
+__global__ __launch_bounds__(RT) void paired_rank_kernel(const double *__restrict__ runs,
+                                                         int64_t nrep, int nruns,
+                                                         double *__restrict__ sorted) {
+  __shared__ double r[KLD_MAX_REPLICATES];
+  for (int i = threadIdx.x; i < nruns * RUN; i += RT) r[i] = runs[i];
+  __syncthreads();
+  const int64_t e = (int64_t)blockIdx.x * RT + threadIdx.x;
+  if (e >= nrep) return;
+  const int own = (int)(e / RUN);
+  const double v = r[e];
+  int64_t rank = e - (int64_t)own * RUN;
+  for (int q = 0; q < nruns; ++q) {
+    if (q == own) continue;
+    const double *run = r + q * RUN;
+    // lo = number of leading values of run q that precede v
+    int lo = 0, hi = RUN;
+    if (q < own) {
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (run[mid] <= v) lo = mid + 1; else hi = mid;
+      }
+    } else {
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (run[mid] < v) lo = mid + 1; else hi = mid;
+      }
+    }
+    rank += lo;
+  }
+  sorted[rank] = v;
+}
+
+constexpr int QT = 1024;
+
+__global__ __launch_bounds__(QT) void paired_quantile_kernel(const double *__restrict__ reps,
+                                                             const double *__restrict__ sorted,
+                                                             int64_t nrep, PairedQuantiles qs,
+                                                             double *__restrict__ out) {
+  __shared__ int any_nan;
+  if (threadIdx.x == 0) any_nan = 0;
+  __syncthreads();
+  int nan_here = 0;
+  for (int64_t i = threadIdx.x; i < nrep; i += QT) nan_here |= reps[i] != reps[i];
+  if (nan_here) any_nan = 1;
+  __syncthreads();
   if ((int)threadIdx.x < qs.count) {
     double v = __builtin_nan("");
     if (nrep > 0 && !any_nan) {
       const double h = qs.q[threadIdx.x] * (double)(nrep - 1);
       const int64_t lo = (int64_t)floor(h);
       const int64_t hi = lo + 1 < nrep ? lo + 1 : nrep - 1;
-      v = x[lo] + (h - (double)lo) * (x[hi] - x[lo]);
+      v = sorted[lo] + (h - (double)lo) * (sorted[hi] - sorted[lo]);
     }
     out[4 + threadIdx.x] = v;
   }
@@ -176,8 +238,11 @@ __global__ __launch_bounds__(QT) void paired_quantile_kernel(const double *__res
 
 }  // namespace
 
-size_t paired_workspace_bytes(int64_t nclust) {
-  return (size_t)(nclust > 0 ? nclust : 0) * (sizeof(double) + sizeof(int64_t));
+size_t paired_workspace_bytes(int64_t nclust, int64_t nrep) {
+  const int64_t c = nclust > 0 ? nclust : 0;
+  const int64_t runs = nrep > 0 ? (nrep + RUN - 1) / RUN : 0;
+  return (size_t)c * (sizeof(double) + sizeof(int64_t)) +
+         (size_t)(runs * RUN + (nrep > 0 ? nrep : 0)) * sizeof(double);
 }
 
 hipError_t launch_paired_bootstrap(const double *sum_a, const double *sum_b, const int64_t *count,
@@ -186,6 +251,9 @@ hipError_t launch_paired_bootstrap(const double *sum_a, const double *sum_b, con
                                    double *reps, double *out, void *ws, hipStream_t stream) {
   double *clus_diff = static_cast<double *>(ws);
   int64_t *clus_count = reinterpret_cast<int64_t *>(clus_diff + nclust);
+  double *runs = reinterpret_cast<double *>(clus_count + nclust);
+  const int nruns = (int)((nrep + RUN - 1) / RUN);
+  double *sorted = runs + (int64_t)nruns * RUN;
   hipLaunchKernelGGL(paired_cluster_kernel, dim3((unsigned)(nclust + 1)), dim3(PT), 0, stream,
                      sum_a, sum_b, count, nctx, cluster, nclust, clus_diff, clus_count, out);
   hipError_t e = hipGetLastError();
@@ -193,10 +261,16 @@ hipError_t launch_paired_bootstrap(const double *sum_a, const double *sum_b, con
   if (nrep > 0) {
     hipLaunchKernelGGL(paired_replicate_kernel, dim3((unsigned)((nrep + RW - 1) / RW)),
                        dim3(RW * 64), 0, stream, clus_diff, clus_count, nclust, draws, nrep, reps);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(paired_runsort_kernel, dim3((unsigned)nruns), dim3(RUN), 0, stream, reps,
+                       nrep, runs);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(paired_rank_kernel, dim3((unsigned)((nrep + RT - 1) / RT)), dim3(RT), 0,
+                       stream, runs, nrep, nruns, sorted);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(paired_quantile_kernel, dim3(1), dim3(QT), 0, stream, reps, nrep, qs, out);
+  hipLaunchKernelGGL(paired_quantile_kernel, dim3(1), dim3(QT), 0, stream, reps, sorted, nrep, qs,
+                     out);
   return hipGetLastError();
 }
 

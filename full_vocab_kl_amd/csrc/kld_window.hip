@@ -5,9 +5,9 @@
 // counts and the score_from 0 / 256 / 1024 window control).
 //
 // One block per segment sums its scored values in a fixed order (f64) and
-// counts them and their exceedances; the exceedance counts of all segments
-// go to integer counters (exact in any order); one block then adds the
-// segment sums in segment order.  Results are bitwise reproducible.
+// counts them and their exceedances; one block then adds the segments'
+// sums and counts in a fixed order.  No atomics: results are bitwise
+// reproducible.
 #include "kld.h"
 #include "kld_device.hpp"
 #include "kld_launch.hpp"
@@ -17,102 +17,139 @@ namespace kld {
 namespace {
 
 constexpr int WT = 256;
+constexpr int WU = 4;   // loads in flight per thread
 
-__global__ __launch_bounds__(WT) void window_zero_kernel(unsigned long long *counters, int m) {
-  if ((int)threadIdx.x < m) counters[threadIdx.x] = 0ull;
+__device__ __forceinline__ double wave_sum_f64(double x) {
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) x += __shfl_xor(x, m);
+  return x;
 }
 
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long x) {
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+// One block per segment.  Each thread keeps WU loads in flight, a running
+// f64 sum and one exceedance counter per threshold; waves reduce with a fixed
+// butterfly, then thread 0 adds the four wave results in order.
 __global__ __launch_bounds__(WT) void window_seg_kernel(
     const float *__restrict__ kl, int64_t n, const int64_t *__restrict__ offsets,
     int64_t score_from, WindowThresholds thr, double *__restrict__ seg_sum,
-    int64_t *__restrict__ seg_count, unsigned long long *__restrict__ counters) {
-  __shared__ double red[WT];
-  __shared__ unsigned int cnt[KLD_MAX_THRESHOLDS];
+    int64_t *__restrict__ seg_count, int64_t *__restrict__ seg_exceed) {
+  __shared__ double wsum[WT / 64];
+  __shared__ unsigned int wcnt[WT / 64][KLD_MAX_THRESHOLDS];
   const int64_t seg = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t a = offsets[seg], b = offsets[seg + 1];
   const bool bad = a < 0 || b < a || b > n;
   const int64_t s = !bad && b - a > score_from ? a + score_from : b;
-  if ((int)threadIdx.x < KLD_MAX_THRESHOLDS) cnt[threadIdx.x] = 0u;
-  __syncthreads();
   double acc = 0.0;
   unsigned int c[KLD_MAX_THRESHOLDS];
 #pragma unroll
   for (int t = 0; t < KLD_MAX_THRESHOLDS; ++t) c[t] = 0u;
-  if (!bad) {
-    for (int64_t j = s + threadIdx.x; j < b; j += WT) {
-      const float x = kl[j];
-      acc += (double)x;
+  for (int64_t j0 = s + threadIdx.x; j0 < b; j0 += WT * WU) {
+    float x[WU];
+#pragma unroll
+    for (int u = 0; u < WU; ++u) {
+      const int64_t j = j0 + (int64_t)u * WT;
+      x[u] = j < b ? __builtin_nontemporal_load(kl + j) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < WU; ++u) {
+      const bool in = j0 + (int64_t)u * WT < b;
+      acc += (double)x[u];
 #pragma unroll
       for (int t = 0; t < KLD_MAX_THRESHOLDS; ++t)
-        if (t < thr.count && x > thr.value[t]) ++c[t];
+        c[t] += (t < thr.count && in && x[u] > thr.value[t]) ? 1u : 0u;
     }
   }
-#pragma unroll
-  for (int t = 0; t < KLD_MAX_THRESHOLDS; ++t)
-    if (t < thr.count && c[t]) atomicAdd(&cnt[t], c[t]);
-  red[threadIdx.x] = acc;
+  acc = wave_sum_f64(acc);
+  if (lane == 0) wsum[wave] = acc;
+  for (int t = 0; t < thr.count; ++t) {
+    const unsigned long long w = wave_sum_u64(c[t]);
+    if (lane == 0) wcnt[wave][t] = (unsigned int)w;
+  }
   __syncthreads();
-  for (int h = WT / 2; h > 0; h >>= 1) {
-    if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
-    __syncthreads();
-  }
   if (threadIdx.x == 0) {
-    seg_sum[seg] = bad ? __builtin_nan("") : red[0];
+    double sum = 0.0;
+#pragma unroll
+    for (int w = 0; w < WT / 64; ++w) sum += wsum[w];
+    seg_sum[seg] = bad ? __builtin_nan("") : sum;
     seg_count[seg] = bad ? 0 : b - s;
-    if (bad) atomicAdd(&counters[KLD_MAX_THRESHOLDS], 1ull);
   }
-  if ((int)threadIdx.x < thr.count && cnt[threadIdx.x])
-    atomicAdd(&counters[threadIdx.x], (unsigned long long)cnt[threadIdx.x]);
+  if ((int)threadIdx.x < thr.count) {
+    unsigned long long e = 0;
+#pragma unroll
+    for (int w = 0; w < WT / 64; ++w) e += wcnt[w][threadIdx.x];
+    seg_exceed[seg * thr.count + threadIdx.x] = (int64_t)e;
+  }
 }
 
-__global__ __launch_bounds__(WT) void window_total_kernel(
-    const double *__restrict__ seg_sum, const int64_t *__restrict__ seg_count, int64_t nseg,
-    const unsigned long long *__restrict__ counters, int nthr, double *__restrict__ totals) {
-  __shared__ double red[WT];
-  __shared__ unsigned long long rc[WT];
+// One block: the totals over every segment in a fixed order.  A malformed
+// segment's NaN sum makes the mean NaN.
+constexpr int TT = 1024;
+
+__global__ __launch_bounds__(TT) void window_total_kernel(
+    const double *__restrict__ seg_sum, const int64_t *__restrict__ seg_count,
+    const int64_t *__restrict__ seg_exceed, int64_t nseg, int nthr, double *__restrict__ totals) {
+  __shared__ double wsum[TT / 64];
+  __shared__ unsigned long long wcnt[TT / 64][KLD_MAX_THRESHOLDS + 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   double acc = 0.0;
-  unsigned long long c = 0ull;
-  for (int64_t i = threadIdx.x; i < nseg; i += WT) {
+  unsigned long long c[KLD_MAX_THRESHOLDS + 1];
+#pragma unroll
+  for (int t = 0; t <= KLD_MAX_THRESHOLDS; ++t) c[t] = 0ull;
+#pragma unroll 2
+  for (int64_t i = threadIdx.x; i < nseg; i += TT) {
     acc += seg_sum[i];
-    c += (unsigned long long)seg_count[i];
+    c[KLD_MAX_THRESHOLDS] += (unsigned long long)seg_count[i];
+#pragma unroll
+    for (int t = 0; t < KLD_MAX_THRESHOLDS; ++t)
+      if (t < nthr) c[t] += (unsigned long long)seg_exceed[i * nthr + t];
   }
-  red[threadIdx.x] = acc;
-  rc[threadIdx.x] = c;
+  acc = wave_sum_f64(acc);
+  if (lane == 0) wsum[wave] = acc;
+#pragma unroll
+  for (int t = 0; t <= KLD_MAX_THRESHOLDS; ++t) {
+    const unsigned long long w = wave_sum_u64(c[t]);
+    if (lane == 0) wcnt[wave][t] = w;
+  }
   __syncthreads();
-  for (int h = WT / 2; h > 0; h >>= 1) {
-    if ((int)threadIdx.x < h) {
-      red[threadIdx.x] += red[threadIdx.x + h];
-      rc[threadIdx.x] += rc[threadIdx.x + h];
-    }
-    __syncthreads();
-  }
   if (threadIdx.x == 0) {
-    const bool bad = counters[KLD_MAX_THRESHOLDS] != 0ull;
-    const double cnt = (double)rc[0];
-    totals[0] = bad || rc[0] == 0ull ? __builtin_nan("") : red[0] / cnt;
-    totals[1] = cnt;
+    double sum = 0.0;
+    unsigned long long cnt = 0;
+#pragma unroll
+    for (int w = 0; w < TT / 64; ++w) {
+      sum += wsum[w];
+      cnt += wcnt[w][KLD_MAX_THRESHOLDS];
+    }
+    totals[0] = cnt == 0ull ? __builtin_nan("") : sum / (double)cnt;
+    totals[1] = (double)cnt;
   }
-  if ((int)threadIdx.x < nthr) totals[2 + threadIdx.x] = (double)counters[threadIdx.x];
+  if ((int)threadIdx.x < nthr) {
+    unsigned long long e = 0;
+#pragma unroll
+    for (int w = 0; w < TT / 64; ++w) e += wcnt[w][threadIdx.x];
+    totals[2 + threadIdx.x] = (double)e;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_window_summary(const float *kl, int64_t n, const int64_t *offsets, int64_t nseg,
                                  int64_t score_from, const WindowThresholds &thr, double *seg_sum,
-                                 int64_t *seg_count, double *totals, void *ws, hipStream_t stream) {
-  unsigned long long *counters = static_cast<unsigned long long *>(ws);
-  hipLaunchKernelGGL(window_zero_kernel, dim3(1), dim3(WT), 0, stream, counters,
-                     KLD_MAX_THRESHOLDS + 1);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+                                 int64_t *seg_count, int64_t *seg_exceed, double *totals,
+                                 hipStream_t stream) {
   if (nseg > 0) {
     hipLaunchKernelGGL(window_seg_kernel, dim3((unsigned)nseg), dim3(WT), 0, stream, kl, n,
-                       offsets, score_from, thr, seg_sum, seg_count, counters);
-    e = hipGetLastError();
+                       offsets, score_from, thr, seg_sum, seg_count, seg_exceed);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(window_total_kernel, dim3(1), dim3(WT), 0, stream, seg_sum, seg_count, nseg,
-                     counters, thr.count, totals);
+  hipLaunchKernelGGL(window_total_kernel, dim3(1), dim3(TT), 0, stream, seg_sum, seg_count,
+                     seg_exceed, nseg, thr.count, totals);
   return hipGetLastError();
 }
 

@@ -83,8 +83,7 @@ enum {
   KLD_OP_TOPK_EXPORT = 2,
   KLD_OP_SUMMARY = 3,
   KLD_OP_COARSE_KL = 4,
-  KLD_OP_WINDOWS = 5,
-  KLD_OP_PAIRED = 6
+  KLD_OP_PAIRED = 5
 };
 #define KLD_FLAG_TOPK 1       /* the call will also export top-64 lists */
 
@@ -121,8 +120,9 @@ typedef struct kld_launch_opts {
 
 /* Bytes of workspace an operation needs.  op is a KLD_OP_* code; flags may
  * hold KLD_FLAG_TOPK.  d is used by KLD_OP_FUSED_HEAD only; for
- * KLD_OP_SUMMARY, n is the number of positions.  Returns 0 for an unknown op
- * or negative sizes. */
+ * KLD_OP_SUMMARY, n is the number of positions; for KLD_OP_PAIRED, n is the
+ * number of clusters and v the number of replicates.  Returns 0 for an
+ * unknown op or negative sizes. */
 size_t kld_workspace_size(int op, int64_t n, int64_t v, int64_t d, int flags);
 
 /*
@@ -277,18 +277,20 @@ kld_status kld_coarse_kl(const void *cand, int dtype, int64_t n, int64_t v, int6
  *              (its mean is seg_sum / seg_count; the mean over a subset of
  *              segments is the sum of their sums over the sum of their counts).
  * seg_count  : [nseg] int64 output, scored positions per segment.
+ * seg_exceed : [nseg, nthr] int64 output (row-major; may be NULL when
+ *              nthr == 0): per segment, the scored positions whose score
+ *              exceeds thresholds[t] (strictly).
  * totals     : [2 + nthr] f64 output: [0] mean over every scored position
  *              (each weighted equally), [1] their count, [2 + t] how many
- *              exceed thresholds[t] (strictly).
- * ws         : kld_workspace_size(KLD_OP_WINDOWS, 0, 0, 0, 0) bytes.
- * A segment whose offsets break the rules gets seg_sum NaN and count 0, and
- * totals[0] is NaN.  Sums are taken in a fixed order: results are bitwise
- * reproducible.
+ *              exceed thresholds[t] over every segment.
+ * Needs no workspace.  A segment whose offsets break the rules gets seg_sum
+ * NaN and count 0, and totals[0] is NaN.  Sums are taken in a fixed order
+ * and nothing uses atomics: results are bitwise reproducible.
  */
 kld_status kld_window_summary(const float *kl, int64_t n, const int64_t *offsets, int64_t nseg,
                               int64_t score_from, const float *thresholds, int nthr,
-                              double *seg_sum, int64_t *seg_count, double *totals, void *ws,
-                              size_t ws_bytes, void *stream);
+                              double *seg_sum, int64_t *seg_count, int64_t *seg_exceed,
+                              double *totals, void *stream);
 
 /*
  * kld_paired_bootstrap -- paired per-context comparison of two candidates
@@ -317,7 +319,8 @@ kld_status kld_window_summary(const float *kl, int64_t n, const int64_t *offsets
  *                a's mean is lower, [2] where b's is lower, [3] ties
  *                (contexts with count 0 are in none), [4 + i] the type-7
  *                percentile of the replicates at quantiles[i].
- * ws           : kld_workspace_size(KLD_OP_PAIRED, nclust, 0, 0, 0) bytes.
+ * ws           : kld_workspace_size(KLD_OP_PAIRED, nclust, nrep, 0, 0) bytes
+ *                (per-cluster sums and two copies of the replicates).
  * A cluster label outside [0, nclust) or a negative count makes out[0] NaN;
  * a draw outside it makes that replicate NaN; any NaN replicate (or none)
  * makes every percentile NaN.  Sums run in a fixed order: results are

@@ -143,19 +143,17 @@ def test_golden_and_coarse_validation_fails_closed():
 def test_window_summary_validation_fails_closed():
     lib = kld.lib()
     thr = (ctypes.c_float * 17)(*range(17))
-    ws = 1 << 20
     # kld_window_summary(kl, n, offsets, nseg, score_from, thr, nthr, seg_sum, seg_count,
-    #                    totals, ws, ws_bytes, stream)
-    assert lib.kld_window_summary(16, 10, 16, 2, 0, thr, 17, 16, 16, 16, 16, ws, None) == 2
-    assert lib.kld_window_summary(16, 10, 16, 2, -1, thr, 1, 16, 16, 16, 16, ws, None) == 1
-    assert lib.kld_window_summary(16, -1, 16, 2, 0, thr, 1, 16, 16, 16, 16, ws, None) == 1
-    assert lib.kld_window_summary(16, 10, None, 2, 0, thr, 1, 16, 16, 16, 16, ws, None) == 1
-    assert lib.kld_window_summary(16, 10, 16, 2, 0, None, 1, 16, 16, 16, 16, ws, None) == 1
-    assert lib.kld_window_summary(16, 10, 16, 2, 0, thr, 1, None, 16, 16, 16, ws, None) == 1
-    assert lib.kld_window_summary(None, 10, 16, 2, 0, thr, 1, 16, 16, 16, 16, ws, None) == 1
-    assert lib.kld_window_summary(16, 10, 16, 2, 0, thr, 1, 16, 16, 16, None, 0, None) == 4
-    assert lib.kld_window_summary(16, 10, 16, 2, 0, thr, 1, 16, 16, 16, 16, 8, None) == 4
-    assert kld.kld_workspace_size(5, 0, 0) >= 17 * 8
+    #                    seg_exceed, totals, stream)
+    assert lib.kld_window_summary(16, 10, 16, 2, 0, thr, 17, 16, 16, 16, 16, None) == 2
+    assert lib.kld_window_summary(16, 10, 16, 2, -1, thr, 1, 16, 16, 16, 16, None) == 1
+    assert lib.kld_window_summary(16, -1, 16, 2, 0, thr, 1, 16, 16, 16, 16, None) == 1
+    assert lib.kld_window_summary(16, 10, None, 2, 0, thr, 1, 16, 16, 16, 16, None) == 1
+    assert lib.kld_window_summary(16, 10, 16, 2, 0, None, 1, 16, 16, 16, 16, None) == 1
+    assert lib.kld_window_summary(16, 10, 16, 2, 0, thr, 1, None, 16, 16, 16, None) == 1
+    assert lib.kld_window_summary(16, 10, 16, 2, 0, thr, 1, 16, 16, None, 16, None) == 1
+    assert lib.kld_window_summary(16, 10, 16, 2, 0, thr, 1, 16, 16, 16, None, None) == 1
+    assert lib.kld_window_summary(None, 10, 16, 2, 0, thr, 1, 16, 16, 16, 16, None) == 1
 
 
 def test_paired_bootstrap_validation_fails_closed():
@@ -181,4 +179,4 @@ def test_paired_bootstrap_validation_fails_closed():
     assert lib.kld_paired_bootstrap(16, 16, 16, 8, 16, 3, 16, 10, q, 2, 16, 16, None, 0,
                                     None) == 4
     assert lib.kld_paired_bootstrap(16, 16, 16, 8, 16, 3, 16, 10, q, 2, 16, 16, 16, 8, None) == 4
-    assert kld.kld_workspace_size(6, 842, 0) >= 842 * 16
+    assert kld.kld_workspace_size(5, 842, 10_000) >= 842 * 16 + 2 * 10_000 * 8

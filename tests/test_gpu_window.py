@@ -28,6 +28,7 @@ def _check(x, offsets, score_from, thr=THR, where=""):
     got = _run(x, offsets, score_from, thr)
     want = oracle.window_summary(x, offsets, score_from, thr)
     assert np.array_equal(got["seg_count"], want["seg_count"]), f"{where}: counts"
+    assert np.array_equal(got["seg_exceed"], want["seg_exceed"]), f"{where}: segment exceedances"
     err = np.abs(got["seg_sum"] - want["seg_sum"])
     assert np.all(err <= 1e-12 * np.maximum(np.abs(want["seg_sum"]), 1e-300)), f"{where}: sums"
     t = got["totals"]
