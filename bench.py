@@ -51,7 +51,9 @@ def _args():
 
 KERNEL_SOURCES = {"fused_head_kernel<true>": "full_vocab_kl_amd/csrc/kld_fused.hip",
                   "logits_partial_kernel_f32": "full_vocab_kl_amd/csrc/kld_logits.hip",
-                  "logits_partial_kernel_bf16_topk": "full_vocab_kl_amd/csrc/kld_logits.hip"}
+                  "logits_partial_kernel_bf16_topk": "full_vocab_kl_amd/csrc/kld_logits.hip",
+                  "coarse_partial_kernel_f32": "full_vocab_kl_amd/csrc/kld_golden.hip",
+                  "window_seg_kernel": "full_vocab_kl_amd/csrc/kld_window.hip"}
 
 
 def _traffic(kernel_key):
@@ -374,7 +376,8 @@ def golden_f32(steps, warmup, cpu_sample):
                    "positions": n, "V": v},
         "roofline": {"bound": "hbm", "kernel": "coarse_partial_kernel + coarse_finalize_kernel",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": _traffic("coarse_partial_kernel_f32"),
                      "kernel_ms": round(kernel_ms, 4),
                      "algorithmic": f"4*N*V = {nbytes:.4e} bytes per call (candidate rows once)"},
         "export_ms": round(export_ms, 4),
@@ -464,7 +467,9 @@ def windows_paired(steps, warmup, cpu_sample):
                    "positions": n, "contexts": nctx, "clusters": nclust, "replicates": nrep},
         "roofline": {"bound": "hbm", "kernel": "window_seg_kernel (two candidates)",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": (None if _traffic("window_seg_kernel") is None
+                                 else 2 * _traffic("window_seg_kernel")),
                      "kernel_ms": round(w_ms, 4),
                      "algorithmic": "2 x (4 B per position + 8 B per offset + 16 B + 8 B per "
                                     f"threshold per context of output) = {nbytes:.4e} bytes"},
