@@ -39,7 +39,7 @@ def _args():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="fused_window",
                    choices=["fused_window", "logits_f32", "logits_bf16_topk", "golden_f32",
-                            "windows_paired"])
+                            "windows_paired", "coarse_fused_window"])
     p.add_argument("--cpu-sample", type=int, default=None,
                    help="positions the CPU oracle scores for the baseline (0 = skip)")
     p.add_argument("--no-secondary", action="store_true",
@@ -49,7 +49,8 @@ def _args():
     return p.parse_args()
 
 
-KERNEL_SOURCES = {"fused_head_kernel<true>": "full_vocab_kl_amd/csrc/kld_fused.hip",
+KERNEL_SOURCES = {"fused_head_kernel<1>": "full_vocab_kl_amd/csrc/kld_fused.hip",
+                  "fused_head_kernel<2>": "full_vocab_kl_amd/csrc/kld_fused.hip",
                   "logits_partial_kernel_f32": "full_vocab_kl_amd/csrc/kld_logits.hip",
                   "logits_partial_kernel_bf16_topk": "full_vocab_kl_amd/csrc/kld_logits.hip",
                   "coarse_partial_kernel_f32": "full_vocab_kl_amd/csrc/kld_golden.hip",
@@ -141,10 +142,10 @@ def fused_window(steps, warmup, cpu_sample):
                                "W~N(0,0.02^2), hidden RMS-normalised, cand noise 0.01, f32 "
                                "accumulate and softmax",
                    "positions": n, "d": d, "V": v},
-        "roofline": {"bound": "mfma", "kernel": "fused_head_kernel<true>",
+        "roofline": {"bound": "mfma", "kernel": "fused_head_kernel<1>",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": _traffic("fused_head_kernel<true>"),
+                     "traffic": _traffic("fused_head_kernel<1>"),
                      "kernel_ms": round(kernel_ms, 4),
                      "algorithmic": f"4*N*d*V = {flops:.4e} flop per launch"},
         "result": {"mean_kl": summary["mean_kl"], "mean_tail_kl": float(tail.double().mean()),
@@ -178,6 +179,79 @@ def cpu_fused(w_np, hr_np, hc_np, t_np, m):
                       f"both sides over all 248,320 ids, KL/argmax/NLL, top-64 + tail KLD, "
                       f"summary), {dt:.1f} s"}
 
+
+
+def coarse_fused_window(steps, warmup, cpu_sample):
+    """One 2047-position window of a candidate given as hidden states (d =
+    5120) through the shared bf16 head (V = 248,320), scored against stored
+    golden records (512 listed ids + tail): one step is kld_coarse_fused and
+    kld_summary.  Records are seeded stand-ins of the golden format."""
+    import numpy as np
+    import torch
+
+    import full_vocab_kl_amd as kld
+    import synth
+
+    n, v, d = synth.WINDOW_POSITIONS, synth.VOCAB, synth.HIDDEN
+    wl = synth.FUSED_WINDOW
+    w_np = synth.head_weight(wl, v, d)
+    _, hc_np = synth.hidden_rows(wl, range(n), d, 0.01)
+    ids_np, lp_np, rec_np = synth.sparse_records(wl, n, v)
+    dev = torch.device("cuda:0")
+    bf = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    W, hc = bf(w_np), bf(hc_np)
+    ids, lp, rec = (torch.from_numpy(x).to(dev) for x in (ids_np, lp_np, rec_np))
+    ws = torch.empty(kld.kld_workspace_size(6, n, v, d), dtype=torch.uint8, device=dev)
+    ws_s = torch.empty(kld.kld_workspace_size(3, n, 0), dtype=torch.uint8, device=dev)
+    summ = torch.empty(8 + len(QUANTILES), dtype=torch.float64, device=dev)
+    kl = torch.empty(n, dtype=torch.float32, device=dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+
+    def step(ev=None):
+        kld.kld_coarse_fused(W, hc, ids, lp, rec, out=kl, ws=ws, events=ev)
+        kld.kld_summary(kl, quantiles=QUANTILES, ws=ws_s, out=summ)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kms = [a.elapsed_time(b) for a, b in evs]
+    kernel_ms = sum(kms) / len(kms)
+    flops = 2.0 * n * d * v
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    summary = kld.summary_dict(summ, QUANTILES)
+    res = {
+        "value": n * steps / elapsed, "unit": "positions/s", "ms_per_step": elapsed * 1e3 / steps,
+        "dtype": "bf16",
+        "config": {"workload": "kld_coarse_fused + kld_summary: one window, N=2047 candidate "
+                               "positions as hidden states, d=5120, V=248,320 through the shared "
+                               "bf16 head, scored against 512-id golden records + tail",
+                   "positions": n, "d": d, "V": v},
+        "roofline": {"bound": "mfma", "kernel": "fused_head_kernel<2> (sparse mode)",
+                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": _traffic("fused_head_kernel<2>"),
+                     "kernel_ms": round(kernel_ms, 4),
+                     "algorithmic": f"2*N*d*V = {flops:.4e} flop per launch (candidate side only)"},
+        "result": {"mean_coarse_kl_vs_stand_in_records": summary["mean_kl"]},
+    }
+    if cpu_sample:
+        import oracle
+        rows = synth.subset(wl, n, cpu_sample)
+        t0 = time.perf_counter()
+        zb = oracle.head_logits(w_np, hc_np[rows])
+        oracle.coarse_kl_rows(ids_np[rows], lp_np[rows], rec_np[rows], zb)
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": len(rows) / dt, "unit": "positions/s", "cores": _cores(),
+                               "kind": "oracle",
+                               "sample": f"{len(rows)} seeded positions of the window (head logits "
+                                         f"in f64 over all 248,320 ids, 513-cell score), {dt:.1f} s"}
+    return res
 
 def logits_f32(steps, warmup, cpu_sample):
     import numpy as np
@@ -530,6 +604,9 @@ def main():
     elif args.workload == "golden_f32":
         cpu = 64 if args.cpu_sample is None else args.cpu_sample
         res = golden_f32(args.steps, args.warmup, cpu)
+    elif args.workload == "coarse_fused_window":
+        cpu = 64 if args.cpu_sample is None else args.cpu_sample
+        res = coarse_fused_window(args.steps, args.warmup, cpu)
     elif args.workload == "windows_paired":
         cpu = 10_000 if args.cpu_sample is None else args.cpu_sample
         res = windows_paired(args.steps, args.warmup, cpu)
@@ -550,7 +627,7 @@ def main():
             line[k] = res[k]
     if args.workload == "fused_window" and not args.no_secondary:
         line["secondary"] = []
-        for fn in (logits_f32, logits_bf16_topk, golden_f32, windows_paired):
+        for fn in (logits_f32, logits_bf16_topk, golden_f32, windows_paired, coarse_fused_window):
             sec = fn(max(5, args.steps), args.warmup, 0)
             entry = {"workload": sec["config"]["workload"], "value": round(sec["value"], 1),
                      "unit": sec["unit"], "ms_per_step": round(sec["ms_per_step"], 4),

@@ -14,7 +14,8 @@ import torch
 
 TOPK = 64
 KLD_F32, KLD_BF16 = 0, 1
-OP_FROM_LOGITS, OP_FUSED_HEAD, OP_TOPK_EXPORT, OP_SUMMARY, OP_COARSE_KL, OP_PAIRED = range(6)
+(OP_FROM_LOGITS, OP_FUSED_HEAD, OP_TOPK_EXPORT, OP_SUMMARY, OP_COARSE_KL, OP_PAIRED,
+ OP_COARSE_FUSED) = range(7)
 FLAG_TOPK = 1
 N_SUMMARY_FIXED = 8
 
@@ -63,6 +64,8 @@ _SIGS = {
     "kld_summary": (_I, [_P, _P, _P, _P, _P, _I64, _P, _I, _P, _P, _SZ, _P]),
     "kld_golden_export": (_I, [_P, _I, _I64, _I64, _I64, _P, _I, _P, _P, _P, _P]),
     "kld_coarse_kl": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P, _I, _P, _P, _SZ, _P]),
+    "kld_coarse_fused": (_I, [_P, _I64, _I64, _P, _I64, _P, _P, _P, _I, _P, _P, _SZ, _P,
+                              ctypes.POINTER(_Opts)]),
     "kld_window_summary": (_I, [_P, _I64, _P, _I64, _I64, _P, _I, _P, _P, _P, _P, _P]),
     "kld_paired_bootstrap": (_I, [_P, _P, _P, _I64, _P, _I64, _P, _I64, _P, _I, _P, _P, _P, _SZ,
                                   _P]),
@@ -302,6 +305,28 @@ def kld_coarse_kl(cand: torch.Tensor, ids: torch.Tensor, lp: torch.Tensor, rec: 
     code = lib().kld_coarse_kl(_ptr(cand), dt, n, v, _rows_ld(cand), _ptr(ids), _ptr(lp), _ptr(rec),
                                GOLDEN_TOPK, _ptr(out), _ptr(ws), ws.numel(), _stream(stream))
     _check(code, "kld_coarse_kl")
+    return out
+
+
+def kld_coarse_fused(W: torch.Tensor, h_cand: torch.Tensor, ids: torch.Tensor, lp: torch.Tensor,
+                     rec: torch.Tensor, out: torch.Tensor | None = None,
+                     ws: torch.Tensor | None = None, stream=None, events=None) -> torch.Tensor:
+    """513-cell coarsened KL of candidate hidden states [n, d], through the
+    shared bf16 head W [v, d], against golden records; logits are never
+    written to memory."""
+    v, d = W.shape
+    n = h_cand.shape[0]
+    for t in (W, h_cand):
+        if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or not t.is_contiguous():
+            raise TypeError("W and hidden states must be contiguous bf16 (or 16-bit bit-pattern) tensors")
+    if h_cand.shape != (n, d):
+        raise ValueError("hidden states must be [n, d] with d = W.shape[1]")
+    out = out if out is not None else torch.empty(n, dtype=torch.float32, device=W.device)
+    ws, need = _workspace(OP_COARSE_FUSED, n, v, d, 0, W.device, ws)
+    code = lib().kld_coarse_fused(_ptr(W), v, d, _ptr(h_cand), n, _ptr(ids), _ptr(lp), _ptr(rec),
+                                  GOLDEN_TOPK, _ptr(out), _ptr(ws), ws.numel(), _stream(stream),
+                                  _opts(events))
+    _check(code, "kld_coarse_fused")
     return out
 
 

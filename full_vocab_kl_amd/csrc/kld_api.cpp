@@ -90,6 +90,19 @@ FusedWs fused_carve(int64_t n, int64_t v, bool topk, Carver *c) {
   return w;
 }
 
+SparseWs sparse_carve(int64_t n, int64_t v, Carver *c) {
+  const SparseGeom g = sparse_geom(n, v);
+  SparseWs w;
+  w.part = c->take<float>((size_t)3 * g.nvt * g.npad);
+  w.zl = c->take<float>((size_t)n * KLD_GOLDEN_TOPK);
+  w.sid = c->take<int32_t>((size_t)n * KLD_GOLDEN_TOPK);
+  w.sslot = c->take<uint16_t>((size_t)n * KLD_GOLDEN_TOPK);
+  w.alias = c->take<uint16_t>((size_t)n * KLD_GOLDEN_TOPK);
+  w.rp = c->take<uint16_t>((size_t)n * (g.nvt + 1));
+  w.bad = c->take<int32_t>((size_t)n);
+  return w;
+}
+
 size_t fused_workspace(int64_t n, int64_t v, int flags, Carver *c) {
   fused_carve(n, v, (flags & KLD_FLAG_TOPK) != 0, c);
   return round_up(c->used, kAlign);
@@ -131,6 +144,7 @@ size_t kld_workspace_size(int op, int64_t n, int64_t v, int64_t d, int flags) {
     case KLD_OP_FUSED_HEAD: return fused_workspace(n, v, flags, &c);
     case KLD_OP_SUMMARY: return round_up(summary_workspace_bytes(n), kAlign);
     case KLD_OP_PAIRED: return round_up(paired_workspace_bytes(n, v), kAlign);
+    case KLD_OP_COARSE_FUSED: sparse_carve(n, v, &c); return round_up(c.used, kAlign);
     case KLD_OP_COARSE_KL: {
       if (n == 0 || v == 0) return 0;
       const CoarseGeom g = coarse_geom(n, v);
@@ -275,6 +289,29 @@ kld_status kld_coarse_kl(const void *cand, int dtype, int64_t n, int64_t v, int6
   if (launch_coarse_kl(cand, dtype, n, v, ld, aligned, ids, lp, rec, kl, ws, as_stream(stream)) !=
       hipSuccess)
     return KLD_EHIP;
+  return KLD_OK;
+}
+
+kld_status kld_coarse_fused(const uint16_t *W, int64_t v, int64_t d, const uint16_t *h_cand,
+                            int64_t n, const int32_t *ids, const float *lp, const float *rec, int k,
+                            float *kl, void *ws, size_t ws_bytes, void *stream,
+                            const kld_launch_opts *opts) {
+  if (n < 0 || v < 0 || d < 0) return KLD_EINVAL;
+  if (k != KLD_GOLDEN_TOPK) return KLD_ESHAPE;
+  if (n == 0) return KLD_OK;
+  if (n > 0x7fffffffLL || v < KLD_GOLDEN_TOPK || v > 0x7fffffffLL || d < 1 || d > (1 << 20))
+    return KLD_ESHAPE;
+  if (!W || !h_cand || !ids || !lp || !rec || !kl) return KLD_EINVAL;
+  if (d % 8 != 0 || !aligned16(W) || !aligned16(h_cand)) return KLD_EUNSUPPORTED;
+  if (!ws || ws_bytes < kld_workspace_size(KLD_OP_COARSE_FUSED, n, v, d, 0)) return KLD_EWORKSPACE;
+  Carver c(ws);
+  const SparseWs w = sparse_carve(n, v, &c);
+  CoarseFusedArgs a;
+  a.W = W; a.h_cand = h_cand; a.v = v; a.d = d; a.n = n;
+  a.ids = ids; a.lp = lp; a.rec = rec; a.kl = kl;
+  a.stream = as_stream(stream);
+  a.ev = events_of(opts);
+  if (launch_coarse_fused(a, w) != hipSuccess) return KLD_EHIP;
   return KLD_OK;
 }
 

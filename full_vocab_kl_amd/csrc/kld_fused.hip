@@ -32,6 +32,7 @@
 // and the head tile is fetched from HBM about once into that XCD's L2.
 #include <type_traits>
 
+#include "kld.h"
 #include "kld_device.hpp"
 #include "kld_launch.hpp"
 
@@ -112,13 +113,52 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, num, 0x00020000);
 }
 
-template <bool TOPK>
+// Online log-sum-exp state of one candidate column over part of a tile:
+// maximum m, s = sum e^(z - m) and u = the same sum over the unlisted ids.
+struct Lsu {
+  float m, s, u;
+};
+__device__ __forceinline__ Lsu lsu_merge(const Lsu &a, const Lsu &b) {
+  const float m = fmaxf(a.m, b.m);
+  const float fa = a.m == kNegInf ? 0.f : exp2_fast((a.m - ref_of(m)) * kL2E);
+  const float fb = b.m == kNegInf ? 0.f : exp2_fast((b.m - ref_of(m)) * kL2E);
+  return Lsu{m, fmaf(a.s, fa, b.s * fb), fmaf(a.u, fa, b.u * fb)};
+}
+
+struct SparseIn;
+template <typename Acc>
+__device__ __forceinline__ void sparse_epilogue(Acc &acc, const struct SparseIn &sp, float *part,
+                                                void *smem, int64_t v, int64_t v0, int vt,
+                                                int64_t p0, int64_t n, int64_t nvt, int64_t npad,
+                                                int wv, int wp, int fr, int fh, bool vtail);
+
+// Epilogue modes: KL state of a (reference, candidate) pair per position,
+// the same with top-64 candidates, or one-sided scoring of candidate
+// positions against stored sparse records (256 positions per block: the two
+// 128-row halves of the hidden unit are two position blocks of the
+// candidate).
+enum { kModeKl = 0, kModeTopk = 1, kModeSparse = 2 };
+
+// Listed ids of a position, sorted by id, for the sparse mode: sid[pos][e]
+// the id, sslot[pos][e] its slot in the record (bit 15: a repeat of the
+// previous id), rp[pos][t] the first entry with id >= 256 t.
+struct SparseIn {
+  const int32_t *sid;
+  const uint16_t *sslot;
+  const uint16_t *rp;
+  float *zl;   // [n][512] listed logits out
+};
+
+template <int MODE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restrict__ Hr,
                        const uint16_t *__restrict__ Hc, int64_t v, int64_t d, int64_t n, int npt,
                        int64_t npad, int64_t nvt, float *__restrict__ part,
                        uint64_t *__restrict__ ckeys, float *__restrict__ resid,
-                       uint64_t *__restrict__ rinfo, uint64_t *__restrict__ tkeys) {
+                       uint64_t *__restrict__ rinfo, uint64_t *__restrict__ tkeys, SparseIn sp) {
+  constexpr bool TOPK = MODE == kModeTopk;
+  constexpr bool SPARSE = MODE == kModeSparse;
+  constexpr int PB = SPARSE ? 2 * BP : BP;   // positions per block
   // The five ring slots (160 KB, the whole LDS) are separate LDS objects, so
   // that the compiler knows the loads into one slot never touch the fragment
   // reads of another and can interleave the two (with one array it kept
@@ -132,7 +172,7 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
 
   const int L = logical_block((int)blockIdx.x, (int)gridDim.x);
   const int vt = L / npt, pt = L % npt;
-  const int64_t v0 = (int64_t)vt * BV, p0 = (int64_t)pt * BP;
+  const int64_t v0 = (int64_t)vt * BV, p0 = (int64_t)pt * PB;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wv = wave >> 1, wp = wave & 1;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -154,13 +194,13 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
     const int r = 64 * wave + 8 * j + (lane >> 3);
     const int cl = (lane & 7) ^ swz_key(r);
     const int64_t rw = v0 + r < v ? r : v - 1 - v0;
-    const int q = r & (BP - 1);
+    const int q = SPARSE ? r : (r & (BP - 1));
     const int64_t rh = p0 + q < n ? q : n - 1 - p0;
     vo_w[j] = (uint32_t)(rw * d * 2 + cl * 16);
     vo_h[j] = (uint32_t)(rh * d * 2 + cl * 16);
   }
   const uint16_t *wbase = W + v0 * d;
-  const uint16_t *hbase = (wave_u < 2 ? Hr : Hc) + p0 * d;
+  const uint16_t *hbase = (SPARSE || wave_u >= 2 ? Hc : Hr) + p0 * d;
   const int64_t wbytes = (v - v0) * d * 2, hbytes = (n - p0) * d * 2;
   const int KT = (int)((d + BK - 1) / BK);
   const bool ktail = (d % BK) != 0;
@@ -389,6 +429,10 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
   // candidate.
   const int64_t vb = v0 + wv * 128 + 4 * fh;
   const bool vtail = v0 + BV > v;
+  if constexpr (SPARSE) {
+    sparse_epilogue(acc, sp, part, smem, v, v0, vt, p0, n, nvt, npad, wv, wp, fr, fh, vtail);
+    return;
+  }
   RowState *xch = reinterpret_cast<RowState *>(smem);          // [2 pos waves][2 pg][32]
   float *rx = reinterpret_cast<float *>(xch + 2 * 2 * 32);       // [2 sides][2][2][32]
   float *qx = rx + 2 * 2 * 2 * 32;                                 // same shape
@@ -542,6 +586,98 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
         // lowest id), position-major for the selection
         tkeys[((int64_t)0 * npad + pos) * nvt + vt] = st.ma == kNegInf ? 0ull : topk_key(st.ma, st.ia);
         tkeys[((int64_t)1 * npad + pos) * nvt + vt] = st.mb == kNegInf ? 0ull : topk_key(st.mb, st.ib);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Sparse-mode epilogue.  Column (pg, sd) of a lane is candidate position
+// p0 + 128 sd + 64 wp + 32 pg + (lane & 31); the lane holds its ids
+// vb + 32 vs + 8 (i / 4) + (i % 4).  For each column: the record's listed ids
+// that fall in this lane's part of the tile are marked in a 64-bit mask (bit
+// 16 vs + i) and their logits written to zl at their record slots; then the
+// lane's maximum, its sum and its sum over unmarked ids, merged with lane
+// l ^ 32 and with the other vocabulary wave, give the tile's partial state
+// (planes m, s, u of part[3][nvt][npad]).
+template <typename Acc>
+__device__ __forceinline__ void sparse_epilogue(Acc &acc, const SparseIn &sp, float *part,
+                                                void *smem, int64_t v, int64_t v0, int vt,
+                                                int64_t p0, int64_t n, int64_t nvt, int64_t npad,
+                                                int wv, int wp, int fr, int fh, bool vtail) {
+  Lsu *xch = reinterpret_cast<Lsu *>(smem);   // [2 pos waves][2 sd][32]
+  const int64_t plane = nvt * npad;
+#pragma unroll
+  for (int pg = 0; pg < 2; ++pg) {
+    if (vtail) {
+      const int lim = (int)(v - v0) - (wv * 128 + 4 * fh);
+#pragma unroll
+      for (int vs = 0; vs < 4; ++vs)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (32 * vs + 8 * (i >> 2) + (i & 3) >= lim) {
+            acc[vs][pg][0][i] = kNegInf;
+            acc[vs][pg][1][i] = kNegInf;
+          }
+    }
+    Lsu st[2];
+#pragma unroll
+    for (int sd = 0; sd < 2; ++sd) {
+      const int64_t pos = p0 + sd * BP + wp * 64 + pg * 32 + fr;
+      uint64_t lm = 0;
+      if (pos < n) {
+        const uint16_t *rr = sp.rp + pos * (nvt + 1) + vt;
+        const int e0 = rr[0], e1 = rr[1];
+        for (int e = e0; e < e1; ++e) {
+          const uint16_t sl = sp.sslot[pos * KLD_GOLDEN_TOPK + e];
+          const int idl = sp.sid[pos * KLD_GOLDEN_TOPK + e] - (int)v0;
+          if ((sl & 0x8000) || (idl >> 7) != wv || ((idl >> 2) & 1) != fh) continue;
+          const int k = ((idl >> 5) & 3) * 16 + ((idl >> 3) & 3) * 4 + (idl & 3);
+          lm |= 1ull << k;
+          float z = 0.f;
+#pragma unroll
+          for (int vs = 0; vs < 4; ++vs)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) z = k == vs * 16 + i ? acc[vs][pg][sd][i] : z;
+          sp.zl[pos * KLD_GOLDEN_TOPK + (sl & 0x1ff)] = z;
+        }
+      }
+      float m = kNegInf;
+#pragma unroll
+      for (int vs = 0; vs < 4; ++vs)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) m = vmax3(m, acc[vs][pg][sd][i], acc[vs][pg][sd][i + 1]);
+      const float r = ref_of(m);
+      float ssum = 0.f, usum = 0.f;
+#pragma unroll
+      for (int vs = 0; vs < 4; ++vs)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float w = exp2_fast((acc[vs][pg][sd][i] - r) * kL2E);
+          ssum += w;
+          usum += ((lm >> (vs * 16 + i)) & 1ull) ? 0.f : w;
+        }
+      st[sd] = Lsu{m, ssum, usum};
+      // lanes l and l ^ 32 hold the same position (interleaved ids)
+      const Lsu o{__shfl_xor(st[sd].m, 32), __shfl_xor(st[sd].s, 32), __shfl_xor(st[sd].u, 32)};
+      st[sd] = fh == 0 ? lsu_merge(st[sd], o) : lsu_merge(o, st[sd]);
+    }
+    if (wv == 1 && fh == 0) {
+#pragma unroll
+      for (int sd = 0; sd < 2; ++sd) xch[(wp * 2 + sd) * 32 + fr] = st[sd];
+    }
+    __syncthreads();
+    if (wv == 0 && fh == 0) {
+#pragma unroll
+      for (int sd = 0; sd < 2; ++sd) {
+        const int64_t pos = p0 + sd * BP + wp * 64 + pg * 32 + fr;
+        if (pos < n) {
+          const Lsu t = lsu_merge(st[sd], xch[(wp * 2 + sd) * 32 + fr]);
+          float *q = part + (int64_t)vt * npad + pos;
+          q[0] = t.m;
+          q[plane] = t.s;
+          q[2 * plane] = t.u;
+        }
       }
     }
     __syncthreads();
@@ -845,6 +981,129 @@ __global__ __launch_bounds__(TK) void fused_topk_kernel(
   }
 }
 
+// Sparse-mode preparation, one block per position: the record's 512 ids
+// sorted by (id, slot) (bitonic in LDS), a repeat of an id marked on its
+// later slots and aliased to the first, the first entry of every 256-id
+// vocabulary tile (binary search), and a flag for ids outside [0, v).
+constexpr int SK = KLD_GOLDEN_TOPK;
+
+__global__ __launch_bounds__(SK) void sparse_prep_kernel(const int32_t *__restrict__ ids,
+                                                         int64_t n, int64_t v, int64_t nvt,
+                                                         int32_t *__restrict__ sid,
+                                                         uint16_t *__restrict__ sslot,
+                                                         uint16_t *__restrict__ alias,
+                                                         uint16_t *__restrict__ rp,
+                                                         int32_t *__restrict__ bad) {
+  __shared__ uint64_t key[SK];
+  __shared__ int32_t sidl[SK];
+  __shared__ int any_bad;
+  const int64_t pos = blockIdx.x;
+  const int t = threadIdx.x;
+  if (t == 0) any_bad = 0;
+  __syncthreads();
+  const int32_t id = ids[pos * SK + t];
+  if (id < 0 || (int64_t)id >= v) any_bad = 1;
+  // order-preserving key of (signed id, slot)
+  key[t] = ((uint64_t)((uint32_t)id ^ 0x80000000u) << 32) | (uint32_t)t;
+  __syncthreads();
+  for (int size = 2; size <= SK; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (t < SK / 2) {
+        const int i = 2 * t - (t & (stride - 1));
+        const int j = i + stride;
+        const bool up = (i & size) == 0;
+        const uint64_t a = key[i], b = key[j];
+        if ((b < a) == up) {
+          key[i] = b;
+          key[j] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  const uint64_t k = key[t];
+  const int32_t my = (int32_t)((uint32_t)(k >> 32) ^ 0x80000000u);
+  const int slot = (int)(uint32_t)k;
+  sidl[t] = my;
+  __syncthreads();
+  const bool rep = t > 0 && sidl[t - 1] == my;
+  int first = t;
+  while (first > 0 && sidl[first - 1] == my) --first;
+  sid[pos * SK + t] = my;
+  sslot[pos * SK + t] = (uint16_t)(slot | (rep ? 0x8000 : 0));
+  alias[pos * SK + slot] = (uint16_t)(uint32_t)key[first];
+  for (int64_t vt = t; vt <= nvt; vt += SK) {
+    const int64_t lo_id = vt * BV;
+    int lo = 0, hi = SK;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if ((int64_t)sidl[mid] < lo_id) lo = mid + 1; else hi = mid;
+    }
+    rp[pos * (nvt + 1) + vt] = (uint16_t)lo;
+  }
+  if (t == 0) bad[pos] = any_bad;
+}
+
+// The 513-cell score of each position from the sparse-mode partial states:
+// one wave per position merges its tiles (maxima, then the sums moved to the
+// overall maximum in f64), giving lse and the candidate's unlisted mass q_T;
+// then sums p_i (lp_i - (z_i - lse)) over the 512 listed cells and
+// p_T (ln p_T - ln q_T) in f64 in a fixed order.
+__global__ __launch_bounds__(256) void sparse_finalize_kernel(
+    const float *__restrict__ part, int64_t nvt, int64_t npad, int64_t n,
+    const float *__restrict__ zl, const uint16_t *__restrict__ alias,
+    const int32_t *__restrict__ bad, const float *__restrict__ lp, const float *__restrict__ rec,
+    float *__restrict__ kl) {
+  const int64_t pos = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (pos >= n) return;
+  const int64_t plane = nvt * npad;
+  float m = kNegInf;
+  for (int64_t t = lane; t < nvt; t += 64) m = fmaxf(m, part[t * npad + pos]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  const double r = (double)ref_of(m);
+  double s = 0.0, u = 0.0;
+  for (int64_t t = lane; t < nvt; t += 64) {
+    const float mt = part[t * npad + pos];
+    if (mt == kNegInf) continue;
+    const double f = exp((double)mt - r);
+    s += (double)part[plane + t * npad + pos] * f;
+    u += (double)part[2 * plane + t * npad + pos] * f;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    s += __shfl_xor(s, o);
+    u += __shfl_xor(u, o);
+  }
+  const double lse = r + log(s);
+  const double q_t = u / s;
+  double acc = 0.0;
+  int inf = 0;
+  for (int i = lane; i < SK; i += 64) {
+    const double l = (double)lp[pos * SK + i];
+    const double p = exp(l);
+    if (p == 0.0) continue;
+    const float z = zl[pos * SK + alias[pos * SK + i]];
+    if (z == kNegInf) { inf = 1; continue; }
+    acc += p * (l - ((double)z - lse));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    acc += __shfl_xor(acc, o);
+    inf |= __shfl_xor(inf, o);
+  }
+  if (lane == 0) {
+    const double p_t = (double)rec[pos * 3 + 2];
+    if (p_t > 0.0) {
+      if (q_t == 0.0) inf = 1;
+      else acc += p_t * (log(p_t) - log(q_t));
+    }
+    const bool nan_in = bad[pos] || !(s > 0.0) || s != s || m != m || m == __builtin_huge_valf();
+    kl[pos] = nan_in ? __builtin_nanf("") : inf ? __builtin_huge_valf() : (float)acc;
+  }
+}
+
 }  // namespace
 
 FusedGeom fused_geom(int64_t n, int64_t v) {
@@ -863,13 +1122,15 @@ hipError_t launch_fused(const FusedArgs &a, const FusedWs &w) {
   e = record(a.ev.start, a.stream);
   if (e != hipSuccess) return e;
   if (tk)
-    hipLaunchKernelGGL(fused_head_kernel<true>, dim3((unsigned)nblocks), dim3(NT),
+    hipLaunchKernelGGL(fused_head_kernel<kModeTopk>, dim3((unsigned)nblocks), dim3(NT),
                        0, a.stream, a.W, a.h_ref, a.h_cand, a.v, a.d,
-                       a.n, (int)g.npt, g.npad, g.nvt, w.part, w.ckeys, w.resid, w.rinfo, w.tkeys);
+                       a.n, (int)g.npt, g.npad, g.nvt, w.part, w.ckeys, w.resid, w.rinfo, w.tkeys,
+                       SparseIn{});
   else
-    hipLaunchKernelGGL(fused_head_kernel<false>, dim3((unsigned)nblocks), dim3(NT),
+    hipLaunchKernelGGL(fused_head_kernel<kModeKl>, dim3((unsigned)nblocks), dim3(NT),
                        0, a.stream, a.W, a.h_ref, a.h_cand, a.v, a.d,
-                       a.n, (int)g.npt, g.npad, g.nvt, w.part, nullptr, nullptr, nullptr, nullptr);
+                       a.n, (int)g.npt, g.npad, g.nvt, w.part, nullptr, nullptr, nullptr, nullptr,
+                       SparseIn{});
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = record(a.ev.stop, a.stream);
@@ -887,6 +1148,36 @@ hipError_t launch_fused(const FusedArgs &a, const FusedWs &w) {
   hipLaunchKernelGGL(fused_topk_kernel, dim3((unsigned)(2 * a.n)), dim3(TK), 0, a.stream, w.ckeys,
                      w.resid, w.rinfo, w.tkeys, g.nvt, g.npad, a.n, a.W, a.h_ref, a.h_cand, a.v, a.d, w.lse,
                      a.topk);
+  return hipGetLastError();
+}
+
+SparseGeom sparse_geom(int64_t n, int64_t v) {
+  SparseGeom g;
+  g.nvt = (v + BV - 1) / BV;
+  g.npt = (n + 2 * BP - 1) / (2 * BP);
+  g.npad = g.npt * 2 * BP;
+  return g;
+}
+
+hipError_t launch_coarse_fused(const CoarseFusedArgs &a, const SparseWs &w) {
+  const SparseGeom g = sparse_geom(a.n, a.v);
+  hipLaunchKernelGGL(sparse_prep_kernel, dim3((unsigned)a.n), dim3(SK), 0, a.stream, a.ids, a.n,
+                     a.v, g.nvt, w.sid, w.sslot, w.alias, w.rp, w.bad);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = record(a.ev.start, a.stream);
+  if (e != hipSuccess) return e;
+  SparseIn sp{w.sid, w.sslot, w.rp, w.zl};
+  hipLaunchKernelGGL(fused_head_kernel<kModeSparse>, dim3((unsigned)(g.nvt * g.npt)), dim3(NT), 0,
+                     a.stream, a.W, a.h_cand, a.h_cand, a.v, a.d, a.n, (int)g.npt, g.npad, g.nvt,
+                     w.part, nullptr, nullptr, nullptr, nullptr, sp);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = record(a.ev.stop, a.stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(sparse_finalize_kernel, dim3((unsigned)((a.n + 3) / 4)), dim3(256), 0,
+                     a.stream, w.part, g.nvt, g.npad, a.n, w.zl, w.alias, w.bad, a.lp, a.rec,
+                     a.kl);
   return hipGetLastError();
 }
 

@@ -83,6 +83,32 @@ struct FusedWs {
 };
 hipError_t launch_fused(const FusedArgs &a, const FusedWs &w);
 
+// candidate hidden states scored against stored golden records through the
+// shared head (sparse mode of the fused kernel)
+struct CoarseFusedArgs {
+  const uint16_t *W, *h_cand;
+  int64_t v, d, n;
+  const int32_t *ids;
+  const float *lp, *rec;
+  float *kl;
+  hipStream_t stream;
+  Events ev;
+};
+struct SparseGeom {
+  int64_t nvt, npt, npad;   // vocabulary tiles, 256-position tiles, padded positions
+};
+SparseGeom sparse_geom(int64_t n, int64_t v);
+struct SparseWs {
+  float *part;        // 3 * nvt * npad partial-state planes (m, s, unlisted s)
+  float *zl;          // n * 512 listed logits
+  int32_t *sid;       // n * 512 listed ids sorted by id
+  uint16_t *sslot;    // n * 512 their record slots (bit 15: repeated id)
+  uint16_t *alias;    // n * 512 slot of the first occurrence of each slot's id
+  uint16_t *rp;       // n * (nvt + 1) first sorted entry of each vocabulary tile
+  int32_t *bad;       // n flags: an id outside [0, v)
+};
+hipError_t launch_coarse_fused(const CoarseFusedArgs &a, const SparseWs &w);
+
 // ---- summary ---------------------------------------------------------------
 constexpr int kSummaryMaxRanks = 32;   // two order statistics per quantile, <= 16 quantiles
 struct SummaryRanks {

@@ -83,7 +83,8 @@ enum {
   KLD_OP_TOPK_EXPORT = 2,
   KLD_OP_SUMMARY = 3,
   KLD_OP_COARSE_KL = 4,
-  KLD_OP_PAIRED = 5
+  KLD_OP_PAIRED = 5,
+  KLD_OP_COARSE_FUSED = 6
 };
 #define KLD_FLAG_TOPK 1       /* the call will also export top-64 lists */
 
@@ -258,6 +259,33 @@ kld_status kld_golden_export(const void *logits, int dtype, int64_t n, int64_t v
 kld_status kld_coarse_kl(const void *cand, int dtype, int64_t n, int64_t v, int64_t ld,
                          const int32_t *ids, const float *lp, const float *rec, int k, float *kl,
                          void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * kld_coarse_fused -- the 513-cell score of a candidate given as hidden
+ * states against golden records ("Qwen3.8-27B Quantization Challenge", "The
+ * score" and "Scoring an entry yourself": the candidate's log-softmax at every
+ * position coarsened onto the record's 512 ids plus the tail; "Qwen3.8-27B
+ * fidelity suite v5", opening paragraphs: candidate logits come from its
+ * final hidden states through the one shared BF16 head).  The logits
+ * z = W h_cand are reduced on the fly and never written to memory.
+ *
+ * W      : [v, d] bf16 head, row-major; v >= 512, d a multiple of 8.
+ * h_cand : [n, d] bf16 candidate hidden states, row-major.
+ * ids, lp, rec : golden records [n, 512] int32, [n, 512] f32, [n, 3] f32
+ *          (kld_golden_export); a repeated id in a record counts in each of
+ *          its cells, like kld_coarse_kl.
+ * k      : must be KLD_GOLDEN_TOPK.
+ * kl     : [n] f32 output: KL(p || q) over the 513 cells, q from the f32
+ *          softmax of the f32-accumulated logits, the tail cell summed
+ *          directly over the unlisted ids.  An id outside [0, v) gives NaN.
+ * ws     : kld_workspace_size(KLD_OP_COARSE_FUSED, n, v, d, 0) bytes.
+ * opts   : optional events around the head kernel, as for kld_fused_head.
+ * W and h_cand need 16-byte alignment.
+ */
+kld_status kld_coarse_fused(const uint16_t *W, int64_t v, int64_t d, const uint16_t *h_cand,
+                            int64_t n, const int32_t *ids, const float *lp, const float *rec, int k,
+                            float *kl, void *ws, size_t ws_bytes, void *stream,
+                            const kld_launch_opts *opts);
 
 /*
  * kld_window_summary -- scored-window statistics of a per-position score

@@ -217,3 +217,22 @@ def bootstrap_draws(workload: int, nrep: int, nclust: int) -> np.ndarray:
     drawn uniformly with replacement."""
     g = rng(workload, STREAM_SCORES, 4)
     return g.integers(0, nclust, (nrep, nclust)).astype(np.int32)
+
+
+def sparse_records(workload: int, n: int, v: int, k: int = 512) -> tuple:
+    """n seeded stand-in records for scoring against stored sparse
+    references: k distinct ids per row (uniform over [0, v)), f32 log-probs
+    of a random distribution over them that leaves a tail mass in [0.05, 0.6)
+    for the rest, and [n, 3] f32 (NaN, NaN, tail).  Used where every row of a
+    large launch needs a record but only sampled rows are checked."""
+    g = rng(workload, STREAM_SCORES, 5)
+    ids = np.empty((n, k), np.int32)
+    lp = np.empty((n, k), np.float32)
+    rec = np.full((n, 3), np.nan, np.float32)
+    for i in range(n):
+        ids[i] = g.choice(v, size=k, replace=False)
+        w = g.exponential(1.0, k) ** 3
+        tail = g.uniform(0.05, 0.6)
+        lp[i] = np.log(w / w.sum() * (1.0 - tail))
+        rec[i, 2] = tail
+    return ids, lp, rec

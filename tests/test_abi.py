@@ -180,3 +180,21 @@ def test_paired_bootstrap_validation_fails_closed():
                                     None) == 4
     assert lib.kld_paired_bootstrap(16, 16, 16, 8, 16, 3, 16, 10, q, 2, 16, 16, 16, 8, None) == 4
     assert kld.kld_workspace_size(5, 842, 10_000) >= 842 * 16 + 2 * 10_000 * 8
+
+
+def test_coarse_fused_validation_fails_closed():
+    lib = kld.lib()
+    big = 1 << 30
+    # kld_coarse_fused(W, v, d, h_cand, n, ids, lp, rec, k, kl, ws, ws_bytes, stream, opts)
+    assert lib.kld_coarse_fused(16, 1000, 64, 16, 4, 16, 16, 16, 100, 16, 16, big, None, None) == 2
+    assert lib.kld_coarse_fused(16, 511, 64, 16, 4, 16, 16, 16, 512, 16, 16, big, None, None) == 2
+    assert lib.kld_coarse_fused(16, 1000, 0, 16, 4, 16, 16, 16, 512, 16, 16, big, None, None) == 2
+    assert lib.kld_coarse_fused(16, 1000, 64, 16, -1, 16, 16, 16, 512, 16, 16, big, None, None) == 1
+    assert lib.kld_coarse_fused(None, 1000, 64, 16, 4, 16, 16, 16, 512, 16, 16, big, None, None) == 1
+    assert lib.kld_coarse_fused(16, 1000, 64, 16, 4, None, 16, 16, 512, 16, 16, big, None, None) == 1
+    assert lib.kld_coarse_fused(16, 1000, 60, 16, 4, 16, 16, 16, 512, 16, 16, big, None, None) == 5
+    assert lib.kld_coarse_fused(16, 1000, 64, 16, 4, 16, 16, 16, 512, 16, None, 0, None, None) == 4
+    assert lib.kld_coarse_fused(16, 1000, 64, 16, 4, 16, 16, 16, 512, 16, 16, 8, None, None) == 4
+    assert lib.kld_coarse_fused(None, 1000, 64, None, 0, None, None, None, 512, None, None, 0, None,
+                                None) == 0
+    assert kld.kld_workspace_size(6, 2047, 248_320, 5120) > 3 * 971 * 2048 * 4
