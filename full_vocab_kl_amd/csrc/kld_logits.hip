@@ -15,13 +15,14 @@
 // complemented id, so equal values rank the lower id first).  Per side, an
 // element becomes a candidate only if its value reaches a threshold that at
 // least 64 elements of the block's range are known to reach: at rounds 0, 1,
-// 3, 7, ... every wave sorts its 64 lanes' running maxima (distinct elements)
-// and publishes the 16th largest; the smallest of the four waves' values is
-// reached by 64 distinct elements.  Candidates are appended to a per-wave LDS
-// buffer (ballot + mbcnt offsets, no atomics, no block barrier); a wave whose
-// buffer fills sorts it in registers, keeps its 64 best keys and from then on
-// also requires keys above the 64th.  At the end the block radix-selects the
-// 64 best keys of the four buffers and wave 0 sorts them; topk_merge_kernel
+// 3, 7, ... every wave finds the 16th largest of its 64 lanes' running maxima
+// (distinct elements) and publishes it; the smallest of the four waves'
+// values is reached by 64 distinct elements.  Candidates are appended to a
+// per-wave LDS buffer (ballot + mbcnt offsets, no atomics, no block barrier);
+// a wave whose buffer fills sorts it in registers, keeps its 64 best keys and
+// from then on also requires keys above the 64th.  At the end each wave drops
+// the entries below the final threshold, the wave that finishes last gathers
+// the four waves' survivors and cuts them to the 64 best; topk_merge_kernel
 // (kld_topk.hip) merges the splits of a row and converts them to ids and fp16
 // log-probs.  On these inputs only a few hundred elements per row and side
 // pass the threshold, so the export costs little beyond the streaming pass.
@@ -100,6 +101,7 @@ struct TopkShared {
   u32x4 stage[2][kWaves][SCAP];       // per side and wave: staged vectors (as loaded)
   int sid[2][kWaves][SCAP];           // id of each staged vector's first element
   float bound[2][kWaves];             // per side and wave: threshold bound (nondecreasing)
+  int lcount[2][kWaves];              // per side and wave: entries in its final list
 };
 
 // Values that are equal in every lane, moved to scalar registers so that the
@@ -122,36 +124,6 @@ __device__ __forceinline__ uint64_t entry_key(uint64_t e) {
   return topk_key(__uint_as_float((uint32_t)e), (int)(e >> 32));
 }
 
-// A wave's candidate buffer (its first cnt of kWCap entries, LDS) -> its 64
-// best, sorted by key, descending, in entries 0..63; returns the 64th key
-// (cnt >= 64).  Bitonic network over keys in LDS, two compare-exchanges per
-// lane and stage; the lanes of one wave share the buffer, so the stages are
-// separated by wave-scope fences (a wave's LDS accesses complete in order).
-// Rare: only inputs with very many equal values fill a buffer.
-__device__ __attribute__((noinline)) uint64_t wave_compact(uint64_t *buf, int cnt) {
-  const int lane = threadIdx.x & 63;
-  for (int e = lane; e < kWCap; e += 64) buf[e] = e < cnt ? entry_key(buf[e]) : 0ull;
-  for (int k = 2; k <= kWCap; k <<= 1)
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      for (int i = lane; i < kWCap / 2; i += 64) {   // pair i: entries a, a + j
-        const int a = ((i & ~(j - 1)) << 1) | (i & (j - 1));
-        const bool desc = (a & k) == 0;
-        const uint64_t x = buf[a], y = buf[a + j];
-        if (desc ? x < y : x > y) { buf[a] = y; buf[a + j] = x; }
-      }
-    }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const uint64_t t64 = buf[63];
-  const uint64_t kl = buf[lane];
-  buf[lane] = make_entry(key_value(kl), key_id(kl));   // back to (value, id)
-  return t64;
-}
-
 // Two key lists of 64, one key per lane, each sorted descending: a from
 // lane order, b given reversed (lane l holds b[63 - l]).  Returns the 64
 // largest keys of both, sorted descending: the lane-wise maximum of a and
@@ -168,8 +140,40 @@ __device__ __forceinline__ uint64_t wave_merge_top64(uint64_t a, uint64_t b_rev)
   return c;
 }
 
+// The 16th largest of the wave's 64 lane values: the bits of its
+// order-preserving key are fixed from the top, each kept if at least 16 lanes
+// reach it (a ballot and a popcount per bit; no shuffles).
+__device__ __forceinline__ float wave_16th_largest(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  uint32_t pre = 0;
+#pragma unroll
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = pre | (1u << b);
+    if (__popcll(__ballot(key >= c)) >= 16) pre = c;
+  }
+  return __uint_as_float((pre & 0x80000000u) ? (pre & 0x7fffffffu) : ~pre);
+}
+
+// The 64 best keys of a wave's candidate buffer (its first cnt of kWCap
+// entries, LDS), sorted descending, one per lane (0 past cnt): each group of
+// 64 entries is sorted across the lanes and merged into the running 64 (lane
+// l of group g takes entry 64 g + l).  Registers and shuffles only; not
+// inlined, so that its registers do not add to the streaming loop's.
+static_assert(kWCap == 4 * 64, "four groups of 64 entries");
+__device__ __attribute__((noinline)) uint64_t wave_best64(const uint64_t *buf, int cnt) {
+  const int lane = threadIdx.x & 63;
+  uint64_t r = wave_sort_desc(lane < cnt ? entry_key(buf[lane]) : (uint64_t)0);
+  for (int g = 1; g < 4 && 64 * g < cnt; ++g) {   // (cnt is wave-uniform)
+    const int e = 64 * g + lane;
+    const uint64_t b = wave_sort_desc(e < cnt ? entry_key(buf[e]) : (uint64_t)0);
+    r = wave_merge_top64(r, __shfl(b, 63 - lane));
+  }
+  return r;
+}
+
 template <typename T, int VEC, int U, bool ALIGNED, bool TWO, bool TOPK>
-__global__ __launch_bounds__(kThreads) void logits_partial_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK && ALIGNED && sizeof(T) == 2 ? 3 : 1))) void logits_partial_kernel(
     const T *__restrict__ ref, const T *__restrict__ cand, int64_t ld_ref, int64_t ld_cand,
     int64_t v, int64_t chunk, int splits, RowState *__restrict__ part,
     uint64_t *__restrict__ topk_keys /*[n][splits][2][64]*/) {
@@ -251,8 +255,7 @@ __global__ __launch_bounds__(kThreads) void logits_partial_kernel(
   auto update = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int side = 0; side < NS; ++side) {
-      const float srt = wave_sort_desc(side ? mb : ma);
-      const float b16 = __shfl(srt, 15);
+      const float b16 = wave_16th_largest(side ? mb : ma);
       if (lane == 0) sh.bound[side][wave] = b16;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -287,9 +290,11 @@ __global__ __launch_bounds__(kThreads) void logits_partial_kernel(
         uint64_t m = __ballot(p);
         if (m == 0ull) continue;
         if (cnt[side] + 64 > kWCap) {
-          // buffer full: keep its 64 best, filter this element again
-          const uint64_t t64 = wave_compact(wbuf, cnt[side]);
-          tkey[side] = uniform_u64(t64);
+          // buffer full: keep its 64 best, filter this element again (each
+          // lane reads its four entries before any lane writes)
+          const uint64_t kb = wave_best64(wbuf, cnt[side]);
+          wbuf[lane] = make_entry(key_value(kb), key_id(kb));
+          tkey[side] = uniform_u64(__shfl(kb, 63));
           cnt[side] = 64;
           thr[side] = uniform_f(fmaxf(thr[side], key_value(tkey[side])));
           p = p && topk_key(x, id) > tkey[side];
@@ -452,22 +457,40 @@ __global__ __launch_bounds__(kThreads) void logits_partial_kernel(
   }
 
   if constexpr (TOPK) {
-    // last threshold from the final maxima, remaining staged vectors, then
-    // each wave sorts its own 64 best
+    // Last threshold from the final maxima and the remaining staged
+    // vectors.  At least 64 elements of the range reach the threshold, so
+    // the range's top 64 do too: entries below it are dropped (most of the
+    // buffer, whose early entries met lower thresholds).  The survivors --
+    // cut to the wave's 64 best only when more remain -- form the wave's
+    // list in its staging area, which is free now.
     update();
 #pragma unroll
     for (int side = 0; side < NS; ++side) {
       flush(side);
       uint64_t *wbuf = sh.buf[side][wave];
-      uint64_t k;
-      if (cnt[side] <= 64) {
-        k = wave_sort_desc(lane < cnt[side] ? entry_key(wbuf[lane]) : (uint64_t)0);
-      } else {
-        wave_compact(wbuf, cnt[side]);   // entries 0..63 become its 64 best, sorted
-        k = entry_key(wbuf[lane]);
+      const float th = uniform_f(thr[side]);
+      int n2 = 0;
+      for (int g = 0; g < kWCap / 64 && 64 * g < cnt[side]; ++g) {
+        // compacting forward: an entry moves to an index at most its own,
+        // and every lane has read its group's entry before any lane writes
+        const int e = 64 * g + lane;
+        const uint64_t en = e < cnt[side] ? wbuf[e] : 0ull;
+        const bool keep = e < cnt[side] && __uint_as_float((uint32_t)en) >= th;
+        const uint64_t m = __ballot(keep);
+        const int at = n2 + (int)__builtin_amdgcn_mbcnt_hi(
+            (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (keep) wbuf[at] = en;
+        n2 += __popcll(m);
       }
-      // the wave's staging area of this side is free now: it takes the list
-      reinterpret_cast<uint64_t *>(sh.stage[side][wave])[lane] = k;
+      uint64_t *lst = reinterpret_cast<uint64_t *>(sh.stage[side][wave]);
+      if (n2 > 64) {
+        const uint64_t k = wave_best64(wbuf, n2);
+        lst[lane] = make_entry(key_value(k), key_id(k));
+        n2 = 64;
+      } else if (lane < n2) {
+        lst[lane] = wbuf[lane];
+      }
+      if (lane == 0) sh.lcount[side][wave] = n2;
     }
   }
   RowState s;
@@ -503,12 +526,20 @@ __global__ __launch_bounds__(kThreads) void logits_partial_kernel(
     part[row * splits + split] = r;
   }
   if constexpr (TOPK) {
+    // the four waves' lists (at most 256 entries) gathered into this wave's
+    // own candidate buffer, then cut to the range's 64 best
 #pragma unroll
     for (int side = 0; side < NS; ++side) {
-      auto list = [&](int w) { return reinterpret_cast<const volatile uint64_t *>(sh.stage[side][w]); };
-      uint64_t k = list(0)[lane];
+      uint64_t *scr = sh.buf[side][wave];
+      int nt = 0;
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) k = wave_merge_top64(k, list(w)[63 - lane]);
+      for (int w = 0; w < kWaves; ++w) {
+        const int c = reinterpret_cast<const volatile int *>(sh.lcount[side])[w];
+        const volatile uint64_t *lst = reinterpret_cast<const volatile uint64_t *>(sh.stage[side][w]);
+        if (lane < c) scr[nt + lane] = lst[lane];
+        nt += c;
+      }
+      const uint64_t k = wave_best64(scr, nt);
       topk_keys[((row * splits + split) * 2 + side) * 64 + lane] = k;
     }
   }
