@@ -140,19 +140,30 @@ __device__ __forceinline__ uint64_t wave_merge_top64(uint64_t a, uint64_t b_rev)
   return c;
 }
 
-// The 16th largest of the wave's 64 lane values: the bits of its
-// order-preserving key are fixed from the top, each kept if at least 16 lanes
-// reach it (a ballot and a popcount per bit; no shuffles).
-__device__ __forceinline__ float wave_16th_largest(float x) {
+// A lower bound of the 16th largest of the wave's 64 lane values, exact to
+// the top 16 bits of its order-preserving key (all of a bf16 value): the
+// bits are fixed from the top, each kept if at least 16 lanes reach it (a
+// ballot and a popcount per bit; no shuffles).  Two values per lane (the two
+// sides) are searched together, so the two dependency chains overlap.
+__device__ __forceinline__ uint32_t order_key(float x) {
   const uint32_t u = __float_as_uint(x);
-  const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  uint32_t pre = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+__device__ __forceinline__ void wave_16th_bound2(float x, float y, float &bx, float &by) {
+  const uint32_t kx = order_key(x), ky = order_key(y);
+  uint32_t px = 0, py = 0;
 #pragma unroll
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t c = pre | (1u << b);
-    if (__popcll(__ballot(key >= c)) >= 16) pre = c;
+  for (int b = 31; b >= 16; --b) {
+    const uint32_t cx = px | (1u << b), cy = py | (1u << b);
+    const int nx = __popcll(__ballot(kx >= cx)), ny = __popcll(__ballot(ky >= cy));
+    px = nx >= 16 ? cx : px;
+    py = ny >= 16 ? cy : py;
   }
-  return __uint_as_float((pre & 0x80000000u) ? (pre & 0x7fffffffu) : ~pre);
+  bx = key_float(px);
+  by = key_float(py);
 }
 
 // The 64 best keys of a wave's candidate buffer (its first cnt of kWCap
@@ -160,8 +171,11 @@ __device__ __forceinline__ float wave_16th_largest(float x) {
 // 64 entries is sorted across the lanes and merged into the running 64 (lane
 // l of group g takes entry 64 g + l).  Registers and shuffles only; not
 // inlined, so that its registers do not add to the streaming loop's.
+template <typename X> using Lds = __attribute__((address_space(3))) X *;
+template <typename X> __device__ __forceinline__ Lds<X> lds(X *p) { return (Lds<X>)p; }
+
 static_assert(kWCap == 4 * 64, "four groups of 64 entries");
-__device__ __attribute__((noinline)) uint64_t wave_best64(const uint64_t *buf, int cnt) {
+__device__ __attribute__((noinline)) uint64_t wave_best64(Lds<const uint64_t> buf, int cnt) {
   const int lane = threadIdx.x & 63;
   uint64_t r = wave_sort_desc(lane < cnt ? entry_key(buf[lane]) : (uint64_t)0);
   for (int g = 1; g < 4 && 64 * g < cnt; ++g) {   // (cnt is wave-uniform)
@@ -170,6 +184,61 @@ __device__ __attribute__((noinline)) uint64_t wave_best64(const uint64_t *buf, i
     r = wave_merge_top64(r, __shfl(b, 63 - lane));
   }
   return r;
+}
+
+// Per side and wave: the value threshold, the key threshold (0 = none) and
+// the number of entries in the wave's candidate buffer.
+struct CandState {
+  uint64_t tkey;
+  float thr;
+  int cnt;
+};
+
+// Filter a wave's scnt staged vectors (as loaded, with the id of each one's
+// first element) against the threshold -- and the key threshold after a
+// compaction -- and append the elements that pass to its candidate buffer,
+// one element per lane at a time.  A full buffer is cut to its 64 best, which
+// sets the key threshold.  (Inlined: as a call it costs more in saved
+// registers than its copies cost in code.)
+template <typename T, int VEC>
+__device__ __forceinline__ CandState topk_flush(Lds<uint64_t> wbuf, Lds<const u32x4> stage,
+                                                Lds<const int> sid, int scnt, int64_t hi,
+                                                CandState st) {
+  using Raw = typename RawOf<T>::type;
+  const int lane = threadIdx.x & 63;
+  const float th = uniform_f(st.thr);
+  for (int b0 = 0; b0 < scnt; b0 += 64) {
+    const int e = b0 + lane;
+    const bool ok = e < scnt;
+    const Raw q = __builtin_bit_cast(Raw, ok ? stage[e] : u32x4{0u, 0u, 0u, 0u});
+    const int bid = ok ? sid[e] : 0;
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+      const float x = elem(q, j);
+      const int id = bid + j;
+      bool p = ok && x >= th && (int64_t)id < hi;
+      if (st.tkey != 0ull) p = p && topk_key(x, id) > st.tkey;
+      uint64_t m = __ballot(p);
+      if (m == 0ull) continue;
+      if (st.cnt + 64 > kWCap) {
+        // buffer full: keep its 64 best, filter this element again (each
+        // lane reads its four entries before any lane writes)
+        const uint64_t kb = wave_best64(wbuf, st.cnt);
+        wbuf[lane] = make_entry(key_value(kb), key_id(kb));
+        st.tkey = uniform_u64(__shfl(kb, 63));
+        st.cnt = 64;
+        st.thr = uniform_f(fmaxf(st.thr, key_value(st.tkey)));
+        p = p && topk_key(x, id) > st.tkey;
+        m = __ballot(p);
+        if (m == 0ull) continue;
+      }
+      const int at = st.cnt + (int)__builtin_amdgcn_mbcnt_hi(
+          (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      if (p) wbuf[at] = make_entry(x, id);
+      st.cnt += __popcll(m);
+    }
+  }
+  return st;
 }
 
 template <typename T, int VEC, int U, bool ALIGNED, bool TWO, bool TOPK>
@@ -185,7 +254,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
   const T *rb = TWO ? cand + row * ld_cand : ra;
   constexpr int NS = TWO ? 2 : 1;
 
-  constexpr int kSCap = 128;
+  constexpr int kSCap = 64 * U > 192 ? 64 * U : 192;   // staged vectors per wave and side
+  static_assert(kSCap >= 64 * U, "a round's vectors fit after a flush");
   __shared__ TopkShared<kSCap> sh_storage[1];
   TopkShared<kSCap> &sh = sh_storage[0];
   __shared__ RowState waves[kWaves];
@@ -253,12 +323,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
   // latest values, which at least 64 elements reach.  Published values only
   // grow, so reading another wave's older value is still valid: no barrier.
   auto update = [&]() __attribute__((always_inline)) {
+    float b16[2];
+    wave_16th_bound2(ma, mb, b16[0], b16[1]);   // (mb unused with one side)
+    // no fence: another wave may read an older (smaller) value, which is
+    // still valid, and a fence here would also wait for this wave's
+    // prefetched row loads
 #pragma unroll
-    for (int side = 0; side < NS; ++side) {
-      const float b16 = wave_16th_largest(side ? mb : ma);
-      if (lane == 0) sh.bound[side][wave] = b16;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    for (int side = 0; side < NS; ++side)
+      if (lane == 0) reinterpret_cast<volatile float *>(sh.bound[side])[wave] = b16[side];
 #pragma unroll
     for (int side = 0; side < NS; ++side) {
       const volatile float *bd = sh.bound[side];
@@ -269,44 +341,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
     }
   };
 
-  // Filter the wave's staged vectors against the current threshold (and key
-  // threshold, after a compaction) and append the elements that pass, one
-  // element per lane at a time.
+  // Filter the wave's staged vectors of one side (topk_flush).
   auto flush = [&](int side) {
-    const float th = uniform_f(thr[side]);
-    uint64_t *wbuf = sh.buf[side][wave];
-    for (int b0 = 0; b0 < scnt[side]; b0 += 64) {
-      const int e = b0 + lane;
-      const bool ok = e < scnt[side];
-      const Raw q = __builtin_bit_cast(Raw, ok ? sh.stage[side][wave][e] : u32x4{0u, 0u, 0u, 0u});
-      const int bid = ok ? sh.sid[side][wave][e] : 0;
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) {
-        const float x = elem(q, j);
-        const int id = bid + j;
-        bool p = ok && x >= th && (int64_t)id < hi;
-        const uint64_t tk = tkey[side];
-        if (tk != 0ull) p = p && topk_key(x, id) > tk;
-        uint64_t m = __ballot(p);
-        if (m == 0ull) continue;
-        if (cnt[side] + 64 > kWCap) {
-          // buffer full: keep its 64 best, filter this element again (each
-          // lane reads its four entries before any lane writes)
-          const uint64_t kb = wave_best64(wbuf, cnt[side]);
-          wbuf[lane] = make_entry(key_value(kb), key_id(kb));
-          tkey[side] = uniform_u64(__shfl(kb, 63));
-          cnt[side] = 64;
-          thr[side] = uniform_f(fmaxf(thr[side], key_value(tkey[side])));
-          p = p && topk_key(x, id) > tkey[side];
-          m = __ballot(p);
-          if (m == 0ull) continue;
-        }
-        const int at = cnt[side] + (int)__builtin_amdgcn_mbcnt_hi(
-            (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        if (p) wbuf[at] = make_entry(x, id);
-        cnt[side] += __popcll(m);
-      }
-    }
+    CandState st{tkey[side], thr[side], cnt[side]};
+    st = topk_flush<T, VEC>(lds(sh.buf[side][wave]), lds<const u32x4>(sh.stage[side][wave]),
+                            lds<const int>(sh.sid[side][wave]), scnt[side], hi, st);
+    tkey[side] = uniform_u64(st.tkey);
+    thr[side] = uniform_f(st.thr);
+    cnt[side] = __builtin_amdgcn_readfirstlane(st.cnt);
     scnt[side] = 0;
   };
 
@@ -360,15 +402,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
 #pragma unroll
       for (int side = 0; side < NS; ++side) {
         const float th = uniform_f(thr[side]);
+        bool c[U];
+        uint64_t any = 0ull;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const bool c = (side ? vmb[u] : vma[u]) >= th;
-          const uint64_t m = __ballot(c);
+          c[u] = (side ? vmb[u] : vma[u]) >= th;
+          any |= __ballot(c[u]);
+        }
+        if (any == 0ull) continue;
+        if (scnt[side] + 64 * U > kSCap) flush(side);   // room for this round's vectors
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint64_t m = __ballot(c[u]);
           if (m == 0ull) continue;
-          if (scnt[side] + 64 > kSCap) flush(side);
           const int at = scnt[side] + (int)__builtin_amdgcn_mbcnt_hi(
               (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-          if (c) {
+          if (c[u]) {
             sh.stage[side][wave][at] = __builtin_bit_cast(u32x4, side ? cb[u] : ca[u]);
             sh.sid[side][wave][at] = id0 + u * kStride;
           }
@@ -484,7 +533,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
       }
       uint64_t *lst = reinterpret_cast<uint64_t *>(sh.stage[side][wave]);
       if (n2 > 64) {
-        const uint64_t k = wave_best64(wbuf, n2);
+        const uint64_t k = wave_best64(lds<const uint64_t>(wbuf), n2);
         lst[lane] = make_entry(key_value(k), key_id(k));
         n2 = 64;
       } else if (lane < n2) {
@@ -539,7 +588,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
         if (lane < c) scr[nt + lane] = lst[lane];
         nt += c;
       }
-      const uint64_t k = wave_best64(scr, nt);
+      const uint64_t k = wave_best64(lds<const uint64_t>(scr), nt);
       topk_keys[((row * splits + split) * 2 + side) * 64 + lane] = k;
     }
   }
