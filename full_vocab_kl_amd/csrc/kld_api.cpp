@@ -321,7 +321,7 @@ kld_status kld_paired_bootstrap(const double *sum_a, const double *sum_b, const 
                                 int nq, double *replicates, double *out, void *ws,
                                 size_t ws_bytes, void *stream) {
   if (nctx < 0 || nclust < 0 || nrep < 0 || nq < 0) return KLD_EINVAL;
-  if (nq > KLD_MAX_QUANTILES || nrep > KLD_MAX_REPLICATES || nclust > (1LL << 30))
+  if (nq > KLD_MAX_QUANTILES || nrep > KLD_MAX_REPLICATES || nclust > (1LL << 28))
     return KLD_ESHAPE;
   if (nrep > 0 && nclust == 0) return KLD_ESHAPE;
   if (!out || (nctx > 0 && (!sum_a || !sum_b || !count || !cluster)) ||

@@ -58,12 +58,14 @@ __global__ __launch_bounds__(PT) void paired_cluster_kernel(
   if (k < nclust) {
     double d = 0.0;
     long long c = 0;
+    // loads unconditional, the contribution masked: no branch around a load
 #pragma unroll 4
     for (int64_t i = threadIdx.x; i < nctx; i += PT) {
-      if (cluster[i] == k) {
-        d += sum_a[i] - sum_b[i];
-        c += count[i];
-      }
+      const bool in = cluster[i] == k;
+      const double x = sum_a[i] - sum_b[i];
+      const int64_t n = count[i];
+      d += in ? x : 0.0;
+      c += in ? n : 0;
     }
     d = block_sum(d, rd);
     c = block_sum(c, ri);
@@ -115,19 +117,25 @@ __global__ __launch_bounds__(RW * 64) void paired_replicate_kernel(
   double num = 0.0;
   long long den = 0;
   int bad = 0;
-  for (int64_t i0 = lane; i0 < nclust; i0 += 64 * 4) {
+  // draws through a buffer resource (past the row: 0, no memory touched) and
+  // gathers at clamped indices, contributions masked: no branch around a load
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t *>(dr), (short)0, (int)(nclust * 4), 0x00020000);
+  for (int i0 = lane; i0 < nclust; i0 += 64 * 4) {
     int32_t k[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) k[u] = i0 + 64 * u < nclust ? dr[i0 + 64 * u] : 0;
+    for (int u = 0; u < 4; ++u)
+      k[u] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, (i0 + 64 * u) * 4, 0, 0);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      if (i0 + 64 * u >= nclust) continue;
-      if (k[u] < 0 || k[u] >= nclust) {
-        bad = 1;
-      } else {
-        num += clus_diff[k[u]];
-        den += clus_count[k[u]];
-      }
+      const bool in = i0 + 64 * u < nclust;
+      const bool ok = k[u] >= 0 && k[u] < nclust;
+      const int32_t kk = ok ? k[u] : 0;
+      const double x = clus_diff[kk];
+      const long long n = clus_count[kk];
+      bad |= (in && !ok) ? 1 : 0;
+      num += (in && ok) ? x : 0.0;
+      den += (in && ok) ? n : 0;
     }
   }
 #pragma unroll

@@ -49,21 +49,29 @@ __global__ __launch_bounds__(WT) void window_seg_kernel(
   unsigned int c[KLD_MAX_THRESHOLDS];
 #pragma unroll
   for (int t = 0; t < KLD_MAX_THRESHOLDS; ++t) c[t] = 0u;
-  for (int64_t j0 = s + threadIdx.x; j0 < b; j0 += WT * WU) {
+  // Loads go through a buffer resource over [s, b): offsets past it read 0
+  // and touch no memory, so the loop has no branch around a load (a branch
+  // would make every load wait for the one before).  Segments are read in
+  // pieces of at most 2^28 positions so that byte offsets fit 31 bits.
+  for (int64_t p0 = s; p0 < b; p0 += (int64_t)1 << 28) {
+  const int64_t pn = b - p0 < ((int64_t)1 << 28) ? b - p0 : ((int64_t)1 << 28);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float *>(kl + p0), (short)0, (int)(pn * 4), 0x00020000);
+  for (int j0 = threadIdx.x; j0 < pn; j0 += WT * WU) {
     float x[WU];
 #pragma unroll
-    for (int u = 0; u < WU; ++u) {
-      const int64_t j = j0 + (int64_t)u * WT;
-      x[u] = j < b ? __builtin_nontemporal_load(kl + j) : 0.f;
-    }
+    for (int u = 0; u < WU; ++u)
+      x[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                 rs, (j0 + u * WT) * 4, 0, 2 /* streaming */));
 #pragma unroll
     for (int u = 0; u < WU; ++u) {
-      const bool in = j0 + (int64_t)u * WT < b;
+      const bool in = j0 + u * WT < pn;
       acc += (double)x[u];
 #pragma unroll
       for (int t = 0; t < KLD_MAX_THRESHOLDS; ++t)
         c[t] += (t < thr.count && in && x[u] > thr.value[t]) ? 1u : 0u;
     }
+  }
   }
   acc = wave_sum_f64(acc);
   if (lane == 0) wsum[wave] = acc;
@@ -101,13 +109,19 @@ __global__ __launch_bounds__(TT) void window_total_kernel(
   unsigned long long c[KLD_MAX_THRESHOLDS + 1];
 #pragma unroll
   for (int t = 0; t <= KLD_MAX_THRESHOLDS; ++t) c[t] = 0ull;
-#pragma unroll 2
+  // every load unconditional (a clamped, valid index) so that an
+  // iteration's loads are all in flight at once
   for (int64_t i = threadIdx.x; i < nseg; i += TT) {
     acc += seg_sum[i];
     c[KLD_MAX_THRESHOLDS] += (unsigned long long)seg_count[i];
+    if (nthr > 0) {
+      const int64_t *row = seg_exceed + i * nthr;
+      int64_t e[KLD_MAX_THRESHOLDS];
 #pragma unroll
-    for (int t = 0; t < KLD_MAX_THRESHOLDS; ++t)
-      if (t < nthr) c[t] += (unsigned long long)seg_exceed[i * nthr + t];
+      for (int t = 0; t < KLD_MAX_THRESHOLDS; ++t) e[t] = row[t < nthr ? t : 0];
+#pragma unroll
+      for (int t = 0; t < KLD_MAX_THRESHOLDS; ++t) c[t] += t < nthr ? (unsigned long long)e[t] : 0ull;
+    }
   }
   acc = wave_sum_f64(acc);
   if (lane == 0) wsum[wave] = acc;

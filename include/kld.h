@@ -333,7 +333,7 @@ kld_status kld_window_summary(const float *kl, int64_t n, const int64_t *offsets
  *                kld_window_summary on each candidate's scores).
  * count        : [nctx] int64 (device): scored positions per context.
  * cluster      : [nctx] int32 (device): source cluster of each context,
- *                in [0, nclust).
+ *                in [0, nclust), nclust <= 2^28.
  * draws        : [nrep, nclust] int32 (device), row-major: replicate r uses
  *                the clusters draws[r][0..nclust-1], drawn by the caller
  *                uniformly with replacement.
