@@ -19,6 +19,8 @@
 // tail keeps its relative accuracy).  The finalize kernel merges a row's
 // ranges in order (f64), gathers the 512 listed logits and sums the cells in
 // f64 in a fixed order, one wave per row.
+#include <type_traits>
+
 #include "kld.h"
 #include "kld_device.hpp"
 #include "kld_launch.hpp"
@@ -291,7 +293,8 @@ __global__ __launch_bounds__(GT) void coarse_partial_kernel(
   const int64_t lo = (int64_t)split * chunk;
   const int64_t hi = lo + chunk < v ? lo + chunk : v;
   const T *r = cand + row * ld;
-  for (int w = (int)threadIdx.x; w < CMAXW; w += GT) listed[w] = 0u;
+  const int nw = (int)((hi - lo + 31) >> 5);   // bitmap words of this range
+  for (int w = (int)threadIdx.x; w < nw; w += GT) listed[w] = 0u;
   __syncthreads();
   for (int i = (int)threadIdx.x; i < GK; i += GT) {
     const int32_t id = ids[row * GK + i];
@@ -305,11 +308,44 @@ __global__ __launch_bounds__(GT) void coarse_partial_kernel(
   constexpr int64_t kStride = (int64_t)GT * VEC;
   LseState st{kNegInf, 0.0, 0.0, 0.0};
   const int64_t rounds = (hi - lo + kStride * U - 1) / (kStride * U);
+  // Aligned rows: the whole vectors of [lo, hi) are read through a buffer
+  // resource (vectors past it read 0 and touch no memory), so a round's loads
+  // carry no branch and are all in flight together; elements past hi become
+  // -inf and a vector straddling hi is completed element by element.
+  const int len = (int)(hi - lo);   // a range spans at most 131,072 ids
+  const int nvec = len / VEC * VEC;
+  __amdgpu_buffer_rsrc_t rs;
+  if constexpr (ALIGNED)
+    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(r + lo), (short)0,
+                                           nvec * (int)sizeof(T), 0x00020000);
   for (int64_t rd = 0; rd < rounds; ++rd) {
     const int64_t base = lo + rd * kStride * U + (int64_t)threadIdx.x * VEC;
     float x[U][VEC];
+    if constexpr (ALIGNED) {
+      typedef typename std::conditional<sizeof(T) == 4, f32x4, u32x4>::type Raw;
+      Raw q[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) load_vecn<T, VEC, ALIGNED>(r, base + u * kStride, hi, x[u]);
+      for (int u = 0; u < U; ++u)
+        q[u] = __builtin_bit_cast(Raw, __builtin_amdgcn_raw_buffer_load_b128(
+                   rs, (int)(base + u * kStride - lo) * (int)sizeof(T), 0, 2 /* streaming */));
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          if constexpr (sizeof(T) == 4) x[u][e] = q[u][e];
+          else x[u][e] = __uint_as_float((e & 1) ? (q[u][e >> 1] & 0xffff0000u) : (q[u][e >> 1] << 16));
+        }
+        const int64_t p = base + u * kStride;
+        if (p + VEC > hi) {   // the last vectors of the range only
+#pragma unroll
+          for (int e = 0; e < VEC; ++e)
+            x[u][e] = p + e < hi ? (p - lo >= nvec ? ld_f32(r, p + e) : x[u][e]) : kNegInf;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) load_vecn<T, VEC, false>(r, base + u * kStride, hi, x[u]);
+    }
     float bm = kNegInf;
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -406,6 +442,7 @@ hipError_t launch_golden_export(const void *logits, int dtype, int64_t n, int64_
 
 CoarseGeom coarse_geom(int64_t n, int64_t v) {
   // ranges of at most 131,072 ids, a multiple of 256, and about 2048 blocks
+  // (more, smaller ranges measured slower: each adds a partial state to merge)
   int64_t want = n > 0 ? (2048 + n - 1) / n : 1;
   const int64_t min_splits = (v + 131071) / 131072;
   const int64_t max_splits = (v + 4095) / 4096;
