@@ -184,10 +184,16 @@ __global__ __launch_bounds__(GT) void golden_export_kernel(
 
   LseState st{kNegInf, 0.0, 0.0, 0.0};
   const int64_t rounds = (v + GROUND - 1) / GROUND;
+  // each round's elements are loaded one round ahead, so the loads are in
+  // flight while the previous round is processed (and waits at its barrier)
+  float xn[GE];
+  load_run<T, ALIGNED>(r, (int64_t)threadIdx.x * GE, v, xn);
   for (int64_t rd = 0; rd < rounds; ++rd) {
     const int64_t pos = rd * GROUND + (int64_t)threadIdx.x * GE;
     float x[GE];
-    load_run<T, ALIGNED>(r, pos, v, x);
+#pragma unroll
+    for (int e = 0; e < GE; ++e) x[e] = xn[e];
+    if (rd + 1 < rounds) load_run<T, ALIGNED>(r, pos + GROUND, v, xn);
     float bm = kNegInf;
 #pragma unroll
     for (int e = 0; e < GE; ++e) bm = fmaxf(bm, x[e]);
@@ -232,10 +238,13 @@ __global__ __launch_bounds__(GT) void golden_export_kernel(
   }
   // second pass: the mass of every id outside the GK listed ones
   double tail = 0.0;
+  load_run<T, ALIGNED>(r, (int64_t)threadIdx.x * GE, v, xn);
   for (int64_t rd = 0; rd < rounds; ++rd) {
     const int64_t pos = rd * GROUND + (int64_t)threadIdx.x * GE;
     float x[GE];
-    load_run<T, ALIGNED>(r, pos, v, x);
+#pragma unroll
+    for (int e = 0; e < GE; ++e) x[e] = xn[e];
+    if (rd + 1 < rounds) load_run<T, ALIGNED>(r, pos + GROUND, v, xn);
     float pt = 0.f;
 #pragma unroll
     for (int e = 0; e < GE; ++e) {
