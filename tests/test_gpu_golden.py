@@ -164,3 +164,27 @@ def test_coarse_kl_edges():
     want0 = oracle.coarse_kl_row(rec["ids"][0], rec["lp"][0], float(rec["rec"][0][2]), b[0].astype(np.float64))
     assert abs(got[0] - want0) <= 1e-6      # the candidate is the reference: only rounding of lp
     assert got[1] == np.inf and np.isnan(got[2]) and np.isnan(got[3])
+
+
+def test_golden_workload_launch_sampled():
+    """The golden workload as timed: records of all 512 f32 reference rows at
+    V = 248,320 in one call, then the 513-cell score of all 512 candidate
+    rows in one call.  Six seeded rows are checked: their records against the
+    oracle's, and their scores computed from the oracle's records (written
+    over the GPU's on those rows) against the oracle's scores."""
+    need_gpu()
+    n, v = 512, synth.VOCAB
+    a, b = synth.logit_rows(synth.LOGITS_F32, range(n), v)
+    t = synth.targets(synth.LOGITS_F32, range(n), v)
+    got = _run_export(a, False, t)
+    rows = synth.subset(synth.LOGITS_F32, n, 6)
+    want = oracle.golden_rows(a[rows].astype(np.float64), t[rows])
+    _check_records({k: x[rows] for k, x in got.items()}, want, "512 rows")
+    ids, lp, rec = got["ids"].copy(), got["lp"].copy(), got["rec"].copy()
+    ids[rows], lp[rows], rec[rows] = want["ids"], want["lp"], want["rec"]
+    score = kld.kld_coarse_kl(to_dev(b), to_dev(ids), to_dev(lp), to_dev(rec))
+    torch.cuda.synchronize()
+    score = score.cpu().numpy()
+    ws = oracle.coarse_kl_rows(want["ids"], want["lp"], want["rec"], b[rows].astype(np.float64))
+    _score_close(score[rows], ws, "512 rows")
+    assert np.all(np.isfinite(score)) and np.all(score > 0)

@@ -106,3 +106,12 @@ def test_bad_offsets_give_nan():
     assert np.isnan(got["totals"][0])
     got = _run(x, np.array([0, 1001], np.int64), 0)             # past the end
     assert np.isnan(got["seg_sum"][0]) and np.isnan(got["totals"][0])
+
+
+def test_ten_shard_launch():
+    """The aggregation workload as timed: 10,480,640 positions in 5,120
+    contexts of 2,047, seven thresholds, every segment against the oracle."""
+    n = 5120 * 2047
+    x, _ = synth.kl_score_pair(synth.LOGITS_F32, n)
+    offsets = np.arange(0, n + 1, 2047, dtype=np.int64)
+    _check(x, offsets, 0, where="ten-shard layout")
