@@ -198,3 +198,15 @@ def test_coarse_fused_validation_fails_closed():
     assert lib.kld_coarse_fused(None, 1000, 64, None, 0, None, None, None, 512, None, None, 0, None,
                                 None) == 0
     assert kld.kld_workspace_size(6, 2047, 248_320, 5120) > 3 * 971 * 2048 * 4
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built library every entry point raises: there is no other
+    path to the results."""
+    from full_vocab_kl_amd import binding
+    monkeypatch.setattr(binding, "_LIB", None)
+    monkeypatch.setattr(binding, "library_path", lambda: str(tmp_path / "libkld.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.lib()
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.kld_workspace_size(0, 4, 1000)
