@@ -582,8 +582,8 @@ def _cores():
 def main():
     args = _args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build scores on exactly one GPU; multi-GPU runs are not part of it "
-              "(see the sharding notes in DESIGN.md)", file=sys.stderr)
+        print("bench.py: libkld scores on one GPU; --gpus must be 1 (sharding positions over "
+              "several GPUs is not implemented)", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():

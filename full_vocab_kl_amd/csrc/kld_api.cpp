@@ -127,7 +127,7 @@ const char *kld_status_str(int s) {
     case KLD_ESHAPE: return "KLD_ESHAPE: inconsistent sizes";
     case KLD_EDTYPE: return "KLD_EDTYPE: unknown dtype";
     case KLD_EWORKSPACE: return "KLD_EWORKSPACE: workspace missing or too small";
-    case KLD_EUNSUPPORTED: return "KLD_EUNSUPPORTED: request not served by this build";
+    case KLD_EUNSUPPORTED: return "KLD_EUNSUPPORTED: valid request the library does not serve";
     case KLD_EHIP: return "KLD_EHIP: HIP runtime error";
     default: return "KLD_UNKNOWN";
   }
