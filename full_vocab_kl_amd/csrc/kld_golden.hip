@@ -145,28 +145,60 @@ struct GoldenShared {
   LseState xw[GT / 64];
   uint64_t thr;
   int cnt;
+  int cut;                      // the buffer has been cut to its GK best
+  int kept;                     // keys kept by a cut
+  int wcnt[GT / 64];            // per wave: keys at or above a trial prefix
+  uint32_t wthr[GT / 64];       // per wave: sampled threshold value
   __align__(8) uint32_t sel[6];
 };
 
-// Keep the GK best keys of the buffer (sorted order is not needed here).
+// Cut the candidate buffer to its GK best keys (distinct; 0 = none) and make
+// the GK-th the threshold.  The GK-th key is found bit by bit from the top:
+// a bit is kept if at least GK keys reach the prefix (each thread counts its
+// keys, a butterfly sums a wave's counts, LDS the four waves').  No
+// histogram: keys that share their high bits would pile onto one bin.
 __device__ void golden_compact(GoldenShared &sh) {
   uint64_t k[GCAP / GT];
   const int cnt = sh.cnt;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int q = 0; q < GCAP / GT; ++q) {
     const int e = q * GT + (int)threadIdx.x;
     k[q] = e < cnt ? sh.buf[e] : 0ull;
   }
+  uint64_t t = 0;   // stays 0 when fewer than GK keys exist: all are kept
+  if (cnt > GK) {
+    for (int b = 63; b >= 0; --b) {
+      const uint64_t c = t | (1ull << b);
+      int n = 0;
+#pragma unroll
+      for (int q = 0; q < GCAP / GT; ++q) n += k[q] >= c ? 1 : 0;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) n += __shfl_xor(n, o);
+      if (lane == 0) sh.wcnt[wave] = n;
+      __syncthreads();
+      int tot = 0;
+#pragma unroll
+      for (int w = 0; w < GT / 64; ++w) tot += sh.wcnt[w];
+      __syncthreads();
+      if (tot >= GK) t = c;
+    }
+  }
+  // the kept keys (exactly GK when t > 0) in any order, then zeros
+  if (threadIdx.x == 0) sh.kept = 0;
   __syncthreads();
-  const uint64_t t = block_select_top<GCAP / GT, GK>(k, sh.top, sh.hist, sh.sel);
-  // top holds the selected keys first, then zeros
-  for (int i = (int)threadIdx.x; i < GK; i += GT) sh.buf[i] = sh.top[i];
+#pragma unroll
+  for (int q = 0; q < GCAP / GT; ++q)
+    if (k[q] != 0ull && k[q] >= t) sh.top[atomicAdd(&sh.kept, 1)] = k[q];
+  __syncthreads();
+  const int kept = sh.kept;
+  for (int i = kept + (int)threadIdx.x; i < GK; i += GT) sh.top[i] = 0ull;
+  for (int i = (int)threadIdx.x; i < kept; i += GT) sh.buf[i] = sh.top[i];
+  __syncthreads();
   if (threadIdx.x == 0) {
-    int kept = 0;
-    while (kept < GK && sh.top[kept] != 0ull) ++kept;
     sh.cnt = kept;
-    // GK keys at or above t exist, so no other key below or at t can be
-    // among the GK best (keys are distinct)
+    // GK keys at or above t exist, so no other key below t can be among
+    // the GK best (keys are distinct)
     if (t != 0ull) sh.thr = t;
   }
   __syncthreads();
@@ -179,8 +211,43 @@ __global__ __launch_bounds__(GT) void golden_export_kernel(
   __shared__ GoldenShared sh;
   const int64_t row = blockIdx.x;
   const T *r = logits + row * ld;
-  if (threadIdx.x == 0) { sh.cnt = 0; sh.thr = 0ull; }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // Starting threshold from a sample of the row: 16 evenly spread ids per
+  // thread; each wave takes the value of the 5th best key of its 1,024 (a
+  // bit search on the top 32 key bits, counts summed over the lanes) and the
+  // block the smallest of the four.  Keys below it are never appended, so
+  // the buffer rarely needs cutting before the end.  If fewer than GK keys
+  // reach it, the candidates are collected again from no threshold (below).
+  {
+    uint64_t sk[GCAP / GT];
+#pragma unroll
+    for (int q = 0; q < GCAP / GT; ++q) {
+      const int64_t p = ((int64_t)(q * GT + (int)threadIdx.x) * v) / GCAP;
+      const float x = ld_f32(r, p);
+      sk[q] = x == x ? topk_key(x, (int)p) : 0ull;
+    }
+    uint32_t pre = 0;
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t c = pre | (1u << b);
+      int cnt = 0;
+#pragma unroll
+      for (int q = 0; q < GCAP / GT; ++q) cnt += (uint32_t)(sk[q] >> 32) >= c ? 1 : 0;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o);
+      if (cnt >= 5) pre = c;
+    }
+    if (lane == 0) sh.wthr[wave] = pre;
+  }
+  if (threadIdx.x == 0) sh.cnt = 0;
   __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t m = sh.wthr[0];
+    for (int w = 1; w < GT / 64; ++w) m = sh.wthr[w] < m ? sh.wthr[w] : m;
+    sh.thr = (uint64_t)m << 32;   // a key with that value and any id reaches it
+    sh.cut = 0;
+  }
+  __syncthreads();
+  const uint64_t thr0 = sh.thr;
 
   LseState st{kNegInf, 0.0, 0.0, 0.0};
   const int64_t rounds = (v + GROUND - 1) / GROUND;
@@ -220,7 +287,34 @@ __global__ __launch_bounds__(GT) void golden_export_kernel(
       }
     }
     __syncthreads();
-    if (sh.cnt > GCAP - GROUND) golden_compact(sh);
+    if (sh.cnt > GCAP - GROUND) {
+      golden_compact(sh);
+      if (threadIdx.x == 0) sh.cut = 1;
+      __syncthreads();
+    }
+  }
+  // Fewer than GK keys reached the sampled threshold and no cut raised it:
+  // the GK best may include keys below it, so collect the candidates again
+  // from no threshold (keys only; the sums are complete).
+  if (thr0 != 0ull && sh.cut == 0 && sh.cnt < GK) {
+    __syncthreads();
+    if (threadIdx.x == 0) { sh.cnt = 0; sh.thr = 0ull; }
+    __syncthreads();
+    for (int64_t rd = 0; rd < rounds; ++rd) {
+      const int64_t pos = rd * GROUND + (int64_t)threadIdx.x * GE;
+      float x[GE];
+      load_run<T, ALIGNED>(r, pos, v, x);
+      const uint64_t th = sh.thr;
+#pragma unroll
+      for (int e = 0; e < GE; ++e) {
+        if (pos + e < v && x[e] == x[e]) {
+          const uint64_t key = topk_key(x[e], (int)(pos + e));
+          if (key > th) sh.buf[atomicAdd(&sh.cnt, 1)] = key;
+        }
+      }
+      __syncthreads();
+      if (sh.cnt > GCAP - GROUND) golden_compact(sh);
+    }
   }
   golden_compact(sh);
   // the GK best keys, sorted descending (zero keys -- fewer than GK valid
