@@ -4,12 +4,13 @@
 // golden_export_kernel: one block per reference row.  One streaming pass keeps
 // the online log-sum-exp state and the entropy sum (f32 per round, f64 across
 // rounds) and filters the 512 largest (value, id) keys through an LDS
-// candidate buffer behind a threshold key (the 512th best so far, raised by a
-// block radix select whenever the buffer nears full).  The 512 are sorted by
-// a block bitonic network and written with their f32 log-probs.  A second
-// pass over the (cache-resident) row sums the probability of every id outside
-// the 512 directly, so a tiny tail mass keeps its relative accuracy instead
-// of coming out of 1 - sum of the listed probabilities.
+// candidate buffer behind a threshold key (first from a sample of the row,
+// then the 512th best so far whenever the buffer nears full and is cut).  The
+// 512 are sorted by a block bitonic network and written with their f32
+// log-probs.  The probability of every id outside the 512 is summed directly
+// in the same pass -- ids below the threshold as they stream by, candidates
+// as cuts drop them -- so a tiny tail mass keeps its relative accuracy
+// instead of coming out of 1 - sum of the listed probabilities.
 //
 // coarse_partial_kernel + coarse_finalize_kernel: a candidate row is split
 // into ranges of at most 131,072 ids, one block each.  A block sets the
@@ -153,11 +154,12 @@ struct GoldenShared {
 };
 
 // Cut the candidate buffer to its GK best keys (distinct; 0 = none) and make
-// the GK-th the threshold.  The GK-th key is found bit by bit from the top:
+// the GK-th the threshold; the mass of every dropped key is added to the
+// thread's unlisted sum (st.w), so the tail is summed directly in one pass.  The GK-th key is found bit by bit from the top:
 // a bit is kept if at least GK keys reach the prefix (each thread counts its
 // keys, a butterfly sums a wave's counts, LDS the four waves').  No
 // histogram: keys that share their high bits would pile onto one bin.
-__device__ void golden_compact(GoldenShared &sh) {
+__device__ void golden_compact(GoldenShared &sh, LseState &st) {
   uint64_t k[GCAP / GT];
   const int cnt = sh.cnt;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -182,6 +184,17 @@ __device__ void golden_compact(GoldenShared &sh) {
       for (int w = 0; w < GT / 64; ++w) tot += sh.wcnt[w];
       __syncthreads();
       if (tot >= GK) t = c;
+    }
+  }
+  // the dropped keys' mass (each key is in one thread's slice)
+#pragma unroll
+  for (int q = 0; q < GCAP / GT; ++q) {
+    if (k[q] != 0ull && k[q] < t) {
+      const float x = key_value(k[q]);
+      if (x != kNegInf) {   // (a -inf logit has no mass)
+        raise_max(st, x);
+        st.w += exp((double)x - (double)st.m);
+      }
     }
   }
   // the kept keys (exactly GK when t > 0) in any order, then zeros
@@ -265,58 +278,68 @@ __global__ __launch_bounds__(GT) void golden_export_kernel(
 #pragma unroll
     for (int e = 0; e < GE; ++e) bm = fmaxf(bm, x[e]);
     raise_max(st, bm);
-    float ps = 0.f, pu = 0.f;
+    float ps = 0.f, pu = 0.f, pw = 0.f;
+    float w[GE];
+#pragma unroll
+    for (int e = 0; e < GE; ++e) w[e] = 0.f;
     if (st.m != kNegInf) {
 #pragma unroll
       for (int e = 0; e < GE; ++e) {
         const float d = x[e] - st.m;
-        const float w = exp2_fast(d * kL2E);
-        ps += w;
-        pu = fmaf(w, fmaxf(d, -kFltMax), pu);   // a -inf logit (w = 0) adds exactly 0
+        w[e] = exp2_fast(d * kL2E);
+        ps += w[e];
+        pu = fmaf(w[e], fmaxf(d, -kFltMax), pu);   // a -inf logit (w = 0) adds exactly 0
       }
     }
-    st.s += (double)ps;
-    st.u += (double)pu;
-    // candidates: keys above the threshold (NaN logits are never listed)
+    // candidates: keys above the threshold (NaN logits are never listed);
+    // the rest are outside the GK best, their mass goes to the tail
     const uint64_t th = sh.thr;
 #pragma unroll
     for (int e = 0; e < GE; ++e) {
       if (pos + e < v && x[e] == x[e]) {
         const uint64_t key = topk_key(x[e], (int)(pos + e));
         if (key > th) sh.buf[atomicAdd(&sh.cnt, 1)] = key;
+        else pw += w[e];
       }
     }
+    st.s += (double)ps;
+    st.u += (double)pu;
+    st.w += (double)pw;
     __syncthreads();
     if (sh.cnt > GCAP - GROUND) {
-      golden_compact(sh);
+      golden_compact(sh, st);
       if (threadIdx.x == 0) sh.cut = 1;
       __syncthreads();
     }
   }
   // Fewer than GK keys reached the sampled threshold and no cut raised it:
-  // the GK best may include keys below it, so collect the candidates again
-  // from no threshold (keys only; the sums are complete).
+  // the GK best may include keys below it, so collect the candidates (and
+  // the tail) again from no threshold; the other sums are complete.
   if (thr0 != 0ull && sh.cut == 0 && sh.cnt < GK) {
     __syncthreads();
     if (threadIdx.x == 0) { sh.cnt = 0; sh.thr = 0ull; }
+    st.w = 0.0;
     __syncthreads();
     for (int64_t rd = 0; rd < rounds; ++rd) {
       const int64_t pos = rd * GROUND + (int64_t)threadIdx.x * GE;
       float x[GE];
       load_run<T, ALIGNED>(r, pos, v, x);
       const uint64_t th = sh.thr;
+      float pw = 0.f;
 #pragma unroll
       for (int e = 0; e < GE; ++e) {
         if (pos + e < v && x[e] == x[e]) {
           const uint64_t key = topk_key(x[e], (int)(pos + e));
           if (key > th) sh.buf[atomicAdd(&sh.cnt, 1)] = key;
+          else if (st.m != kNegInf) pw += exp2_fast((x[e] - st.m) * kL2E);
         }
       }
+      st.w += (double)pw;
       __syncthreads();
-      if (sh.cnt > GCAP - GROUND) golden_compact(sh);
+      if (sh.cnt > GCAP - GROUND) golden_compact(sh, st);
     }
   }
-  golden_compact(sh);
+  golden_compact(sh, st);
   // the GK best keys, sorted descending (zero keys -- fewer than GK valid
   // ids -- sort last)
   __syncthreads();
@@ -324,30 +347,12 @@ __global__ __launch_bounds__(GT) void golden_export_kernel(
   const LseState tot = lse_block(st, sh.xw);
   const double ls = log(tot.s);
   const double lse = (double)tot.m + ls;
-  const uint64_t t512 = sh.top[GK - 1];
   for (int i = (int)threadIdx.x; i < GK; i += GT) {
     const uint64_t key = sh.top[i];
     ids[row * GK + i] = key ? key_id(key) : 0;
     lp[row * GK + i] = key ? (float)((double)key_value(key) - lse) : kNegInf;
   }
-  // second pass: the mass of every id outside the GK listed ones
-  double tail = 0.0;
-  load_run<T, ALIGNED>(r, (int64_t)threadIdx.x * GE, v, xn);
-  for (int64_t rd = 0; rd < rounds; ++rd) {
-    const int64_t pos = rd * GROUND + (int64_t)threadIdx.x * GE;
-    float x[GE];
-#pragma unroll
-    for (int e = 0; e < GE; ++e) x[e] = xn[e];
-    if (rd + 1 < rounds) load_run<T, ALIGNED>(r, pos + GROUND, v, xn);
-    float pt = 0.f;
-#pragma unroll
-    for (int e = 0; e < GE; ++e) {
-      if (pos + e < v && x[e] == x[e] && topk_key(x[e], (int)(pos + e)) < t512)
-        pt += exp2_fast((float)(((double)x[e] - lse) * kL2E));
-    }
-    tail += (double)pt;
-  }
-  tail = sum_block(tail, sh.red);
+  const double tail = tot.w / tot.s;   // every id outside the GK listed ones, summed directly
   if (threadIdx.x == 0) {
     float nll = __builtin_nanf("");
     if (target) {
