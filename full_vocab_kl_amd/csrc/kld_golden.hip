@@ -111,19 +111,6 @@ __device__ LseState lse_block(LseState st, LseState *xw) {
   return r;
 }
 
-// Fixed-order block sum of one double per thread; every thread gets it.
-__device__ double sum_block(double x, double *red) {
-  red[threadIdx.x] = x;
-  __syncthreads();
-  for (int h = GT / 2; h > 0; h >>= 1) {
-    if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
-    __syncthreads();
-  }
-  const double r = red[0];
-  __syncthreads();
-  return r;
-}
-
 // Fold one round's f32 partial sums (relative to m) into the thread's state,
 // after raising m to the round maximum bm when it grew.
 __device__ __forceinline__ void raise_max(LseState &st, float bm) {
@@ -142,7 +129,6 @@ struct GoldenShared {
   uint64_t buf[GCAP];
   uint64_t top[GK];
   uint32_t hist[256];
-  double red[GT];
   LseState xw[GT / 64];
   uint64_t thr;
   int cnt;
