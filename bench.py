@@ -539,7 +539,7 @@ def windows_paired(steps, warmup, cpu_sample):
         "config": {"workload": "kld_window_summary x 2 + kld_paired_bootstrap: 10,480,640 scored "
                                "positions = 5,120 contexts x 2,047, 842 clusters, 10,000 replicates",
                    "positions": n, "contexts": nctx, "clusters": nclust, "replicates": nrep},
-        "roofline": {"bound": "hbm", "kernel": "window_seg_kernel (two candidates)",
+        "roofline": {"bound": "hbm", "kernel": "window_seg_wave_kernel + window_total_kernel (two candidates)",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": (None if _traffic("window_seg_kernel") is None

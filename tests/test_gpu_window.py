@@ -115,3 +115,51 @@ def test_ten_shard_launch():
     x, _ = synth.kl_score_pair(synth.LOGITS_F32, n)
     offsets = np.arange(0, n + 1, 2047, dtype=np.int64)
     _check(x, offsets, 0, where="ten-shard layout")
+
+
+def test_many_short_documents():
+    """Enough short documents (at least 1,024, averaging at most 16 Ki
+    positions) for the one-wave-per-segment launch: ragged lengths from 0 to
+    9,000 positions, some shorter than score_from, sixteen thresholds."""
+    lengths = [int(v) for v in np.random.default_rng(308).integers(0, 9000, 1500)]
+    lengths[:4] = [0, 1, 256, 2048]
+    offsets = synth.doc_offsets(308, lengths)
+    x = synth.kl_scores(308, int(offsets[-1]))
+    thr = tuple(float(np.float32(v)) for v in np.geomspace(1e-4, 10.0, 16))
+    a, _ = _check(x, offsets, 256, thr=thr, where="short documents")
+    b = _run(x, offsets, 256, thr)
+    for k in a:
+        assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), f"{k} not reproducible"
+
+
+def test_many_short_documents_bad_pair():
+    """A decreasing offset pair in the one-wave launch: that segment's sum is
+    NaN and its count 0, the mean is NaN, every other segment is unaffected."""
+    x = synth.kl_scores(309, 1200 * 500)
+    offsets = np.arange(0, 1200 * 500 + 1, 500, dtype=np.int64)
+    offsets[7] = offsets[6] - 1                                  # segment 6 decreasing
+    got = _run(x, offsets, 0)
+    assert np.isnan(got["seg_sum"][6]) and got["seg_count"][6] == 0
+    assert np.isnan(got["totals"][0])
+    want = oracle.window_summary(x, offsets, 0, THR)            # segment 6 empty there
+    ok = np.arange(1200) != 6
+    assert np.array_equal(got["seg_count"][ok], want["seg_count"][ok])
+    assert np.array_equal(got["seg_exceed"][ok], want["seg_exceed"][ok])
+    err = np.abs(got["seg_sum"][ok] - want["seg_sum"][ok])
+    assert np.all(err <= 1e-12 * want["seg_sum"][ok])
+    assert got["seg_count"][7] == 1001
+
+
+@pytest.mark.parametrize("nthr", [0, 1, 4, 5, 9, 16])
+@pytest.mark.parametrize("layout", ["wave", "block"])
+def test_threshold_counts(nthr, layout):
+    """Every padded threshold-count class (none, up to 4, 8 and 16) in both
+    launches: 1,100 segments of 300 positions (one wave each) and 10 segments
+    of 3,000 (one block each), score_from 7, unsorted thresholds with a
+    duplicate."""
+    pool = [0.5, 0.01, 2.0, 0.1, 0.5, 5.0, 1.0, 0.0, 0.05, 3.0, 0.2, 8.0, 0.3, 0.02, 0.7, 1.5]
+    thr = tuple(float(np.float32(v)) for v in pool[:nthr])
+    nseg, per = (1100, 300) if layout == "wave" else (10, 3000)
+    x = synth.kl_scores(310 + nthr, nseg * per)
+    offsets = np.arange(0, nseg * per + 1, per, dtype=np.int64)
+    _check(x, offsets, 7, thr=thr, where=f"{layout} nthr={nthr}")
