@@ -34,15 +34,17 @@ namespace {
 
 constexpr int PT = 256;
 
+// Sum over the block in a fixed order: a butterfly within each wave, then the
+// wave results in order.  red holds PT / 64 entries.
 template <typename T>
 __device__ __forceinline__ T block_sum(T x, T *red) {
-  red[threadIdx.x] = x;
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) x += __shfl_xor(x, m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
   __syncthreads();
-  for (int h = PT / 2; h > 0; h >>= 1) {
-    if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
-    __syncthreads();
-  }
-  const T r = red[0];
+  T r = red[0];
+#pragma unroll
+  for (int w = 1; w < PT / 64; ++w) r += red[w];
   __syncthreads();
   return r;
 }
@@ -52,20 +54,32 @@ __global__ __launch_bounds__(PT) void paired_cluster_kernel(
     const int64_t *__restrict__ count, int64_t nctx, const int32_t *__restrict__ cluster,
     int64_t nclust, double *__restrict__ clus_diff, int64_t *__restrict__ clus_count,
     double *__restrict__ out) {
-  __shared__ double rd[PT];
-  __shared__ long long ri[PT];
+  __shared__ double rd[PT / 64];
+  __shared__ long long ri[PT / 64];
+  constexpr int U = 8;   // contexts per thread and round, loads issued together
   const int64_t k = blockIdx.x;
+  const int64_t last = nctx > 0 ? nctx - 1 : 0;
   if (k < nclust) {
+    // every block reads all labels (unconditional, clamped loads); a
+    // context's values are loaded only where its label matches, a branch
+    // almost never taken
     double d = 0.0;
     long long c = 0;
-    // loads unconditional, the contribution masked: no branch around a load
-#pragma unroll 4
-    for (int64_t i = threadIdx.x; i < nctx; i += PT) {
-      const bool in = cluster[i] == k;
-      const double x = sum_a[i] - sum_b[i];
-      const int64_t n = count[i];
-      d += in ? x : 0.0;
-      c += in ? n : 0;
+    for (int64_t i0 = threadIdx.x; i0 < nctx; i0 += (int64_t)PT * U) {
+      int32_t lab[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = i0 + (int64_t)u * PT;
+        lab[u] = cluster[i < nctx ? i : last];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = i0 + (int64_t)u * PT;
+        if (i < nctx && lab[u] == k) {
+          d += sum_a[i] - sum_b[i];
+          c += count[i];
+        }
+      }
     }
     d = block_sum(d, rd);
     c = block_sum(c, ri);
@@ -78,17 +92,32 @@ __global__ __launch_bounds__(PT) void paired_cluster_kernel(
   // the overall difference, wins and ties, and a check of the labels
   double d = 0.0;
   long long c = 0, wa = 0, wb = 0, ti = 0, bad = 0;
-  for (int64_t i = threadIdx.x; i < nctx; i += PT) {
-    const double a = sum_a[i], b = sum_b[i];
-    const int64_t n = count[i];
-    d += a - b;
-    c += n;
-    bad += (cluster[i] < 0 || cluster[i] >= nclust || n < 0) ? 1 : 0;
-    if (n > 0) {
-      const double ma = a / (double)n, mb = b / (double)n;
-      wa += ma < mb;
-      wb += mb < ma;
-      ti += ma == mb;
+  for (int64_t i0 = threadIdx.x; i0 < nctx; i0 += (int64_t)PT * U) {
+    double va[U], vb[U];
+    int64_t vn[U];
+    int32_t vl[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i0u = i0 + (int64_t)u * PT, i = i0u < nctx ? i0u : last;
+      va[u] = sum_a[i];
+      vb[u] = sum_b[i];
+      vn[u] = count[i];
+      vl[u] = cluster[i];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (i0 + (int64_t)u * PT >= nctx) continue;
+      const double a = va[u], b = vb[u];
+      const int64_t n = vn[u];
+      d += a - b;
+      c += n;
+      bad += (vl[u] < 0 || vl[u] >= nclust || n < 0) ? 1 : 0;
+      if (n > 0) {
+        const double ma = a / (double)n, mb = b / (double)n;
+        wa += ma < mb;
+        wb += mb < ma;
+        ti += ma == mb;
+      }
     }
   }
   d = block_sum(d, rd);
