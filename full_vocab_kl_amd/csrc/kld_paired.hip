@@ -215,12 +215,30 @@ __global__ __launch_bounds__(RUN) void paired_runsort_kernel(const double *__res
 }
 
 constexpr int RT = 256;
+static_assert((RUN / 2) % RT == 0, "runs are copied in whole 16-byte rows of the block");
 
 __global__ __launch_bounds__(RT) void paired_rank_kernel(const double *__restrict__ runs,
                                                          int64_t nrep, int nruns,
                                                          double *__restrict__ sorted) {
   __shared__ double r[KLD_MAX_REPLICATES];
-  for (int i = threadIdx.x; i < nruns * RUN; i += RT) r[i] = runs[i];
+  // copy every run into LDS as 16-byte pieces, eight loads in flight per
+  // thread (clamped, unconditional), then the stores that are in range
+  {
+    const double2 *src = reinterpret_cast<const double2 *>(runs);
+    double2 *dst = reinterpret_cast<double2 *>(r);
+    const int per = nruns * (RUN / 2 / RT);   // pieces per thread (RUN / 2 a multiple of RT)
+    for (int j0 = 0; j0 < per; j0 += 8) {
+      double2 x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u < per ? j0 + u : per - 1;
+        x[u] = src[j * RT + threadIdx.x];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (j0 + u < per) dst[(j0 + u) * RT + threadIdx.x] = x[u];
+    }
+  }
   __syncthreads();
   const int64_t e = (int64_t)blockIdx.x * RT + threadIdx.x;
   if (e >= nrep) return;

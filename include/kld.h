@@ -66,7 +66,7 @@ typedef enum kld_status {
   KLD_EINVAL = 1,       /* a required pointer is NULL or a count is negative */
   KLD_ESHAPE = 2,       /* inconsistent sizes (ld < v, v < 64 with top-k, k != 64, ...) */
   KLD_EDTYPE = 3,       /* unknown dtype code */
-  KLD_EWORKSPACE = 4,   /* workspace missing or smaller than kld_workspace_size() */
+  KLD_EWORKSPACE = 4,   /* workspace missing, smaller than kld_workspace_size() or not 16-byte aligned */
   KLD_EUNSUPPORTED = 5, /* valid request the library does not serve (alignment, d % 8) */
   KLD_EHIP = 6          /* the HIP runtime reported an error at launch */
 } kld_status;

@@ -179,6 +179,8 @@ def test_paired_bootstrap_validation_fails_closed():
     assert lib.kld_paired_bootstrap(16, 16, 16, 8, 16, 3, 16, 10, q, 2, 16, 16, None, 0,
                                     None) == 4
     assert lib.kld_paired_bootstrap(16, 16, 16, 8, 16, 3, 16, 10, q, 2, 16, 16, 16, 8, None) == 4
+    # a workspace that is not 16-byte aligned
+    assert lib.kld_paired_bootstrap(16, 16, 16, 8, 16, 3, 16, 10, q, 2, 16, 16, 24, ws, None) == 4
     assert kld.kld_workspace_size(5, 842, 10_000) >= 842 * 16 + 2 * 10_000 * 8
 
 
