@@ -337,7 +337,7 @@ kld_status kld_paired_bootstrap(const double *sum_a, const double *sum_b, const 
   if ((nclust > 0 || nrep > 0) &&
       (!ws || ws_bytes < kld_workspace_size(KLD_OP_PAIRED, nclust, nrep, 0, 0)))
     return KLD_EWORKSPACE;
-  if (nrep > 0 && !aligned16(ws)) return KLD_EWORKSPACE;   // runs are copied in 16-byte pieces
+  if ((nclust > 0 || nrep > 0) && !aligned16(ws)) return KLD_EWORKSPACE;   // 16-byte entries
   if (launch_paired_bootstrap(sum_a, sum_b, count, nctx, cluster, nclust, draws, nrep, qs,
                               replicates, out, ws, as_stream(stream)) != hipSuccess)
     return KLD_EHIP;

@@ -52,7 +52,7 @@ __device__ __forceinline__ T block_sum(T x, T *red) {
 __global__ __launch_bounds__(PT) void paired_cluster_kernel(
     const double *__restrict__ sum_a, const double *__restrict__ sum_b,
     const int64_t *__restrict__ count, int64_t nctx, const int32_t *__restrict__ cluster,
-    int64_t nclust, double *__restrict__ clus_diff, int64_t *__restrict__ clus_count,
+    int64_t nclust, longlong2 *__restrict__ clus,
     double *__restrict__ out) {
   __shared__ double rd[PT / 64];
   __shared__ long long ri[PT / 64];
@@ -84,8 +84,7 @@ __global__ __launch_bounds__(PT) void paired_cluster_kernel(
     d = block_sum(d, rd);
     c = block_sum(c, ri);
     if (threadIdx.x == 0) {
-      clus_diff[k] = d;
-      clus_count[k] = c;
+      clus[k] = make_longlong2(__double_as_longlong(d), c);   // one 16-byte gather later
     }
     return;
   }
@@ -137,10 +136,12 @@ __global__ __launch_bounds__(PT) void paired_cluster_kernel(
 constexpr int RW = 4;   // waves (replicates) per block
 
 __global__ __launch_bounds__(RW * 64) void paired_replicate_kernel(
-    const double *__restrict__ clus_diff, const int64_t *__restrict__ clus_count, int64_t nclust,
+    const longlong2 *__restrict__ clus, int64_t nclust,
     const int32_t *__restrict__ draws, int64_t nrep, double *__restrict__ reps) {
   const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * RW + (threadIdx.x >> 6);
+  // the wave index made visibly uniform, so that the buffer resource lives
+  // in scalar registers (else every load would loop over the lanes)
+  const int64_t r = (int64_t)blockIdx.x * RW + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (r >= nrep) return;
   const int32_t *dr = draws + r * nclust;
   double num = 0.0;
@@ -150,18 +151,20 @@ __global__ __launch_bounds__(RW * 64) void paired_replicate_kernel(
   // gathers at clamped indices, contributions masked: no branch around a load
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int32_t *>(dr), (short)0, (int)(nclust * 4), 0x00020000);
-  for (int i0 = lane; i0 < nclust; i0 += 64 * 4) {
-    int32_t k[4];
+  constexpr int RU = 16;   // draws per lane and round: 1,024 per wave
+  for (int i0 = lane; i0 < nclust; i0 += 64 * RU) {
+    int32_t k[RU];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < RU; ++u)
       k[u] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, (i0 + 64 * u) * 4, 0, 0);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < RU; ++u) {
       const bool in = i0 + 64 * u < nclust;
       const bool ok = k[u] >= 0 && k[u] < nclust;
       const int32_t kk = ok ? k[u] : 0;
-      const double x = clus_diff[kk];
-      const long long n = clus_count[kk];
+      const longlong2 cv = clus[kk];   // the cluster's summed difference and count
+      const double x = __longlong_as_double(cv.x);
+      const long long n = cv.y;
       bad |= (in && !ok) ? 1 : 0;
       num += (in && ok) ? x : 0.0;
       den += (in && ok) ? n : 0;
@@ -304,18 +307,17 @@ hipError_t launch_paired_bootstrap(const double *sum_a, const double *sum_b, con
                                    int64_t nctx, const int32_t *cluster, int64_t nclust,
                                    const int32_t *draws, int64_t nrep, const PairedQuantiles &qs,
                                    double *reps, double *out, void *ws, hipStream_t stream) {
-  double *clus_diff = static_cast<double *>(ws);
-  int64_t *clus_count = reinterpret_cast<int64_t *>(clus_diff + nclust);
-  double *runs = reinterpret_cast<double *>(clus_count + nclust);
+  longlong2 *clus = static_cast<longlong2 *>(ws);   // per cluster: difference (f64 bits), count
+  double *runs = reinterpret_cast<double *>(clus + nclust);
   const int nruns = (int)((nrep + RUN - 1) / RUN);
   double *sorted = runs + (int64_t)nruns * RUN;
   hipLaunchKernelGGL(paired_cluster_kernel, dim3((unsigned)(nclust + 1)), dim3(PT), 0, stream,
-                     sum_a, sum_b, count, nctx, cluster, nclust, clus_diff, clus_count, out);
+                     sum_a, sum_b, count, nctx, cluster, nclust, clus, out);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (nrep > 0) {
     hipLaunchKernelGGL(paired_replicate_kernel, dim3((unsigned)((nrep + RW - 1) / RW)),
-                       dim3(RW * 64), 0, stream, clus_diff, clus_count, nclust, draws, nrep, reps);
+                       dim3(RW * 64), 0, stream, clus, nclust, draws, nrep, reps);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(paired_runsort_kernel, dim3((unsigned)nruns), dim3(RUN), 0, stream, reps,
                        nrep, runs);
