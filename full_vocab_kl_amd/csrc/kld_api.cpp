@@ -16,6 +16,16 @@ namespace {
 constexpr size_t kAlign = 256;
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+// Every pointer argument must be aligned to its element size (NULL passes);
+// workspaces to 16 bytes.
+inline bool al(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+inline bool rows_aligned(const kld_rows *o) {
+  return al(o->kl, 4) && al(o->nll_ref, 4) && al(o->nll_cand, 4) && al(o->lse_ref, 4) &&
+         al(o->lse_cand, 4) && al(o->argmax_ref, 4) && al(o->argmax_cand, 4);
+}
+inline bool topk_aligned(const kld_topk *t) {
+  return !t || (al(t->ids_ref, 4) && al(t->ids_cand, 4) && al(t->lp_ref, 2) && al(t->lp_cand, 2));
+}
 
 // Workspace carving: a bump allocator over the caller's buffer.
 struct Carver {
@@ -126,8 +136,8 @@ const char *kld_status_str(int s) {
     case KLD_EINVAL: return "KLD_EINVAL: null pointer or negative count";
     case KLD_ESHAPE: return "KLD_ESHAPE: inconsistent sizes";
     case KLD_EDTYPE: return "KLD_EDTYPE: unknown dtype";
-    case KLD_EWORKSPACE: return "KLD_EWORKSPACE: workspace missing or too small";
-    case KLD_EUNSUPPORTED: return "KLD_EUNSUPPORTED: valid request the library does not serve";
+    case KLD_EWORKSPACE: return "KLD_EWORKSPACE: workspace missing, too small or not 16-byte aligned";
+    case KLD_EUNSUPPORTED: return "KLD_EUNSUPPORTED: valid request the library does not serve (alignment, d % 8)";
     case KLD_EHIP: return "KLD_EHIP: HIP runtime error";
     default: return "KLD_UNKNOWN";
   }
@@ -167,10 +177,13 @@ kld_status kld_from_logits(const void *ref, const void *cand, int dtype, int64_t
   if (ld_ref < v || ld_cand < v) return KLD_ESHAPE;
   if ((out->nll_ref || out->nll_cand) && !target) return KLD_EINVAL;
   if (topk && v < KLD_TOPK) return KLD_ESHAPE;
-  const size_t need = kld_workspace_size(KLD_OP_FROM_LOGITS, n, v, 0, topk ? KLD_FLAG_TOPK : 0);
-  if (!ws || ws_bytes < need) return KLD_EWORKSPACE;
-
   const size_t esize = dtype == KLD_F32 ? 4 : 2;
+  if (!al(ref, esize) || !al(cand, esize) || !al(target, 4) || !rows_aligned(out) ||
+      !topk_aligned(topk))
+    return KLD_EUNSUPPORTED;
+  const size_t need = kld_workspace_size(KLD_OP_FROM_LOGITS, n, v, 0, topk ? KLD_FLAG_TOPK : 0);
+  if (!ws || ws_bytes < need || !aligned16(ws)) return KLD_EWORKSPACE;
+
   LogitsGeom g = logits_geom(n, v);
   LogitsArgs a;
   a.ref = ref; a.cand = cand; a.dtype = dtype; a.n = n; a.v = v;
@@ -206,11 +219,12 @@ kld_status kld_fused_head(const uint16_t *W, int64_t v, int64_t d, const uint16_
   if (v < 1 || v > 0x7fffffffLL || d < 1 || d > (1 << 20)) return KLD_ESHAPE;
   if (!W || !h_ref || !h_cand || !out->kl) return KLD_EINVAL;
   if ((out->nll_ref || out->nll_cand) && !target) return KLD_EINVAL;
-  if (d % 8 != 0 || !aligned16(W) || !aligned16(h_ref) || !aligned16(h_cand))
-    return KLD_EUNSUPPORTED;
   if (topk && v < KLD_TOPK) return KLD_ESHAPE;
+  if (d % 8 != 0 || !aligned16(W) || !aligned16(h_ref) || !aligned16(h_cand) || !al(target, 4) ||
+      !rows_aligned(out) || !topk_aligned(topk))
+    return KLD_EUNSUPPORTED;
   const size_t need = kld_workspace_size(KLD_OP_FUSED_HEAD, n, v, d, topk ? KLD_FLAG_TOPK : 0);
-  if (!ws || ws_bytes < need) return KLD_EWORKSPACE;
+  if (!ws || ws_bytes < need || !aligned16(ws)) return KLD_EWORKSPACE;
 
   Carver c(ws);
   const FusedWs w = fused_carve(n, v, topk != nullptr, &c);
@@ -236,9 +250,12 @@ kld_status topk_export(const void *logits, int dtype, int64_t n, int64_t v, int6
   if (v < KLD_TOPK || v > 0x7fffffffLL || ld < v) return KLD_ESHAPE;
   if (!logits || !ids || !lp) return KLD_EINVAL;
   if (target_lp && !target) return KLD_EINVAL;
-  if (!ws || ws_bytes < kld_workspace_size(KLD_OP_TOPK_EXPORT, n, v, 0, KLD_FLAG_TOPK))
-    return KLD_EWORKSPACE;
   const size_t esize = dtype == KLD_F32 ? 4 : 2;
+  if (!al(logits, esize) || !al(ids, 4) || !al(lp, 2) || !al(target, 4) || !al(target_lp, 4))
+    return KLD_EUNSUPPORTED;
+  if (!ws || ws_bytes < kld_workspace_size(KLD_OP_TOPK_EXPORT, n, v, 0, KLD_FLAG_TOPK) ||
+      !aligned16(ws))
+    return KLD_EWORKSPACE;
   const LogitsGeom g = logits_geom(n, v);
   LogitsArgs a;
   a.ref = logits; a.cand = logits; a.dtype = dtype; a.n = n; a.v = v;
@@ -267,6 +284,8 @@ kld_status kld_golden_export(const void *logits, int dtype, int64_t n, int64_t v
   if (n > 0x7fffffffLL || v < KLD_GOLDEN_TOPK || v > 0x7fffffffLL || ld < v) return KLD_ESHAPE;
   if (!logits || !ids || !lp || !rec) return KLD_EINVAL;
   const size_t esize = dtype == KLD_F32 ? 4 : 2;
+  if (!al(logits, esize) || !al(target, 4) || !al(ids, 4) || !al(lp, 4) || !al(rec, 4))
+    return KLD_EUNSUPPORTED;
   const bool aligned = aligned16(logits) && (ld * esize) % 16 == 0;
   if (launch_golden_export(logits, dtype, n, v, ld, aligned, target, ids, lp, rec,
                            as_stream(stream)) != hipSuccess)
@@ -283,8 +302,11 @@ kld_status kld_coarse_kl(const void *cand, int dtype, int64_t n, int64_t v, int6
   if (n == 0) return KLD_OK;
   if (n > 0x7fffffffLL || v < KLD_GOLDEN_TOPK || v > 0x7fffffffLL || ld < v) return KLD_ESHAPE;
   if (!cand || !ids || !lp || !rec || !kl) return KLD_EINVAL;
-  if (!ws || ws_bytes < kld_workspace_size(KLD_OP_COARSE_KL, n, v, 0, 0)) return KLD_EWORKSPACE;
   const size_t esize = dtype == KLD_F32 ? 4 : 2;
+  if (!al(cand, esize) || !al(ids, 4) || !al(lp, 4) || !al(rec, 4) || !al(kl, 4))
+    return KLD_EUNSUPPORTED;
+  if (!ws || ws_bytes < kld_workspace_size(KLD_OP_COARSE_KL, n, v, 0, 0) || !aligned16(ws))
+    return KLD_EWORKSPACE;
   const bool aligned = aligned16(cand) && (ld * esize) % 16 == 0;
   if (launch_coarse_kl(cand, dtype, n, v, ld, aligned, ids, lp, rec, kl, ws, as_stream(stream)) !=
       hipSuccess)
@@ -302,8 +324,11 @@ kld_status kld_coarse_fused(const uint16_t *W, int64_t v, int64_t d, const uint1
   if (n > 0x7fffffffLL || v < KLD_GOLDEN_TOPK || v > 0x7fffffffLL || d < 1 || d > (1 << 20))
     return KLD_ESHAPE;
   if (!W || !h_cand || !ids || !lp || !rec || !kl) return KLD_EINVAL;
-  if (d % 8 != 0 || !aligned16(W) || !aligned16(h_cand)) return KLD_EUNSUPPORTED;
-  if (!ws || ws_bytes < kld_workspace_size(KLD_OP_COARSE_FUSED, n, v, d, 0)) return KLD_EWORKSPACE;
+  if (d % 8 != 0 || !aligned16(W) || !aligned16(h_cand) || !al(ids, 4) || !al(lp, 4) ||
+      !al(rec, 4) || !al(kl, 4))
+    return KLD_EUNSUPPORTED;
+  if (!ws || ws_bytes < kld_workspace_size(KLD_OP_COARSE_FUSED, n, v, d, 0) || !aligned16(ws))
+    return KLD_EWORKSPACE;
   Carver c(ws);
   const SparseWs w = sparse_carve(n, v, &c);
   CoarseFusedArgs a;
@@ -327,6 +352,9 @@ kld_status kld_paired_bootstrap(const double *sum_a, const double *sum_b, const 
   if (!out || (nctx > 0 && (!sum_a || !sum_b || !count || !cluster)) ||
       (nrep > 0 && (!draws || !replicates)) || (nq > 0 && !quantiles))
     return KLD_EINVAL;
+  if (!al(sum_a, 8) || !al(sum_b, 8) || !al(count, 8) || !al(cluster, 4) || !al(draws, 4) ||
+      !al(replicates, 8) || !al(out, 8))
+    return KLD_EUNSUPPORTED;
   PairedQuantiles qs;
   qs.count = nq;
   for (int i = 0; i < KLD_MAX_QUANTILES; ++i) {
@@ -354,6 +382,9 @@ kld_status kld_window_summary(const float *kl, int64_t n, const int64_t *offsets
       (nthr > 0 && (!thresholds || (nseg > 0 && !seg_exceed))))
     return KLD_EINVAL;
   if (n > 0 && !kl) return KLD_EINVAL;
+  if (!al(kl, 4) || !al(offsets, 8) || !al(seg_sum, 8) || !al(seg_count, 8) ||
+      !al(seg_exceed, 8) || !al(totals, 8))
+    return KLD_EUNSUPPORTED;
   WindowThresholds thr;
   thr.count = nthr;
   for (int t = 0; t < KLD_MAX_THRESHOLDS; ++t) thr.value[t] = t < nthr ? thresholds[t] : 0.f;
@@ -371,6 +402,8 @@ kld_status kld_topk_tail(const int32_t *ids_p, const uint16_t *lp_p, const int32
   if (n == 0) return KLD_OK;
   if (v <= KLD_TOPK || v > 0x7fffffffLL) return KLD_ESHAPE;
   if (!ids_p || !lp_p || !ids_q || !lp_q || !kl_tail) return KLD_EINVAL;
+  if (!al(ids_p, 4) || !al(lp_p, 2) || !al(ids_q, 4) || !al(lp_q, 2) || !al(kl_tail, 4))
+    return KLD_EUNSUPPORTED;
   if (launch_topk_tail(ids_p, lp_p, ids_q, lp_q, n, v, kl_tail, as_stream(stream)) != hipSuccess)
     return KLD_EHIP;
   return KLD_OK;
@@ -401,7 +434,11 @@ kld_status kld_summary(const float *kl, const int32_t *argmax_ref, const int32_t
     a.ranks.rank[2 * i + 1] = (uint32_t)hi;
     a.qs.frac[i] = h - (double)lo;
   }
-  if (!ws || ws_bytes < kld_workspace_size(KLD_OP_SUMMARY, n, 0, 0, 0)) return KLD_EWORKSPACE;
+  if (!al(kl, 4) || !al(argmax_ref, 4) || !al(argmax_cand, 4) || !al(nll_ref, 4) ||
+      !al(nll_cand, 4) || !al(out, 8))
+    return KLD_EUNSUPPORTED;
+  if (!ws || ws_bytes < kld_workspace_size(KLD_OP_SUMMARY, n, 0, 0, 0) || !aligned16(ws))
+    return KLD_EWORKSPACE;
   a.kl = kl; a.argmax_ref = argmax_ref; a.argmax_cand = argmax_cand;
   a.nll_ref = nll_ref; a.nll_cand = nll_cand; a.n = n; a.out = out;
   a.stream = as_stream(stream);

@@ -30,13 +30,19 @@
  *
  *  - Every tensor argument is DEVICE memory owned by the caller; the library
  *    never allocates or frees memory.  Scratch space comes from the caller's
- *    workspace (`ws`, `ws_bytes`), sized by kld_workspace_size().  Device
- *    pointers must be 16-byte aligned unless stated otherwise.
+ *    workspace (`ws`, `ws_bytes`), sized by kld_workspace_size().
+ *  - Alignment: every pointer must be aligned to its element size (4 bytes
+ *    for f32 / int32 arrays, 2 for bf16 / fp16 bit patterns, 8 for f64 /
+ *    int64), otherwise KLD_EUNSUPPORTED; the head and hidden states of the
+ *    fused entry points need 16 bytes.  A workspace must be 16-byte aligned,
+ *    otherwise KLD_EWORKSPACE.  Allocations from the HIP allocator (or
+ *    torch) meet all of these.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *    stream).  Outputs are valid once that stream has completed the work.
- *  - Fail-closed: every argument is checked before anything is launched; on
- *    an error nothing is launched and nothing is written.  n == 0 is a valid
- *    no-op.  A failed launch returns KLD_EHIP.
+ *  - Fail-closed: every argument (pointers, sizes, alignment, workspace size)
+ *    is checked before anything is launched; on an error nothing is launched
+ *    and nothing is written.  n == 0 is a valid no-op.  A failed launch
+ *    returns KLD_EHIP.
  *  - No global mutable state: calls are thread-safe.  Results are bitwise
  *    deterministic (fixed-order merges, no floating-point atomics).
  *  - Non-finite inputs: a -inf logit is a zero-probability id; a finite
@@ -130,8 +136,8 @@ size_t kld_workspace_size(int op, int64_t n, int64_t v, int64_t d, int flags);
  * kld_from_logits -- score n positions given both logit tensors.
  *
  * ref, cand : [n, v] row-major logits (dtype f32 or bf16 bits), leading
- *             dimensions ld_ref, ld_cand >= v (in elements).  Any alignment is
- *             accepted; 16-byte-aligned rows take the vector path.
+ *             dimensions ld_ref, ld_cand >= v (in elements).  Element
+ *             alignment suffices; 16-byte-aligned rows take the vector path.
  * target    : [n] int32 true next-token ids, or NULL (then nll_* must be NULL).
  * out       : per-position outputs (see kld_rows).
  * topk      : NULL, or top-64 export of both sides (needs v >= 64).
@@ -187,7 +193,7 @@ kld_status topk_export(const void *logits, int dtype, int64_t n, int64_t v, int6
  * from the candidate list gets r / (v - k), r = max(0, 1 - candidate list
  * mass); the candidate tail cell is max(0, 1 - sum of its cell estimates);
  * the reference tail is max(0, 1 - reference list mass).  0 ln(0/x) = 0,
- * p ln(p/0) = +inf.  Needs no workspace.  Pointers need 4-byte alignment.
+ * p ln(p/0) = +inf.  Needs no workspace.
  */
 kld_status kld_topk_tail(const int32_t *ids_p, const uint16_t *lp_p, const int32_t *ids_q,
                          const uint16_t *lp_q, int64_t n, int k, int64_t v, float *kl_tail,
@@ -233,7 +239,6 @@ kld_status kld_summary(const float *kl, const int32_t *argmax_ref, const int32_t
  *          over the ids outside the 512, summed directly (not 1 - the listed
  *          mass, which would drown a tiny tail in rounding).
  * Needs no workspace.  Rows holding NaN logits give unspecified records.
- * Pointers need 4-byte alignment (logits: its element size).
  */
 kld_status kld_golden_export(const void *logits, int dtype, int64_t n, int64_t v, int64_t ld,
                              const int32_t *target, int k, int32_t *ids, float *lp, float *rec,
@@ -254,7 +259,6 @@ kld_status kld_golden_export(const void *logits, int dtype, int64_t n, int64_t v
  *          gives +inf; a listed id outside [0, v) or a candidate row with a
  *          NaN or +inf logit gives NaN.
  * ws     : workspace of kld_workspace_size(KLD_OP_COARSE_KL, n, v, 0, 0) bytes.
- * Pointers need 4-byte alignment (cand: its element size; ws: 16 bytes).
  */
 kld_status kld_coarse_kl(const void *cand, int dtype, int64_t n, int64_t v, int64_t ld,
                          const int32_t *ids, const float *lp, const float *rec, int k, float *kl,

@@ -48,3 +48,55 @@ def assert_nll_close(got, want, where=""):
     fin = np.isfinite(want)
     err = np.abs(got[fin] - want[fin])
     assert np.all(err <= 1e-5 * np.maximum(1.0, np.abs(want[fin]))), f"{where}: NLL max err {err.max()}"
+
+
+def _threads():
+    import os
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def oracle_rows(a, b, target=None, k=None, block=8):
+    """oracle.score_rows over row blocks on a thread pool (numpy releases the
+    GIL in the row arithmetic and sorts); the per-row results are the
+    oracle's own, concatenated in row order."""
+    from concurrent.futures import ThreadPoolExecutor
+    import oracle
+
+    n = a.shape[0]
+    starts = list(range(0, n, block))
+
+    def one(s):
+        t = None if target is None else target[s:s + block]
+        return oracle.score_rows(a[s:s + block], b[s:s + block], t, k=k)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        parts = list(ex.map(one, starts))
+    return {key: np.concatenate([p[key] for p in parts]) for key in parts[0]}
+
+
+def top_gaps(z, idx):
+    """Per row of z (f64 logits [n, v]): z_(i) - z_(i+1) of the descending
+    order for each 1-based rank i in idx (e.g. (1,) for the argmax gap,
+    (64,) for the top-64 set gap)."""
+    kth = sorted({v - 1 for v in idx} | {v for v in idx})
+    part = -np.partition(-z, kth, axis=1)
+    return {i: part[:, i - 1] - part[:, i] for i in idx}
+
+
+def host_quantiles(kl, qs):
+    """Type-7 quantiles of the given f32 values with the arithmetic the
+    device summary documents: h = q (n - 1) in f64, lo = floor(h), the two
+    order statistics widened to f64, lo + (h - lo) (hi - lo)."""
+    x = np.sort(np.asarray(kl, np.float32)).astype(np.float64)
+    n = x.shape[0]
+    res = []
+    for q in qs:
+        h = float(q) * float(n - 1)
+        lo = min(int(h), n - 1)
+        hi = min(lo + 1, n - 1)
+        res.append(x[lo] + (h - float(lo)) * (x[hi] - x[lo]))
+    return res

@@ -42,7 +42,7 @@ def test_workspace_sizes():
     assert kld.kld_workspace_size(0, 0, 10) == 0
 
 
-def _rows(kl=1):
+def _rows(kl=16):
     return binding._Rows(kl, None, None, None, None, None, None)
 
 
@@ -212,3 +212,83 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         binding.lib()
     with pytest.raises(RuntimeError, match="missing"):
         binding.kld_workspace_size(0, 4, 1000)
+
+
+def _call_fused(W=16, v=1000, d=64, hr=16, hc=16, n=4, target=None, rows=None, topk=None, ws=16,
+                ws_bytes=1 << 30):
+    rows = rows if rows is not None else _rows()
+    return kld.lib().kld_fused_head(W, v, d, hr, hc, n, target, ctypes.byref(rows), topk, ws,
+                                    ws_bytes, None, None)
+
+
+def test_fused_head_validation_fails_closed():
+    # kld_fused_head(W, v, d, h_ref, h_cand, n, target, out, topk, ws, ws_bytes, stream, opts)
+    assert _call_fused(W=None) == 1
+    assert _call_fused(hr=None) == 1
+    assert _call_fused(hc=None) == 1
+    assert _call_fused(rows=_rows(kl=None)) == 1
+    assert _call_fused(n=-1) == 1
+    assert _call_fused(d=-8) == 1
+    assert _call_fused(d=0) == 2
+    assert _call_fused(d=(1 << 20) + 8) == 2
+    assert _call_fused(v=0) == 2
+    assert _call_fused(d=60) == 5                     # d % 8 != 0
+    assert _call_fused(W=24) == 5                     # head not 16-byte aligned
+    assert _call_fused(hr=40) == 5
+    assert _call_fused(hc=8) == 5
+    assert _call_fused(target=18) == 5                # int32 ids not 4-byte aligned
+    assert _call_fused(rows=binding._Rows(18, None, None, None, None, None, None)) == 5
+    nll_rows = binding._Rows(16, 16, None, None, None, None, None)
+    assert _call_fused(rows=nll_rows, target=None) == 1   # NLL without a target
+    tk = binding._Topk(16, 16, 16, 16)
+    assert _call_fused(v=63, topk=ctypes.byref(tk)) == 2  # top-64 of fewer than 64 ids
+    bad_tk = binding._Topk(16, 17, 16, 16)
+    assert _call_fused(topk=ctypes.byref(bad_tk)) == 5   # fp16 list not 2-byte aligned
+    need = kld.kld_workspace_size(1, 4, 1000, 64)
+    assert need > 0
+    assert _call_fused(ws=None) == 4
+    assert _call_fused(ws_bytes=need - 1) == 4
+    assert _call_fused(ws=24) == 4                    # workspace not 16-byte aligned
+    need_topk = kld.kld_workspace_size(1, 4, 1000, 64, 1)
+    assert need_topk > need
+    assert _call_fused(topk=ctypes.byref(tk), ws_bytes=need) == 4
+    assert _call_fused(n=0) == 0
+
+
+def test_alignment_checked_everywhere():
+    """Pointers must be aligned to their element size, workspaces to 16 bytes;
+    misalignment is rejected before any launch."""
+    lib = kld.lib()
+    assert _call_from_logits(ref=18) == 5             # f32 rows need 4 bytes
+    assert _call_from_logits(cand=17, dtype=1) == 5
+    assert _call_from_logits(target=6) == 5
+    assert _call_from_logits(rows=binding._Rows(16, None, None, 18, None, None, None)) == 5
+    assert _call_from_logits(ws=40) == 4
+    tk = binding._Topk(18, 16, 16, 16)
+    assert _call_from_logits(topk=ctypes.byref(tk)) == 5
+    # topk_export(logits, dtype, n, v, ld, k, ids, lp, target, target_lp, ws, ws_bytes, stream)
+    assert lib.topk_export(16, 0, 4, 100, 100, 64, 18, 16, None, None, 16, 1 << 30, None) == 5
+    assert lib.topk_export(16, 0, 4, 100, 100, 64, 16, 17, None, None, 16, 1 << 30, None) == 5
+    assert lib.topk_export(16, 0, 4, 100, 100, 64, 16, 16, None, None, 8, 1 << 30, None) == 4
+    # kld_topk_tail(ids_p, lp_p, ids_q, lp_q, n, k, v, kl_tail, stream)
+    assert lib.kld_topk_tail(18, 16, 16, 16, 4, 64, 1000, 16, None) == 5
+    assert lib.kld_topk_tail(16, 16, 16, 17, 4, 64, 1000, 16, None) == 5
+    assert lib.kld_topk_tail(16, 16, 16, 16, 4, 64, 1000, 18, None) == 5
+    # kld_summary(kl, ar, ac, nr, nc, n, q, nq, out, ws, ws_bytes, stream)
+    qs = (ctypes.c_double * 1)(0.5)
+    assert lib.kld_summary(18, None, None, None, None, 10, qs, 1, 16, 16, 1 << 30, None) == 5
+    assert lib.kld_summary(16, None, None, None, None, 10, qs, 1, 20, 16, 1 << 30, None) == 5
+    assert lib.kld_summary(16, None, None, None, None, 10, qs, 1, 16, 8, 1 << 30, None) == 4
+    # kld_golden_export(logits, dtype, n, v, ld, target, k, ids, lp, rec, stream)
+    assert lib.kld_golden_export(18, 0, 4, 1000, 1000, None, 512, 16, 16, 16, None) == 5
+    assert lib.kld_golden_export(16, 0, 4, 1000, 1000, None, 512, 16, 16, 18, None) == 5
+    # kld_coarse_kl(cand, dtype, n, v, ld, ids, lp, rec, k, kl, ws, ws_bytes, stream)
+    assert lib.kld_coarse_kl(16, 1, 4, 1000, 1000, 18, 16, 16, 512, 16, 16, 1 << 30, None) == 5
+    assert lib.kld_coarse_kl(16, 1, 4, 1000, 1000, 16, 16, 16, 512, 16, 24, 1 << 30, None) == 4
+    # kld_window_summary(kl, n, offsets, nseg, score_from, thr, nthr, ...)
+    thr = (ctypes.c_float * 1)(0.5)
+    assert lib.kld_window_summary(16, 10, 20, 2, 0, thr, 1, 16, 16, 16, 16, None) == 5
+    # kld_paired_bootstrap(sum_a, sum_b, count, nctx, cluster, nclust, draws, nrep, q, nq, ...)
+    q = (ctypes.c_double * 1)(0.5)
+    assert lib.kld_paired_bootstrap(20, 16, 16, 8, 16, 3, 16, 10, q, 1, 16, 16, 16, 1 << 20,
+                                    None) == 5

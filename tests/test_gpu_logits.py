@@ -8,7 +8,8 @@ import torch
 import oracle
 import synth
 import full_vocab_kl_amd as kld
-from gpu_util import gpu, need_gpu, to_dev, assert_kl_close, assert_mean_rel, assert_nll_close
+from gpu_util import (gpu, need_gpu, to_dev, assert_kl_close, assert_mean_rel, assert_nll_close,
+                      oracle_rows, host_quantiles)
 
 pytestmark = gpu
 
@@ -124,16 +125,26 @@ def test_logits_deterministic():
         assert np.array_equal(r1[k].view(np.uint8), r2[k].view(np.uint8)), k
 
 
-def test_logits_full_size_f32_sampled():
+def test_logits_full_size_f32_all_rows():
     """The f32 workload at full size (512 x 248,320) in the launch the bench
-    times; the oracle checks a seeded sample of rows."""
+    times; the oracle checks every row, and the device summary of the call
+    equals the oracle's summary of the device values (quantiles exactly)."""
     need_gpu()
     n, v = 512, synth.VOCAB
     a, b = synth.logit_rows(synth.LOGITS_F32, range(n), v)
     t = synth.targets(synth.LOGITS_F32, range(n), v)
     got = _run(a, b, t, False)
-    rows = synth.subset(synth.LOGITS_F32, n, 48)
-    want = _oracle(a[rows], b[rows], t[rows], False)
-    sub = {k: x[rows] for k, x in got.items()}
-    _compare(sub, want, "full f32", strict_mean=True)
+    want = oracle_rows(a, b, t)
+    _compare(got, want, "full f32", strict_mean=True)
     assert np.all(np.isfinite(got["kl"])) and np.all(got["kl"] >= 0)
+    qs = (0.5, 0.99, 0.999)
+    summ = kld.summary_dict(kld.kld_summary(*(to_dev(got[k]) for k in (
+        "kl", "argmax_ref", "argmax_cand", "nll_ref", "nll_cand")), quantiles=qs), qs)
+    ow = oracle.summarize(want["kl"], want["argmax_ref"], want["argmax_cand"], want["nll_ref"],
+                          want["nll_cand"], quantiles=qs)
+    assert summ["top1"] == ow["top1"]
+    assert summ["mean_kl"] == pytest.approx(ow["mean_kl"], rel=1e-4)
+    assert summ["ppl_ref"] == pytest.approx(ow["ppl_ref"], rel=1e-4)
+    assert summ["ppl_cand"] == pytest.approx(ow["ppl_cand"], rel=1e-4)
+    for q, hq in zip(qs, host_quantiles(got["kl"], qs)):
+        assert summ["quantiles"][q] == hq, q

@@ -78,24 +78,6 @@ def test_topk_adversarial_orders_and_ties():
     assert list(got["ids_ref"][2]) == list(range(64))
 
 
-def test_topk_bf16_batch_sampled():
-    """One 4096-row bf16 batch of the top-64 workload at V = 248,320 (one
-    split per row); the oracle checks a seeded sample of rows."""
-    need_gpu()
-    n, v = 4096, synth.VOCAB
-    rows = synth.subset(synth.LOGITS_BF16_TOPK, n, 24)
-    a_all, b_all = synth.logit_rows(synth.LOGITS_BF16_TOPK, range(n), v, dtype="bf16")
-    out = kld.kld_from_logits(to_dev(a_all, True), to_dev(b_all, True), None, topk=True)
-    torch.cuda.synchronize()
-    got = {k: x.cpu().numpy()[rows] for k, x in out.items()}
-    want = oracle.score_rows(oracle.bf16_bits_to_f64(a_all[rows]), oracle.bf16_bits_to_f64(b_all[rows]),
-                             None, k=64)
-    for s in ("ref", "cand"):
-        assert np.array_equal(got[f"ids_{s}"], want[f"ids_{s}"]), s
-        assert_lp_close(got[f"lp_{s}"].view(np.uint16), want[f"lp_{s}"], s)
-    assert_kl_close(got["kl"], want["kl"], "bf16 batch")
-
-
 @pytest.mark.parametrize("bf16", [False, True])
 def test_topk_export_single_side_with_target(bf16):
     need_gpu()
