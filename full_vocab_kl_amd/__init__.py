@@ -9,5 +9,5 @@ from .binding import (  # noqa: F401
     KldError, KLD_F32, KLD_BF16, TOPK, lib, library_path, kld_workspace_size, kld_from_logits,
     kld_fused_head, topk_export, kld_topk_tail, kld_summary, summary_dict, kld_status_str,
     kld_abi_version, GOLDEN_TOPK, kld_golden_export, kld_coarse_kl,
-    kld_window_summary, kld_paired_bootstrap, kld_coarse_fused,
+    kld_window_summary, kld_paired_bootstrap, kld_coarse_fused, kld_from_logits_noalloc,
 )

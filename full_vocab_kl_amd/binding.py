@@ -57,6 +57,8 @@ _SIGS = {
     "kld_workspace_size": (_SZ, [_I, _I64, _I64, _I64, _I]),
     "kld_from_logits": (_I, [_P, _P, _I, _I64, _I64, _I64, _I64, _P, ctypes.POINTER(_Rows),
                              ctypes.POINTER(_Topk), _P, _SZ, _P, ctypes.POINTER(_Opts)]),
+    "kld_from_logits_noalloc": (_I, [_P, _P, _I, _I64, _I64, _I64, _I64, _P, ctypes.POINTER(_Rows),
+                                     ctypes.POINTER(_Topk), _P, ctypes.POINTER(_Opts)]),
     "kld_fused_head": (_I, [_P, _I64, _I64, _P, _P, _I64, _P, ctypes.POINTER(_Rows),
                             ctypes.POINTER(_Topk), _P, _SZ, _P, ctypes.POINTER(_Opts)]),
     "topk_export": (_I, [_P, _I, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -214,6 +216,32 @@ def kld_from_logits(ref: torch.Tensor, cand: torch.Tensor, target: torch.Tensor 
                                  ctypes.byref(tks) if tks else None, _ptr(ws), ws.numel(),
                                  _stream(stream), _opts(events))
     _check(code, "kld_from_logits")
+    if tk:
+        out.update(tk)
+    return out
+
+
+def kld_from_logits_noalloc(ref: torch.Tensor, cand: torch.Tensor,
+                            target: torch.Tensor | None = None, topk: bool = False,
+                            out: dict | None = None, stream=None, events=None) -> dict:
+    """kld_from_logits without a workspace: the library's static device
+    scratch serves instead.  Pass preallocated outputs in `out` (the rows and,
+    with topk, the four top-64 arrays) for a call that allocates nothing."""
+    n, v = ref.shape
+    if cand.shape != ref.shape:
+        raise ValueError("ref and cand must have the same shape")
+    dt = _dtype_code(ref)
+    if _dtype_code(cand) != dt:
+        raise TypeError("ref and cand must have the same dtype")
+    tk = _topk_from(out, n, ref.device) if topk else None
+    out = out if out is not None else _alloc_rows(n, ref.device, target)
+    rows = _rows_struct(out)
+    tks = _topk_struct(tk) if tk else None
+    code = lib().kld_from_logits_noalloc(_ptr(ref), _ptr(cand), dt, n, v, _rows_ld(ref),
+                                         _rows_ld(cand), _ptr(target), ctypes.byref(rows),
+                                         ctypes.byref(tks) if tks else None, _stream(stream),
+                                         _opts(events))
+    _check(code, "kld_from_logits_noalloc")
     if tk:
         out.update(tk)
     return out

@@ -5,11 +5,15 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <mutex>
 
 #include "kld_device.hpp"
 #include "kld_launch.hpp"
 
 using namespace kld;
+
+// Workspace of kld_from_logits_noalloc (see device_scratch below).
+static __device__ __align__(256) unsigned char scratch[KLD_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -126,6 +130,86 @@ Events events_of(const kld_launch_opts *o) {
   return e;
 }
 
+// ---- kld_from_logits: validation and launch, shared by the workspace and
+// the allocation-free entry points ------------------------------------------
+kld_status check_from_logits(const void *ref, const void *cand, int dtype, int64_t n, int64_t v,
+                             int64_t ld_ref, int64_t ld_cand, const int32_t *target,
+                             const kld_rows *out, const kld_topk *topk) {
+  if (dtype != KLD_F32 && dtype != KLD_BF16) return KLD_EDTYPE;
+  if (n < 0 || v < 0) return KLD_EINVAL;
+  if (!out) return KLD_EINVAL;
+  if (n == 0) return KLD_OK;
+  if (v < 1 || v > 0x7fffffffLL) return KLD_ESHAPE;
+  if (!ref || !cand || !out->kl) return KLD_EINVAL;
+  if (ld_ref < v || ld_cand < v) return KLD_ESHAPE;
+  if ((out->nll_ref || out->nll_cand) && !target) return KLD_EINVAL;
+  if (topk && v < KLD_TOPK) return KLD_ESHAPE;
+  const size_t esize = dtype == KLD_F32 ? 4 : 2;
+  if (!al(ref, esize) || !al(cand, esize) || !al(target, 4) || !rows_aligned(out) ||
+      !topk_aligned(topk))
+    return KLD_EUNSUPPORTED;
+  return KLD_OK;
+}
+
+kld_status run_from_logits(const void *ref, const void *cand, int dtype, int64_t n, int64_t v,
+                           int64_t ld_ref, int64_t ld_cand, const int32_t *target,
+                           const kld_rows *out, const kld_topk *topk, void *ws, void *stream,
+                           const kld_launch_opts *opts) {
+  const size_t esize = dtype == KLD_F32 ? 4 : 2;
+  const LogitsGeom g = logits_geom(n, v);
+  LogitsArgs a;
+  a.ref = ref; a.cand = cand; a.dtype = dtype; a.n = n; a.v = v;
+  a.ld_ref = ld_ref; a.ld_cand = ld_cand; a.chunk = g.chunk; a.splits = g.splits;
+  a.aligned = aligned16(ref) && aligned16(cand) && (ld_ref * esize) % 16 == 0 &&
+              (ld_cand * esize) % 16 == 0;
+  a.two = true;
+  a.target = target;
+  a.out = RowsOut{out->kl, out->nll_ref, out->nll_cand, out->lse_ref, out->lse_cand,
+                  out->argmax_ref, out->argmax_cand};
+  a.stream = as_stream(stream);
+  a.ev = events_of(opts);
+
+  Carver c(ws);
+  const LogitsWs w = logits_carve(n, v, topk != nullptr, &c);
+  if (launch_logits_state(a, w.part, w.keys) != hipSuccess) return KLD_EHIP;
+  if (launch_logits_finalize(a, w.part, w.lse, nullptr) != hipSuccess) return KLD_EHIP;
+  if (topk) {
+    const TopkOut to{topk->ids_ref, topk->lp_ref, topk->ids_cand, topk->lp_cand};
+    if (launch_topk_merge(w.keys, g.splits, 2, n, w.lse, to, a.stream) != hipSuccess)
+      return KLD_EHIP;
+  }
+  return KLD_OK;
+}
+
+// ---- the allocation-free variant's scratch ---------------------------------
+// The workspace of kld_from_logits_noalloc is this file-scope device array:
+// every GPU the library runs on holds its own copy (at its own address) until
+// the process ends.  Host code never uses the array's name as an address (on
+// the host it is only a stand-in); the device address is looked up once per
+// device, with that device current, and kept.  Nothing in the logits path
+// needs the workspace cleared: every partial state and candidate key is
+// written before it is read.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+hipError_t device_scratch(void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr || ((uintptr_t)p & 255u) != 0) return hipErrorInvalidValue;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -139,6 +223,9 @@ const char *kld_status_str(int s) {
     case KLD_EWORKSPACE: return "KLD_EWORKSPACE: workspace missing, too small or not 16-byte aligned";
     case KLD_EUNSUPPORTED: return "KLD_EUNSUPPORTED: valid request the library does not serve (alignment, d % 8)";
     case KLD_EHIP: return "KLD_EHIP: HIP runtime error";
+    case KLD_ETOOBIG:
+      return "KLD_ETOOBIG: the request needs more workspace than the static scratch of "
+             "kld_from_logits_noalloc holds";
     default: return "KLD_UNKNOWN";
   }
 }
@@ -168,45 +255,27 @@ kld_status kld_from_logits(const void *ref, const void *cand, int dtype, int64_t
                            int64_t ld_ref, int64_t ld_cand, const int32_t *target,
                            const kld_rows *out, const kld_topk *topk, void *ws, size_t ws_bytes,
                            void *stream, const kld_launch_opts *opts) {
-  if (dtype != KLD_F32 && dtype != KLD_BF16) return KLD_EDTYPE;
-  if (n < 0 || v < 0) return KLD_EINVAL;
-  if (!out) return KLD_EINVAL;
-  if (n == 0) return KLD_OK;
-  if (v < 1 || v > 0x7fffffffLL) return KLD_ESHAPE;
-  if (!ref || !cand || !out->kl) return KLD_EINVAL;
-  if (ld_ref < v || ld_cand < v) return KLD_ESHAPE;
-  if ((out->nll_ref || out->nll_cand) && !target) return KLD_EINVAL;
-  if (topk && v < KLD_TOPK) return KLD_ESHAPE;
-  const size_t esize = dtype == KLD_F32 ? 4 : 2;
-  if (!al(ref, esize) || !al(cand, esize) || !al(target, 4) || !rows_aligned(out) ||
-      !topk_aligned(topk))
-    return KLD_EUNSUPPORTED;
+  const kld_status st = check_from_logits(ref, cand, dtype, n, v, ld_ref, ld_cand, target, out, topk);
+  if (st != KLD_OK || n == 0) return st;
   const size_t need = kld_workspace_size(KLD_OP_FROM_LOGITS, n, v, 0, topk ? KLD_FLAG_TOPK : 0);
   if (!ws || ws_bytes < need || !aligned16(ws)) return KLD_EWORKSPACE;
+  return run_from_logits(ref, cand, dtype, n, v, ld_ref, ld_cand, target, out, topk, ws, stream,
+                         opts);
+}
 
-  LogitsGeom g = logits_geom(n, v);
-  LogitsArgs a;
-  a.ref = ref; a.cand = cand; a.dtype = dtype; a.n = n; a.v = v;
-  a.ld_ref = ld_ref; a.ld_cand = ld_cand; a.chunk = g.chunk; a.splits = g.splits;
-  a.aligned = aligned16(ref) && aligned16(cand) && (ld_ref * esize) % 16 == 0 &&
-              (ld_cand * esize) % 16 == 0;
-  a.two = true;
-  a.target = target;
-  a.out = RowsOut{out->kl, out->nll_ref, out->nll_cand, out->lse_ref, out->lse_cand,
-                  out->argmax_ref, out->argmax_cand};
-  a.stream = as_stream(stream);
-  a.ev = events_of(opts);
-
-  Carver c(ws);
-  const LogitsWs w = logits_carve(n, v, topk != nullptr, &c);
-  if (launch_logits_state(a, w.part, w.keys) != hipSuccess) return KLD_EHIP;
-  if (launch_logits_finalize(a, w.part, w.lse, nullptr) != hipSuccess) return KLD_EHIP;
-  if (topk) {
-    const TopkOut to{topk->ids_ref, topk->lp_ref, topk->ids_cand, topk->lp_cand};
-    if (launch_topk_merge(w.keys, g.splits, 2, n, w.lse, to, a.stream) != hipSuccess)
-      return KLD_EHIP;
-  }
-  return KLD_OK;
+kld_status kld_from_logits_noalloc(const void *ref, const void *cand, int dtype, int64_t n,
+                                   int64_t v, int64_t ld_ref, int64_t ld_cand,
+                                   const int32_t *target, const kld_rows *out,
+                                   const kld_topk *topk, void *stream,
+                                   const kld_launch_opts *opts) {
+  const kld_status st = check_from_logits(ref, cand, dtype, n, v, ld_ref, ld_cand, target, out, topk);
+  if (st != KLD_OK || n == 0) return st;
+  const size_t need = kld_workspace_size(KLD_OP_FROM_LOGITS, n, v, 0, topk ? KLD_FLAG_TOPK : 0);
+  if (need == 0 || need > (size_t)KLD_NOALLOC_SCRATCH_BYTES) return KLD_ETOOBIG;
+  void *ws = nullptr;
+  if (device_scratch(&ws) != hipSuccess) return KLD_EHIP;
+  return run_from_logits(ref, cand, dtype, n, v, ld_ref, ld_cand, target, out, topk, ws, stream,
+                         opts);
 }
 
 kld_status kld_fused_head(const uint16_t *W, int64_t v, int64_t d, const uint16_t *h_ref,

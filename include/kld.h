@@ -43,7 +43,8 @@
  *    is checked before anything is launched; on an error nothing is launched
  *    and nothing is written.  n == 0 is a valid no-op.  A failed launch
  *    returns KLD_EHIP.
- *  - No global mutable state: calls are thread-safe.  Results are bitwise
+ *  - No global mutable state (except the static scratch of
+ *    kld_from_logits_noalloc): calls are thread-safe.  Results are bitwise
  *    deterministic (fixed-order merges, no floating-point atomics).
  *  - Non-finite inputs: a -inf logit is a zero-probability id; a finite
  *    reference logit against a -inf candidate logit makes KL +inf; a row with
@@ -66,6 +67,7 @@ extern "C" {
 #define KLD_MAX_QUANTILES 16
 #define KLD_MAX_THRESHOLDS 16
 #define KLD_MAX_REPLICATES 16384
+#define KLD_NOALLOC_SCRATCH_BYTES (16u << 20)   /* static scratch of kld_from_logits_noalloc */
 
 typedef enum kld_status {
   KLD_OK = 0,
@@ -74,7 +76,8 @@ typedef enum kld_status {
   KLD_EDTYPE = 3,       /* unknown dtype code */
   KLD_EWORKSPACE = 4,   /* workspace missing, smaller than kld_workspace_size() or not 16-byte aligned */
   KLD_EUNSUPPORTED = 5, /* valid request the library does not serve (alignment, d % 8) */
-  KLD_EHIP = 6          /* the HIP runtime reported an error at launch */
+  KLD_EHIP = 6,         /* the HIP runtime reported an error at launch */
+  KLD_ETOOBIG = 7       /* kld_from_logits_noalloc: needs more than its static scratch */
 } kld_status;
 
 typedef enum kld_dtype {
@@ -149,6 +152,30 @@ kld_status kld_from_logits(const void *ref, const void *cand, int dtype, int64_t
                            int64_t ld_ref, int64_t ld_cand, const int32_t *target,
                            const kld_rows *out, const kld_topk *topk, void *ws, size_t ws_bytes,
                            void *stream, const kld_launch_opts *opts);
+
+/*
+ * kld_from_logits_noalloc -- kld_from_logits for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, outputs and results as
+ * kld_from_logits, without the workspace: the library's own static device
+ * buffer of KLD_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU serves instead, so the
+ * call allocates nothing (no hipMalloc, no allocating library routine).
+ *
+ * Limit: a request whose kld_workspace_size(KLD_OP_FROM_LOGITS, n, v, 0,
+ * flags) exceeds KLD_NOALLOC_SCRATCH_BYTES is rejected with KLD_ETOOBIG
+ * before anything is launched (at v = 248,320: about 15,000 rows with top-64,
+ * about 600,000 without).
+ * The buffer belongs to the calling thread's current device, which must be
+ * the device of `stream`.  Every call on one GPU shares that GPU's buffer:
+ * calls that overlap on one GPU (concurrent streams or threads) race and
+ * must be serialised by the caller.  The buffer is held until the process
+ * ends.  The first call on a device looks up the buffer's address once.
+ */
+kld_status kld_from_logits_noalloc(const void *ref, const void *cand, int dtype, int64_t n,
+                                   int64_t v, int64_t ld_ref, int64_t ld_cand,
+                                   const int32_t *target, const kld_rows *out,
+                                   const kld_topk *topk, void *stream,
+                                   const kld_launch_opts *opts);
 
 /*
  * kld_fused_head -- score n positions from final hidden states through one

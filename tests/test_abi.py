@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 def test_abi_version_and_status_strings():
     assert kld.kld_abi_version() == 1
     assert kld.kld_status_str(0) == "KLD_OK"
-    for c in range(1, 7):
+    for c in range(1, 8):
         assert kld.kld_status_str(c).startswith("KLD_E")
 
 
@@ -292,3 +292,31 @@ def test_alignment_checked_everywhere():
     q = (ctypes.c_double * 1)(0.5)
     assert lib.kld_paired_bootstrap(20, 16, 16, 8, 16, 3, 16, 10, q, 1, 16, 16, 16, 1 << 20,
                                     None) == 5
+
+
+def test_noalloc_validation_fails_closed():
+    """kld_from_logits_noalloc checks every argument like kld_from_logits and
+    rejects requests beyond its static scratch before any HIP call."""
+    lib = kld.lib()
+
+    def call(ref=16, cand=16, dtype=0, n=4, v=100, ld_ref=100, ld_cand=100, target=None,
+             rows=None, topk=None):
+        rows = rows if rows is not None else _rows()
+        return lib.kld_from_logits_noalloc(ref, cand, dtype, n, v, ld_ref, ld_cand, target,
+                                           ctypes.byref(rows), topk, None, None)
+    assert call(dtype=4) == 3
+    assert call(n=-1) == 1
+    assert call(ref=None) == 1
+    assert call(rows=_rows(kl=None)) == 1
+    assert call(ld_cand=99) == 2
+    assert call(ref=18) == 5
+    nll_rows = binding._Rows(16, 16, None, None, None, None, None)
+    assert call(rows=nll_rows) == 1
+    tk = binding._Topk(16, 16, 16, 16)
+    assert call(v=63, ld_ref=63, ld_cand=63, topk=ctypes.byref(tk)) == 2
+    assert call(n=0) == 0
+    # beyond the static scratch: 20,000 rows of V = 248,320 with top-64
+    v = 248_320
+    assert kld.kld_workspace_size(0, 20_000, v, 0, 1) > 16 << 20
+    assert call(n=20_000, v=v, ld_ref=v, ld_cand=v, topk=ctypes.byref(tk)) == 7
+    assert kld.kld_workspace_size(0, 4096, v, 0, 1) <= 16 << 20
