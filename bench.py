@@ -139,14 +139,68 @@ def _oracle_scores(za, zb, t, k=None, block=4):
     return {key: np.concatenate([p[key] for p in parts]) for key in parts[0]}
 
 
+_HIP = None
+
+
+def _hip():
+    """The HIP runtime this process already uses (the one torch loaded)."""
+    global _HIP
+    if _HIP is None:
+        import ctypes
+        import torch
+        torch.cuda.init()
+        with open("/proc/self/maps") as f:
+            path = next(l.split()[-1] for l in f if "libamdhip64" in l)
+        h = ctypes.CDLL(path)
+        h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                          ctypes.c_void_p]
+        h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        _HIP = h
+    return _HIP
+
+
+class TimingEvent:
+    """A HIP timing event created with hipEventDisableSystemFence: recording it
+    takes a timestamp without the system-scope cache writeback and
+    invalidation a default event performs, which would slow the kernels that
+    follow it (a default event pair around each launch costs a ~200 us step
+    about 24 us).  Used only to time kernels; `cuda_event` is the raw handle
+    the library records around its dominant kernel."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        h = ctypes.c_void_p()
+        if _hip().hipEventCreateWithFlags(ctypes.byref(h), self.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        self.cuda_event = h.value
+
+    def record(self):
+        import torch
+        if _hip().hipEventRecord(self.cuda_event, torch.cuda.current_stream().cuda_stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end):
+        import ctypes
+        ms = ctypes.c_float()
+        if _hip().hipEventElapsedTime(ctypes.byref(ms), self.cuda_event, end.cuda_event) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        if _HIP is not None and getattr(self, "cuda_event", None):
+            _HIP.hipEventDestroy(self.cuda_event)
+
+
 def _timeit(step, steps, warmup, n_ev=1):
     """Run warmup untimed steps, then `steps` timed ones; step(i, evs) gets a
     list of n_ev (start, stop) event pairs for the dominant kernel's launches
     (None during warmup).  Returns (elapsed seconds, mean dominant-kernel ms
     per launch)."""
     import torch
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(n_ev)] for _ in range(steps)]
+    evs = [[(TimingEvent(), TimingEvent()) for _ in range(n_ev)] for _ in range(steps)]
     for i in range(warmup):
         step(i, None)
     torch.cuda.synchronize()
@@ -642,7 +696,7 @@ def golden_f32(steps, warmup, cpu_sample):
     for _ in range(warmup):
         step(0, None)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = TimingEvent(), TimingEvent()
     e0.record()
     kld.kld_golden_export(ra, tg, out=rec)
     e1.record()
@@ -714,8 +768,7 @@ def windows_paired(steps, warmup, cpu_sample):
                 "totals": torch.empty(2 + len(thr), dtype=torch.float64, device=dev)}
     wa, wb = wout(), wout()
     ws_p = torch.empty(kld.kld_workspace_size(5, nclust, nrep), dtype=torch.uint8, device=dev)
-    ev_p = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(steps)]
+    ev_p = [(TimingEvent(), TimingEvent()) for _ in range(steps)]
     box = {"k": 0}
 
     def step(i, ev):
@@ -955,15 +1008,39 @@ def record_traffic(d):
 
 def counter_table(d):
     """Per-kernel averages of every counter in the rocprofv3 counter runs
-    under d, one line per (kernel, counter)."""
+    under d (rows already summed over the counter's instances), with the
+    kernel duration and, where GRBM_GUI_ACTIVE and SQ_VALU_MFMA_BUSY_CYCLES
+    were collected, the shader clock (GRBM_GUI_ACTIVE summed over the 8 XCDs,
+    / 8, over the duration) and the MFMA utilisation (busy cycles summed over
+    the 1,024 SIMDs over 1,024 x the per-XCD active cycles)."""
     from collections import defaultdict
     rows = _read_counter_csv(d)
-    acc = defaultdict(lambda: defaultdict(float))
+    vals = defaultdict(lambda: defaultdict(float))
+    dur, name = {}, {}
     for r in rows:
-        acc[(r["Kernel_Name"][:90], r["Counter_Name"])][r["Dispatch_Id"]] += float(r["Counter_Value"])
-    for (k, c), disp in sorted(acc.items()):
-        vals = list(disp.values())
-        print(f"{k:90s} {c:28s} n={len(vals):3d} avg={sum(vals) / len(vals):.6g}")
+        key = (f'{r.get("Kernel_Name", "")[:60]} grid={r.get("Grid_Size", "?")}', r["Dispatch_Id"])
+        vals[key][r["Counter_Name"]] += float(r["Counter_Value"])
+        dur[key] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    by_kernel = defaultdict(list)
+    for (k, disp), c in vals.items():
+        by_kernel[k].append((dur[(k, disp)], c))
+    for k, lst in sorted(by_kernel.items()):
+        if max(x[0] for x in lst) < 20_000:   # skip launches under 20 us
+            continue
+        ns = sum(x[0] for x in lst) / len(lst)
+        avg = defaultdict(float)
+        for _, c in lst:
+            for cn, v in c.items():
+                avg[cn] += v / len(lst)
+        line = f"{k} n={len(lst)} avg_ms={ns / 1e6:.3f}"
+        for cn in sorted(avg):
+            line += f" {cn}={avg[cn]:.5g}"
+        if "GRBM_GUI_ACTIVE" in avg and ns >= 1e6:   # clocks only for launches of 1 ms or more
+            per_xcd = avg["GRBM_GUI_ACTIVE"] / 8.0
+            line += f" clock_GHz={per_xcd / ns:.3f}"
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+                line += f" mfma_util={avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (per_xcd * 1024):.3f}"
+        print(line)
 
 
 # --------------------------------------------------------------------------

@@ -12,7 +12,8 @@
 // value order; NaN patterns sort above +inf).  Each pass builds per-block LDS
 // histograms of the next 8 bits for every rank whose prefix matches and adds
 // them into global integer histograms; one small kernel then fixes the next
-// digit of every rank.
+// digit of every rank.  Inputs of at most 16,384 values take one block that
+// does all of this in LDS (one launch).
 #include "kld_device.hpp"
 #include "kld_launch.hpp"
 
@@ -168,6 +169,116 @@ __global__ __launch_bounds__(SCAN_T) void summary_scan_kernel(
   }
 }
 
+// ---- small inputs: the whole summary in one block ---------------------------
+// For n <= kSmallMax the values fit in LDS, so one 1024-thread block takes the
+// sums (per-thread strided partials, then a fixed butterfly per wave and a
+// fixed order over the waves) and the same 4-pass radix select of every rank,
+// with block barriers between the passes instead of kernel launches: one
+// launch instead of nine, which is most of the cost at these sizes.
+constexpr int SMALL_T = 1024;
+constexpr int kSmallMax = 16384;
+
+__device__ __forceinline__ SumPart shfl_xor_part(const SumPart &s, int m) {
+  SumPart o;
+  o.kl = __shfl_xor(s.kl, m); o.nll_ref = __shfl_xor(s.nll_ref, m);
+  o.nll_cand = __shfl_xor(s.nll_cand, m);
+  o.top1 = __shfl_xor(s.top1, m); o.nonfinite = __shfl_xor(s.nonfinite, m);
+  return o;
+}
+
+__global__ __launch_bounds__(SMALL_T) void summary_small_kernel(
+    const float *__restrict__ kl, const int32_t *__restrict__ am_ref,
+    const int32_t *__restrict__ am_cand, const float *__restrict__ nll_ref,
+    const float *__restrict__ nll_cand, int n, SummaryRanks ranks, SummaryQuantiles qs,
+    double *__restrict__ out) {
+  __shared__ uint32_t keys[kSmallMax];
+  __shared__ uint32_t hist[kSummaryMaxRanks][256];
+  __shared__ uint32_t pre[kSummaryMaxRanks], rk[kSummaryMaxRanks];
+  __shared__ SumPart wpart[SMALL_T / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nranks = ranks.count;
+
+  SumPart s = {0.0, 0.0, 0.0, 0ull, 0ull};
+  for (int i = tid; i < n; i += SMALL_T) {
+    const float x = kl[i];
+    keys[i] = __float_as_uint(x);
+    s.kl += (double)x;
+    if (!isfinite(x)) s.nonfinite += 1;
+    if (am_ref) s.top1 += am_ref[i] == am_cand[i] ? 1 : 0;
+    if (nll_ref) { s.nll_ref += (double)nll_ref[i]; s.nll_cand += (double)nll_cand[i]; }
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {   // the same butterfly in every wave: a fixed order
+    const SumPart o = shfl_xor_part(s, m);
+    s = (lane & m) ? add(o, s) : add(s, o);
+  }
+  if (lane == 0) wpart[wave] = s;
+  if (tid < nranks) { pre[tid] = 0; rk[tid] = ranks.rank[tid]; }
+
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    const uint32_t hmask = pass == 0 ? 0u : (0xffffffffu << (32 - 8 * pass));
+    for (int i = tid; i < nranks * 256; i += SMALL_T) hist[i / 256][i % 256] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += SMALL_T) {
+      const uint32_t key = keys[i];
+      const uint32_t dig = (key >> shift) & 0xffu;
+      for (int r = 0; r < nranks; ++r)
+        if (((key ^ pre[r]) & hmask) == 0) atomicAdd(&hist[r][dig], 1u);
+    }
+    __syncthreads();
+    // one wave per rank: lane l owns bins 4 l .. 4 l + 3; an inclusive scan
+    // over the lanes finds the bin that holds the rank
+    for (int r = wave; r < nranks; r += SMALL_T / 64) {
+      uint32_t c[4], s4 = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) { c[b] = hist[r][4 * lane + b]; s4 += c[b]; }
+      uint32_t inc = s4;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_up(inc, o);
+        if (lane >= o) inc += t;
+      }
+      const uint32_t k = rk[r];
+      uint32_t below = inc - s4, bel = 0;
+      int dig = -1;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if (dig < 0 && below + c[b] > k) { dig = 4 * lane + b; bel = below; }
+        below += c[b];
+      }
+      const uint64_t m = __ballot(dig >= 0);
+      const int src = m ? __ffsll((long long)m) - 1 : 0;
+      const int dd = m ? __shfl(dig, src) : 255;
+      const uint32_t bb = m ? __shfl(bel, src) : 0u;
+      if (lane == 0) {
+        pre[r] |= (uint32_t)dd << shift;
+        rk[r] = k - bb;
+      }
+    }
+    __syncthreads();
+  }
+  if (tid != 0) return;
+  s = wpart[0];
+  for (int w = 1; w < SMALL_T / 64; ++w) s = add(s, wpart[w]);
+  const double nan = __builtin_nan(""), dn = (double)n;
+  const bool have_nll = nll_ref != nullptr;
+  out[0] = s.kl / dn;
+  out[1] = am_ref ? (double)s.top1 / dn : nan;
+  const double mr = s.nll_ref / dn, mc = s.nll_cand / dn;
+  out[2] = have_nll ? mr : nan;
+  out[3] = have_nll ? mc : nan;
+  out[4] = have_nll ? exp(mr) : nan;
+  out[5] = have_nll ? exp(mc) : nan;
+  out[6] = have_nll ? exp(mc) / exp(mr) : nan;
+  out[7] = (double)s.nonfinite;
+  for (int i = 0; i < qs.count; ++i) {
+    const double lo = (double)__uint_as_float(pre[2 * i]);
+    const double hi = (double)__uint_as_float(pre[2 * i + 1]);
+    out[8 + i] = lo + qs.frac[i] * (hi - lo);
+  }
+}
+
 }  // namespace
 
 int summary_blocks(int64_t n) {
@@ -178,6 +289,12 @@ int summary_blocks(int64_t n) {
 }
 
 hipError_t launch_summary(const SummaryArgs &a, void *ws) {
+  if (a.n <= kSmallMax) {
+    hipLaunchKernelGGL(summary_small_kernel, dim3(1), dim3(SMALL_T), 0, a.stream, a.kl,
+                       a.argmax_ref, a.argmax_cand, a.nll_ref, a.nll_cand, (int)a.n, a.ranks, a.qs,
+                       a.out);
+    return hipGetLastError();
+  }
   const int nb = summary_blocks(a.n);
   const int R = a.ranks.count;
   char *p = (char *)ws;

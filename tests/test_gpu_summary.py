@@ -22,7 +22,7 @@ def _run(kl, am_r=None, am_c=None, nr=None, nc=None, qs=QS):
     return kld.summary_dict(out, qs)
 
 
-@pytest.mark.parametrize("n", [1, 2, 7, 2047, 100_003, 262_144])
+@pytest.mark.parametrize("n", [1, 2, 7, 2047, 16_384, 16_385, 100_003, 262_144])
 def test_summary_matches_oracle(n):
     need_gpu()
     g = np.random.default_rng(n)
