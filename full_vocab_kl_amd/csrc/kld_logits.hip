@@ -594,16 +594,46 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
   }
 }
 
+__device__ __forceinline__ RowStateD shfl_xor_d(const RowStateD &s, int m) {
+  RowStateD o;
+  o.ma = __shfl_xor(s.ma, m); o.mb = __shfl_xor(s.mb, m);
+  o.sa = __shfl_xor(s.sa, m); o.t = __shfl_xor(s.t, m); o.sb = __shfl_xor(s.sb, m);
+  o.ia = __shfl_xor(s.ia, m); o.ib = __shfl_xor(s.ib, m);
+  return o;
+}
+
+// One group of 2^lg lanes per row (2^lg >= splits, a divisor of the wave):
+// lane k loads split k's state (the empty state past the last split), the
+// group merges them in f64 by a butterfly in split order (the lower split
+// always first, so every lane computes the same bits), and lane 0 finishes
+// the row.  The target logits are loaded first, so that their latency
+// overlaps the merge.
 template <typename T>
 __global__ __launch_bounds__(256) void finalize_rows_kernel(
-    const RowState *__restrict__ part, int splits, int64_t n, const T *__restrict__ ref,
+    const RowState *__restrict__ part, int splits, int lg, int64_t n, const T *__restrict__ ref,
     const T *__restrict__ cand, int64_t ld_ref, int64_t ld_cand, int64_t v,
     const int32_t *__restrict__ target, RowsOut out, double *__restrict__ lse_d /*[2][n]*/,
     float *__restrict__ target_lp) {
-  const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (row >= n) return;
-  RowStateD s = to_d(part[row * splits]);
-  for (int i = 1; i < splits; ++i) s = merge_d(s, to_d(part[row * splits + i]));
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = gid >> lg;
+  const int k = (int)(gid & ((1 << lg) - 1));
+  const bool live = row < n;
+  bool tok = false;
+  float za = 0.f, zb = 0.f;
+  if (live && k == 0 && target) {
+    const int32_t tg = target[row];
+    tok = tg >= 0 && (int64_t)tg < v;
+    if (tok) {
+      za = to_f32(ref[row * ld_ref + tg]);
+      zb = to_f32(cand[row * ld_cand + tg]);
+    }
+  }
+  RowStateD s = live && k < splits ? to_d(part[row * splits + k]) : empty_state_d();
+  for (int m = 1; m < (1 << lg); m <<= 1) {
+    const RowStateD o = shfl_xor_d(s, m);
+    s = (k & m) ? merge_d(o, s) : merge_d(s, o);
+  }
+  if (!live || k != 0) return;
   double la, lb;
   const RowResult r = finish_d(s, &la, &lb);
   if (lse_d) { lse_d[row] = la; lse_d[n + row] = lb; }
@@ -613,13 +643,10 @@ __global__ __launch_bounds__(256) void finalize_rows_kernel(
   if (out.argmax_ref) out.argmax_ref[row] = r.ia;
   if (out.argmax_cand) out.argmax_cand[row] = r.ib;
   if (target) {
-    const int32_t tg = target[row];
-    const bool ok = tg >= 0 && (int64_t)tg < v;
     const float nan = __builtin_nanf("");
-    if (out.nll_ref) out.nll_ref[row] = ok ? (float)(la - (double)to_f32(ref[row * ld_ref + tg])) : nan;
-    if (out.nll_cand)
-      out.nll_cand[row] = ok ? (float)(lb - (double)to_f32(cand[row * ld_cand + tg])) : nan;
-    if (target_lp) target_lp[row] = ok ? (float)((double)to_f32(ref[row * ld_ref + tg]) - la) : nan;
+    if (out.nll_ref) out.nll_ref[row] = tok ? (float)(la - (double)za) : nan;
+    if (out.nll_cand) out.nll_cand[row] = tok ? (float)(lb - (double)zb) : nan;
+    if (target_lp) target_lp[row] = tok ? (float)((double)za - la) : nan;
   }
 }
 
@@ -657,13 +684,18 @@ hipError_t launch_partial_plain(const LogitsArgs &a, RowState *part) {
   return launch_partial_t<T, VEC, U, false, true, false>(a, part, nullptr);
 }
 
+static_assert(kMaxSplits <= 64, "a row's group of finalize lanes fits in one wave");
+
 template <typename T>
 hipError_t launch_finalize(const LogitsArgs &a, const RowState *part, double *lse_d,
                            float *target_lp) {
-  const unsigned blocks = (unsigned)((a.n + 255) / 256);
+  int lg = 0;
+  while ((1 << lg) < a.splits) ++lg;   // splits <= kMaxSplits = 64: a group fits a wave
+  const int64_t threads = a.n << lg;
+  const unsigned blocks = (unsigned)((threads + 255) / 256);
   hipLaunchKernelGGL((finalize_rows_kernel<T>), dim3(blocks), dim3(256), 0, a.stream, part,
-                     a.splits, a.n, (const T *)a.ref, (const T *)a.cand, a.ld_ref, a.ld_cand, a.v,
-                     a.target, a.out, lse_d, target_lp);
+                     a.splits, lg, a.n, (const T *)a.ref, (const T *)a.cand, a.ld_ref, a.ld_cand,
+                     a.v, a.target, a.out, lse_d, target_lp);
   return hipGetLastError();
 }
 

@@ -194,6 +194,7 @@ __global__ __launch_bounds__(SMALL_T) void summary_small_kernel(
   __shared__ uint32_t keys[kSmallMax];
   __shared__ uint32_t hist[kSummaryMaxRanks][256];
   __shared__ uint32_t pre[kSummaryMaxRanks], rk[kSummaryMaxRanks];
+  __shared__ int lead[kSummaryMaxRanks];   // the first rank with the same prefix
   __shared__ SumPart wpart[SMALL_T / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nranks = ranks.count;
@@ -218,13 +219,29 @@ __global__ __launch_bounds__(SMALL_T) void summary_small_kernel(
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     const uint32_t hmask = pass == 0 ? 0u : (0xffffffffu << (32 - 8 * pass));
+    // ranks whose prefixes agree share one histogram (in pass 0 all do)
+    if (tid < nranks) {
+      int l = tid;
+      while (l > 0 && pre[l - 1] == pre[tid]) --l;   // a run of equal prefixes shares its first
+      lead[tid] = l;
+    }
     for (int i = tid; i < nranks * 256; i += SMALL_T) hist[i / 256][i % 256] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += SMALL_T) {
-      const uint32_t key = keys[i];
+    for (int i0 = 0; i0 < n; i0 += SMALL_T) {   // (i0 is uniform: whole waves loop together)
+      const int i = i0 + tid;
+      const uint32_t key = i < n ? keys[i] : 0u;
       const uint32_t dig = (key >> shift) & 0xffu;
-      for (int r = 0; r < nranks; ++r)
-        if (((key ^ pre[r]) & hmask) == 0) atomicAdd(&hist[r][dig], 1u);
+      // the lanes holding the wave's first digit add their count with one
+      // atomic (most keys share the leading digits); the rest add their own
+      const uint32_t d0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)dig);
+      for (int r = 0; r < nranks; ++r) {
+        if (lead[r] != r) continue;
+        const bool in = i < n && ((key ^ pre[r]) & hmask) == 0;
+        const uint64_t same = __ballot(in && dig == d0);
+        if (same != 0ull && lane == __ffsll((long long)same) - 1)
+          atomicAdd(&hist[r][d0], (uint32_t)__popcll(same));
+        if (in && dig != d0) atomicAdd(&hist[r][dig], 1u);
+      }
     }
     __syncthreads();
     // one wave per rank: lane l owns bins 4 l .. 4 l + 3; an inclusive scan
@@ -232,7 +249,7 @@ __global__ __launch_bounds__(SMALL_T) void summary_small_kernel(
     for (int r = wave; r < nranks; r += SMALL_T / 64) {
       uint32_t c[4], s4 = 0;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) { c[b] = hist[r][4 * lane + b]; s4 += c[b]; }
+      for (int b = 0; b < 4; ++b) { c[b] = hist[lead[r]][4 * lane + b]; s4 += c[b]; }
       uint32_t inc = s4;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
