@@ -15,9 +15,9 @@
 // complemented id, so equal values rank the lower id first).  Per side, an
 // element becomes a candidate only if its value reaches a threshold that at
 // least 64 elements of the block's range are known to reach: at rounds 0, 1,
-// 3, 7, ... every wave finds the 16th largest of its 64 lanes' running maxima
-// (distinct elements) and publishes it; the smallest of the four waves'
-// values is reached by 64 distinct elements.  Candidates are appended to a
+// 2, 3, 5, 7, 11, 15, ... every wave finds the 16th largest of its 64 lanes'
+// running maxima (distinct elements) and publishes it; the smallest of the
+// four waves' values is reached by 64 distinct elements.  Candidates are appended to a
 // per-wave LDS buffer (ballot + mbcnt offsets, no atomics, no block barrier);
 // a wave whose buffer fills sorts it in registers, keeps its 64 best keys and
 // from then on also requires keys above the 64th.  At the end each wave drops
@@ -284,13 +284,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
   const int rounds = (len + kRound - 1) / kRound;
   const int tofs = (int)threadIdx.x * VEC;   // the thread's first offset in a round
 
-  // Round r + 1's rows are loaded while round r is processed.  Aligned rows
+  // Rounds r + 1 .. r + DEPTH - 1 are loaded while round r is processed
+  // (three rounds in flight for bf16 with top-k, whose rounds are one vector
+  // per side: two would leave too few bytes in flight per CU).  Aligned rows
   // are read through buffer resources over the whole vectors of [lo, hi):
   // loads past them return zeros and touch no memory, so the loop carries no
   // bounds checks; the last round masks offsets past hi to -inf and reads a
   // vector that straddles hi element by element.
   using Raw = typename RawOf<T>::type;
-  Raw qa[2][U], qb[2][U];   // two rounds in flight: round r in slot r % 2
+  constexpr int DEPTH = (TOPK && sizeof(T) == 2) ? 3 : 2;
+  Raw qa[DEPTH][U], qb[DEPTH][U];   // round r in slot r % DEPTH
   const int nvec = len / VEC * VEC;   // ids in whole vectors
   __amdgpu_buffer_rsrc_t rsa, rsb;
   if constexpr (ALIGNED) {
@@ -301,7 +304,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
   }
   // Load round r into slot sl.  Rounds past the last one load nothing (zeros
   // from the buffer resources, -inf from the checked path), so the loop
-  // fetches two ahead without conditions.
+  // fetches DEPTH rounds ahead without conditions.
   auto fetch = [&](int r, int sl) {
     const int e0 = r * kRound + tofs;
 #pragma unroll
@@ -373,29 +376,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
       bma = fmaxf(bma, vma[u]);
       if (TWO) bmb = fmaxf(bmb, vmb[u]);
     }
+    // Lowest id in this batch whose value equals m (m is one of its
+    // non-NaN values): one bit per element, then the lowest set bit -- no
+    // per-element id arithmetic, which the compiler would otherwise keep
+    // live across the loop.
+    auto first_id = [&](const Raw (&c)[U], float m) -> int {
+      static_assert(U * VEC <= 32, "one bit per element of a round");
+      uint32_t bits = 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) bits |= (elem(c[u], j) == m ? 1u : 0u) << (u * VEC + j);
+      const int k = __builtin_ctz(bits);
+      return id0 + (k / VEC) * kStride + (k % VEC);
+    };
     if (bma > ma) {   // new maximum: locate its lowest id in this batch, rebase the sums
-      int id = kNoId;
-#pragma unroll
-      for (int u = U - 1; u >= 0; --u)
-#pragma unroll
-        for (int j = VEC - 1; j >= 0; --j)
-          if (elem(ca[u], j) == bma) id = id0 + u * kStride + j;
+      const int id = first_id(ca, bma);
       const float f = rescale(ma, bma);
       if (TWO && sa != 0.f) t = fmaf(-sa, bma - ref_of(ma), t);
       t *= f; sa *= f; ma = bma; ia = id;
     }
     if (TWO && bmb > mb) {
-      int id = kNoId;
-#pragma unroll
-      for (int u = U - 1; u >= 0; --u)
-#pragma unroll
-        for (int j = VEC - 1; j >= 0; --j)
-          if (elem(cb[u], j) == bmb) id = id0 + u * kStride + j;
+      const int id = first_id(cb, bmb);
       if (sa != 0.f) t = fmaf(sa, bmb - ref_of(mb), t);
       sb *= rescale(mb, bmb); mb = bmb; ib = id;
     }
     if constexpr (TOPK) {
-      if (((r + 1) & r) == 0) update();   // rounds 0, 1, 3, 7, ...
+      {   // rounds 0, 1, 2, 3, 5, 7, 11, 15, 23, 31, ...: r + 1 = 2^k or 3 * 2^k
+        const int x = r + 1, y = x / 3;
+        if ((x & (x - 1)) == 0 || (x % 3 == 0 && (y & (y - 1)) == 0)) update();
+      }
       // stage the vectors whose maximum reaches the threshold; their elements
       // are filtered in batches (flush), so the common path has no
       // per-element work and a single branch per vector and side
@@ -458,7 +468,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
 #pragma unroll
     for (int u = 0; u < U; ++u) { ca[u] = qa[sl][u]; cb[u] = qb[sl][u]; }
     if (!last) {
-      fetch(r + 2, sl);
+      fetch(r + DEPTH, sl);
       process(r, ca, cb, false, kRound);
       return;
     }
@@ -490,19 +500,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
   };
 
   if (rounds > 0) {
-    fetch(0, 0);
-    fetch(1, 1);
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) fetch(d, d);
     int r = 0;
-    for (; r + 2 < rounds; r += 2) {   // rounds r, r + 1: neither is the last
-      run(r, 0, false);
-      run(r + 1, 1, false);
+    for (; r + DEPTH < rounds; r += DEPTH) {   // none of these rounds is the last
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) run(r + d, d, false);
     }
-    if (r + 1 < rounds) {
-      run(r, 0, false);
-      run(r + 1, 1, true);
-    } else {
-      run(r, 0, true);
-    }
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)   // the 1 .. DEPTH rounds left
+      if (r + d < rounds) run(r + d, d, r + d == rounds - 1);
   }
 
   if constexpr (TOPK) {
