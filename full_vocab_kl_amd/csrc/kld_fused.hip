@@ -25,11 +25,14 @@
 // (vocab tile, position).  fused_finalize_kernel merges the partial states
 // of each position over all vocabulary tiles in a fixed order.
 //
-// Grid: one block per (vocab tile, position tile).  Consecutive hardware
-// block ids are dealt round-robin over the 8 XCDs; the block id is remapped
-// so that each XCD receives a contiguous range of tiles, position tiles
-// fastest, so all position tiles of one head tile run together on one XCD
-// and the head tile is fetched from HBM about once into that XCD's L2.
+// Grid: one block per (vocab tile, position tile).  Position tiles are
+// grouped 16 at a time and the groups run one after the other, so the hidden
+// states in use stay cache-resident at any number of positions.  Within a
+// group, consecutive hardware block ids are dealt round-robin over the 8
+// XCDs; the block id is remapped so that each XCD receives a contiguous range
+// of tiles, position tiles fastest, so all position tiles of one head tile run
+// together on one XCD and the head tile is fetched from HBM about once per
+// group into that XCD's L2.
 #include <type_traits>
 
 #include "kld.h"
@@ -106,6 +109,25 @@ __device__ __forceinline__ int logical_block(int b, int nb) {
   return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + slot;
 }
 
+// Position tiles are taken in groups of kGroupTiles: every vocabulary tile of
+// one group runs before the next group starts (blocks are dispatched in id
+// order), so the hidden states the resident blocks read -- one group, 16 x
+// 256 rows x d -- stay in the 256 MB cache however many positions the call
+// scores, and the head streams once per group.  Within a group the XCD-aware
+// order above applies.  kGroupTiles is a multiple of 8, so every group starts
+// on XCD 0.  Returns (vocabulary tile, position tile).
+constexpr int kGroupTiles = 16;
+static_assert(kGroupTiles % kXcds == 0, "groups start on XCD 0");
+__device__ __forceinline__ int2 tile_of_block(int b, int npt, int nvt) {
+  const int per = nvt * kGroupTiles;           // blocks of a full group
+  const int ngroups = (npt + kGroupTiles - 1) / kGroupTiles;
+  int g = b / per;
+  if (g > ngroups - 1) g = ngroups - 1;
+  const int gp = min(kGroupTiles, npt - g * kGroupTiles);   // position tiles of group g
+  const int L = logical_block(b - g * per, nvt * gp);
+  return make_int2(L / gp, g * kGroupTiles + L % gp);
+}
+
 // Buffer resource over `bytes` bytes at p (raw addressing, no stride): loads
 // at offsets past the range return zero and touch no memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64_t bytes) {
@@ -170,8 +192,8 @@ void fused_head_kernel(const uint16_t *__restrict__ W, const uint16_t *__restric
   static_assert(sizeof(u32x4) * UCHUNKS * NSLOT == kFusedLds, "ring = all of LDS");
   u32x4 *const smem = lds0;   // epilogue exchange area (after the loop)
 
-  const int L = logical_block((int)blockIdx.x, (int)gridDim.x);
-  const int vt = L / npt, pt = L % npt;
+  const int2 tile = tile_of_block((int)blockIdx.x, npt, (int)nvt);
+  const int vt = tile.x, pt = tile.y;
   const int64_t v0 = (int64_t)vt * BV, p0 = (int64_t)pt * PB;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wv = wave >> 1, wp = wave & 1;
