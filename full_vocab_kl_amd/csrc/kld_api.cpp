@@ -45,16 +45,18 @@ struct Carver {
 };
 
 // ---- logits path geometry --------------------------------------------------
-// Splits per row so that the grid holds about 4096 blocks (16 per CU), each
-// streaming at least 4096 ids; chunk is a multiple of 8 ids so that 16-byte
-// vectors never straddle a split for either dtype.
+// Splits per row so that the grid holds about 4096 blocks (16 per CU; the
+// nearest whole number of splits, so 4080 rows take one split each rather
+// than two half-rows), each streaming at least 4096 ids; chunk is a multiple
+// of 8 ids so that 16-byte vectors never straddle a split for either dtype.
 struct LogitsGeom {
   int splits;
   int64_t chunk;
 };
 
 LogitsGeom logits_geom(int64_t n, int64_t v) {
-  int64_t want = n > 0 ? (4096 + n - 1) / n : 1;
+  int64_t want = n > 0 ? (4096 + n / 2) / n : 1;
+  if (want < 1) want = 1;
   if (want > kMaxSplits) want = kMaxSplits;
   int64_t max_splits = (v + 4095) / 4096;
   if (max_splits < 1) max_splits = 1;
