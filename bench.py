@@ -157,6 +157,7 @@ def _hip():
         h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                           ctypes.c_void_p]
         h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        h.hipStreamWaitEvent.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
         _HIP = h
     return _HIP
 
@@ -194,19 +195,41 @@ class TimingEvent:
             _HIP.hipEventDestroy(self.cuda_event)
 
 
+_STREAMS = []
+
+
+def _streams():
+    """Two HIP streams (default priority) that consecutive steps alternate on."""
+    import torch
+    if not _STREAMS:
+        _STREAMS.extend(torch.cuda.Stream() for _ in range(2))
+    return _STREAMS
+
+
 def _timeit(step, steps, warmup, n_ev=1):
     """Run warmup untimed steps, then `steps` timed ones; step(i, evs) gets a
     list of n_ev (start, stop) event pairs for the dominant kernel's launches
-    (None during warmup).  Returns (elapsed seconds, mean dominant-kernel ms
-    per launch)."""
+    (None during warmup).  Step i runs on stream i % 2 and must use buffers
+    of its own parity.  Each timed step first waits for the end of the
+    previous step's last dominant launch, so the dominant kernels run one at
+    a time (each event pair brackets one launch) while one step's small
+    closing kernels (finalize, top-64 select, tail KLD, summary) overlap the
+    next step's dominant kernel, as a scorer fed batch after batch would run
+    them.  Returns (elapsed seconds, mean dominant-kernel ms per launch)."""
     import torch
     evs = [[(TimingEvent(), TimingEvent()) for _ in range(n_ev)] for _ in range(steps)]
+    ss = _streams()
     for i in range(warmup):
-        step(i, None)
+        with torch.cuda.stream(ss[i % 2]):
+            step(i, None)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(i, evs[i])
+        if i > 0 and _hip().hipStreamWaitEvent(ss[i % 2].cuda_stream, evs[i - 1][-1][1].cuda_event,
+                                                0) != 0:
+            raise RuntimeError("hipStreamWaitEvent failed")
+        with torch.cuda.stream(ss[i % 2]):
+            step(i, evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     kms = [a.elapsed_time(b) for e in evs for a, b in e]
@@ -313,22 +336,27 @@ def fused_window(steps, warmup, cpu_sample):
     dev = torch.device("cuda:0")
     W, hr, hc = _bf(w_np, dev), _bf(hr_np, dev), _bf(hc_np, dev)
     tg = torch.from_numpy(t_np).to(dev)
-    ws = torch.empty(kld.kld_workspace_size(1, n, v, d, 1), dtype=torch.uint8, device=dev)
-    ws_s = torch.empty(kld.kld_workspace_size(3, n, 0), dtype=torch.uint8, device=dev)
-    summ = torch.empty(8 + len(QUANTILES), dtype=torch.float64, device=dev)
-    tail = torch.empty(n, dtype=torch.float32, device=dev)
-    box = {}
+    # per stream parity: workspaces and outputs
+    ws = [torch.empty(kld.kld_workspace_size(1, n, v, d, 1), dtype=torch.uint8, device=dev)
+          for _ in range(2)]
+    ws_s = [torch.empty(kld.kld_workspace_size(3, n, 0), dtype=torch.uint8, device=dev)
+            for _ in range(2)]
+    summs = [torch.empty(8 + len(QUANTILES), dtype=torch.float64, device=dev) for _ in range(2)]
+    tails = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(2)]
+    outs = [None, None]
 
     def step(i, ev):
-        box["out"] = kld.kld_fused_head(W, hr, hc, tg, topk=True, ws=ws, out=box.get("out"),
-                                        events=ev[0] if ev else None)
-        o = box["out"]
-        kld.kld_topk_tail(o["ids_ref"], o["lp_ref"], o["ids_cand"], o["lp_cand"], v, out=tail)
+        k = i % 2
+        outs[k] = kld.kld_fused_head(W, hr, hc, tg, topk=True, ws=ws[k], out=outs[k],
+                                     events=ev[0] if ev else None)
+        o = outs[k]
+        kld.kld_topk_tail(o["ids_ref"], o["lp_ref"], o["ids_cand"], o["lp_cand"], v, out=tails[k])
         kld.kld_summary(o["kl"], o["argmax_ref"], o["argmax_cand"], o["nll_ref"], o["nll_cand"],
-                        quantiles=QUANTILES, ws=ws_s, out=summ)
+                        quantiles=QUANTILES, ws=ws_s[k], out=summs[k])
 
     elapsed, kernel_ms = _timeit(step, steps, warmup)
     flops = 4.0 * n * d * v
+    summ, tail, box = summs[0], tails[0], {"out": outs[0]}
     summary = kld.summary_dict(summ, QUANTILES)
     res = {
         "value": n * steps / elapsed, "unit": "positions/s", "ms_per_step": elapsed * 1e3 / steps,
@@ -377,19 +405,23 @@ def fused_batch(steps, warmup, cpu_sample):
     dev = torch.device("cuda:0")
     W, hr, hc = _bf(w_np, dev), _bf(hr_np, dev), _bf(hc_np, dev)
     tg = torch.from_numpy(t_np).to(dev)
-    ws = torch.empty(kld.kld_workspace_size(1, n, v, d, 0), dtype=torch.uint8, device=dev)
-    ws_s = torch.empty(kld.kld_workspace_size(3, n, 0), dtype=torch.uint8, device=dev)
-    summ = torch.empty(8 + len(QUANTILES), dtype=torch.float64, device=dev)
-    box = {}
+    ws = [torch.empty(kld.kld_workspace_size(1, n, v, d, 0), dtype=torch.uint8, device=dev)
+          for _ in range(2)]
+    ws_s = [torch.empty(kld.kld_workspace_size(3, n, 0), dtype=torch.uint8, device=dev)
+            for _ in range(2)]
+    summs = [torch.empty(8 + len(QUANTILES), dtype=torch.float64, device=dev) for _ in range(2)]
+    outs = [None, None]
 
     def step(i, ev):
-        box["out"] = kld.kld_fused_head(W, hr, hc, tg, ws=ws, out=box.get("out"),
-                                        events=ev[0] if ev else None)
-        o = box["out"]
+        k = i % 2
+        outs[k] = kld.kld_fused_head(W, hr, hc, tg, ws=ws[k], out=outs[k],
+                                     events=ev[0] if ev else None)
+        o = outs[k]
         kld.kld_summary(o["kl"], o["argmax_ref"], o["argmax_cand"], o["nll_ref"], o["nll_cand"],
-                        quantiles=QUANTILES, ws=ws_s, out=summ)
+                        quantiles=QUANTILES, ws=ws_s[k], out=summs[k])
 
     elapsed, kernel_ms = _timeit(step, steps, warmup)
+    summ, box = summs[0], {"out": outs[0]}
     flops = 4.0 * n * d * v
     summary = kld.summary_dict(summ, QUANTILES)
     res = {
@@ -453,28 +485,38 @@ def long_trace(steps, warmup, cpu_sample):
             keep_c.append(b[sel])
     t_np = synth.targets(synth.LONG_TRACE, range(n), v)
     tg = torch.from_numpy(t_np).to(dev)
-    ws = torch.empty(kld.kld_workspace_size(1, chunk, v, d, 1), dtype=torch.uint8, device=dev)
-    ws_s = torch.empty(kld.kld_workspace_size(3, n, 0), dtype=torch.uint8, device=dev)
-    summ = torch.empty(8 + len(QUANTILES), dtype=torch.float64, device=dev)
-    out = {k: torch.empty(n, dtype=dt, device=dev) for k, dt in (
-        ("kl", torch.float32), ("nll_ref", torch.float32), ("nll_cand", torch.float32),
-        ("lse_ref", torch.float32), ("lse_cand", torch.float32), ("argmax_ref", torch.int32),
-        ("argmax_cand", torch.int32))}
-    out.update({"ids_ref": torch.empty((n, 64), dtype=torch.int32, device=dev),
-                "ids_cand": torch.empty((n, 64), dtype=torch.int32, device=dev),
-                "lp_ref": torch.empty((n, 64), dtype=torch.float16, device=dev),
-                "lp_cand": torch.empty((n, 64), dtype=torch.float16, device=dev)})
-    views = [{k: x[c * chunk:(c + 1) * chunk] for k, x in out.items()} for c in range(nchunk)]
+    ws = [torch.empty(kld.kld_workspace_size(1, chunk, v, d, 1), dtype=torch.uint8, device=dev)
+          for _ in range(2)]
+    ws_s = [torch.empty(kld.kld_workspace_size(3, n, 0), dtype=torch.uint8, device=dev)
+            for _ in range(2)]
+    summs = [torch.empty(8 + len(QUANTILES), dtype=torch.float64, device=dev) for _ in range(2)]
+
+    def outputs():
+        o = {k: torch.empty(n, dtype=dt, device=dev) for k, dt in (
+            ("kl", torch.float32), ("nll_ref", torch.float32), ("nll_cand", torch.float32),
+            ("lse_ref", torch.float32), ("lse_cand", torch.float32), ("argmax_ref", torch.int32),
+            ("argmax_cand", torch.int32))}
+        o.update({"ids_ref": torch.empty((n, 64), dtype=torch.int32, device=dev),
+                  "ids_cand": torch.empty((n, 64), dtype=torch.int32, device=dev),
+                  "lp_ref": torch.empty((n, 64), dtype=torch.float16, device=dev),
+                  "lp_cand": torch.empty((n, 64), dtype=torch.float16, device=dev)})
+        return o
+    outs = [outputs() for _ in range(2)]
+    views = [[{k: x[c * chunk:(c + 1) * chunk] for k, x in o.items()} for c in range(nchunk)]
+             for o in outs]
 
     def step(i, ev):
+        k = i % 2
         for c in range(nchunk):
             sl = slice(c * chunk, (c + 1) * chunk)
-            kld.kld_fused_head(W, hr[sl], hc[sl], tg[sl], topk=True, ws=ws, out=views[c],
+            kld.kld_fused_head(W, hr[sl], hc[sl], tg[sl], topk=True, ws=ws[k], out=views[k][c],
                                events=ev[c] if ev else None)
-        kld.kld_summary(out["kl"], out["argmax_ref"], out["argmax_cand"], out["nll_ref"],
-                        out["nll_cand"], quantiles=QUANTILES, ws=ws_s, out=summ)
+        o = outs[k]
+        kld.kld_summary(o["kl"], o["argmax_ref"], o["argmax_cand"], o["nll_ref"],
+                        o["nll_cand"], quantiles=QUANTILES, ws=ws_s[k], out=summs[k])
 
     elapsed, kernel_ms = _timeit(step, steps, warmup, n_ev=nchunk)
+    summ, out = summs[0], outs[0]
     flops = 4.0 * chunk * d * v
     summary = kld.summary_dict(summ, QUANTILES)
     res = {
@@ -521,20 +563,24 @@ def logits_f32(steps, warmup, cpu_sample):
     # two copies rotate so that one step's rows are not still in the 256 MB cache
     sets = [(torch.from_numpy(a_np).to(dev), torch.from_numpy(b_np).to(dev)) for _ in range(2)]
     tg = torch.from_numpy(t_np).to(dev)
-    ws = torch.empty(kld.kld_workspace_size(0, n, v), dtype=torch.uint8, device=dev)
-    ws_s = torch.empty(kld.kld_workspace_size(3, n, 0), dtype=torch.uint8, device=dev)
-    summ = torch.empty(8 + len(QUANTILES), dtype=torch.float64, device=dev)
-    box = {}
+    ws = [torch.empty(kld.kld_workspace_size(0, n, v), dtype=torch.uint8, device=dev)
+          for _ in range(2)]
+    ws_s = [torch.empty(kld.kld_workspace_size(3, n, 0), dtype=torch.uint8, device=dev)
+            for _ in range(2)]
+    summs = [torch.empty(8 + len(QUANTILES), dtype=torch.float64, device=dev) for _ in range(2)]
+    outs = [None, None]
 
     def step(i, ev):
-        ra, rb = sets[i % 2]
-        box["out"] = kld.kld_from_logits(ra, rb, tg, ws=ws, out=box.get("out"),
-                                         events=ev[0] if ev else None)
-        o = box["out"]
+        k = i % 2
+        ra, rb = sets[k]
+        outs[k] = kld.kld_from_logits(ra, rb, tg, ws=ws[k], out=outs[k],
+                                      events=ev[0] if ev else None)
+        o = outs[k]
         kld.kld_summary(o["kl"], o["argmax_ref"], o["argmax_cand"], o["nll_ref"], o["nll_cand"],
-                        quantiles=QUANTILES, ws=ws_s, out=summ)
+                        quantiles=QUANTILES, ws=ws_s[k], out=summs[k])
 
     elapsed, kernel_ms = _timeit(step, steps, warmup)
+    box = {"out": outs[0]}
     nbytes = 8.0 * n * v
     res = {
         "value": n * steps / elapsed, "unit": "positions/s", "ms_per_step": elapsed * 1e3 / steps,
@@ -586,29 +632,38 @@ def bf16_topk_stream(steps, warmup, cpu_sample):
         a, b = synth.logit_rows(wl, range(r0, r0 + nb), v, dtype="bf16")
         batches.append((r0, nb, _bf(a, dev), _bf(b, dev)))
         del a, b
-    ws = torch.empty(kld.kld_workspace_size(0, bsz, v, 0, 1), dtype=torch.uint8, device=dev)
-    ws_s = torch.empty(kld.kld_workspace_size(3, total, 0), dtype=torch.uint8, device=dev)
-    summ = torch.empty(8 + len(QUANTILES), dtype=torch.float64, device=dev)
-    out = {k: torch.empty(total, dtype=dt, device=dev) for k, dt in (
-        ("kl", torch.float32), ("lse_ref", torch.float32), ("lse_cand", torch.float32),
-        ("argmax_ref", torch.int32), ("argmax_cand", torch.int32))}
-    out.update({"ids_ref": torch.empty((total, 64), dtype=torch.int32, device=dev),
-                "ids_cand": torch.empty((total, 64), dtype=torch.int32, device=dev),
-                "lp_ref": torch.empty((total, 64), dtype=torch.float16, device=dev),
-                "lp_cand": torch.empty((total, 64), dtype=torch.float16, device=dev)})
-    tail = torch.empty(total, dtype=torch.float32, device=dev)
-    views = [{k: x[r0:r0 + nb] for k, x in out.items()} for r0, nb, _, _ in batches]
+    ws = [torch.empty(kld.kld_workspace_size(0, bsz, v, 0, 1), dtype=torch.uint8, device=dev)
+          for _ in range(2)]
+    ws_s = [torch.empty(kld.kld_workspace_size(3, total, 0), dtype=torch.uint8, device=dev)
+            for _ in range(2)]
+    summs = [torch.empty(8 + len(QUANTILES), dtype=torch.float64, device=dev) for _ in range(2)]
+
+    def outputs():
+        o = {k: torch.empty(total, dtype=dt, device=dev) for k, dt in (
+            ("kl", torch.float32), ("lse_ref", torch.float32), ("lse_cand", torch.float32),
+            ("argmax_ref", torch.int32), ("argmax_cand", torch.int32))}
+        o.update({"ids_ref": torch.empty((total, 64), dtype=torch.int32, device=dev),
+                  "ids_cand": torch.empty((total, 64), dtype=torch.int32, device=dev),
+                  "lp_ref": torch.empty((total, 64), dtype=torch.float16, device=dev),
+                  "lp_cand": torch.empty((total, 64), dtype=torch.float16, device=dev)})
+        return o
+    outs = [outputs() for _ in range(2)]
+    tails = [torch.empty(total, dtype=torch.float32, device=dev) for _ in range(2)]
+    views = [[{k: x[r0:r0 + nb] for k, x in o.items()} for r0, nb, _, _ in batches] for o in outs]
 
     def step(i, ev):
+        k = i % 2
         for j, (r0, nb, ra, rb) in enumerate(batches):
-            o = kld.kld_from_logits(ra, rb, None, topk=True, ws=ws, out=views[j],
+            o = kld.kld_from_logits(ra, rb, None, topk=True, ws=ws[k], out=views[k][j],
                                     events=ev[j] if ev else None)
             kld.kld_topk_tail(o["ids_ref"], o["lp_ref"], o["ids_cand"], o["lp_cand"], v,
-                              out=tail[r0:r0 + nb])
-        kld.kld_summary(out["kl"], out["argmax_ref"], out["argmax_cand"], quantiles=QUANTILES,
-                        ws=ws_s, out=summ)   # no targets in this workload: no NLL
+                              out=tails[k][r0:r0 + nb])
+        o = outs[k]
+        kld.kld_summary(o["kl"], o["argmax_ref"], o["argmax_cand"], quantiles=QUANTILES,
+                        ws=ws_s[k], out=summs[k])   # no targets in this workload: no NLL
 
     elapsed, kernel_ms = _timeit(step, steps, warmup, n_ev=len(batches))
+    summ, out, tail = summs[0], outs[0], tails[0]
     nbytes = 4.0 * bsz * v
     mean_ms = kernel_ms
     achieved_bytes = 4.0 * total * v / len(batches)   # average launch
@@ -680,18 +735,21 @@ def golden_f32(steps, warmup, cpu_sample):
     ra, rb = torch.from_numpy(a_np).to(dev), torch.from_numpy(b_np).to(dev)
     tg = torch.from_numpy(t_np).to(dev)
     rec = kld.kld_golden_export(ra, tg)
-    ws = torch.empty(kld.kld_workspace_size(4, n, v), dtype=torch.uint8, device=dev)
-    ws_s = torch.empty(kld.kld_workspace_size(3, n, 0), dtype=torch.uint8, device=dev)
-    summ = torch.empty(8 + len(QUANTILES), dtype=torch.float64, device=dev)
-    kl = torch.empty(n, dtype=torch.float32, device=dev)
+    ws = [torch.empty(kld.kld_workspace_size(4, n, v), dtype=torch.uint8, device=dev)
+          for _ in range(2)]
+    ws_s = [torch.empty(kld.kld_workspace_size(3, n, 0), dtype=torch.uint8, device=dev)
+            for _ in range(2)]
+    summs = [torch.empty(8 + len(QUANTILES), dtype=torch.float64, device=dev) for _ in range(2)]
+    kls = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(2)]
 
     def step(i, ev):
+        k = i % 2
         if ev:
             ev[0][0].record()
-        kld.kld_coarse_kl(rb, rec["ids"], rec["lp"], rec["rec"], out=kl, ws=ws)
+        kld.kld_coarse_kl(rb, rec["ids"], rec["lp"], rec["rec"], out=kls[k], ws=ws[k])
         if ev:
             ev[0][1].record()
-        kld.kld_summary(kl, quantiles=QUANTILES, ws=ws_s, out=summ)
+        kld.kld_summary(kls[k], quantiles=QUANTILES, ws=ws_s[k], out=summs[k])
 
     for _ in range(warmup):
         step(0, None)
@@ -704,7 +762,7 @@ def golden_f32(steps, warmup, cpu_sample):
     export_ms = e0.elapsed_time(e1)
     elapsed, kernel_ms = _timeit(step, steps, 0)
     nbytes = 4.0 * n * v
-    summary = kld.summary_dict(summ, QUANTILES)
+    summary = kld.summary_dict(summs[0], QUANTILES)
     res = {
         "value": n * steps / elapsed, "unit": "positions/s", "ms_per_step": elapsed * 1e3 / steps,
         "dtype": "f32",
@@ -766,12 +824,15 @@ def windows_paired(steps, warmup, cpu_sample):
                 "seg_count": torch.empty(nctx, dtype=torch.int64, device=dev),
                 "seg_exceed": torch.empty((nctx, len(thr)), dtype=torch.int64, device=dev),
                 "totals": torch.empty(2 + len(thr), dtype=torch.float64, device=dev)}
-    wa, wb = wout(), wout()
-    ws_p = torch.empty(kld.kld_workspace_size(5, nclust, nrep), dtype=torch.uint8, device=dev)
+    was, wbs = [wout() for _ in range(2)], [wout() for _ in range(2)]
+    ws_p = [torch.empty(kld.kld_workspace_size(5, nclust, nrep), dtype=torch.uint8, device=dev)
+            for _ in range(2)]
     ev_p = [(TimingEvent(), TimingEvent()) for _ in range(steps)]
     box = {"k": 0}
 
     def step(i, ev):
+        k = i % 2
+        wa, wb = was[k], wbs[k]
         if ev:
             ev[0][0].record()
         kld.kld_window_summary(a, off, 0, thr, out=wa)
@@ -780,7 +841,7 @@ def windows_paired(steps, warmup, cpu_sample):
             ev[0][1].record()
             ev_p[i][0].record()
         box["p"] = kld.kld_paired_bootstrap(wa["seg_sum"], wb["seg_sum"], wa["seg_count"], lab,
-                                            dr, qs, ws=ws_p)
+                                            dr, qs, ws=ws_p[k])
         if ev:
             ev_p[i][1].record()
 
@@ -842,16 +903,21 @@ def coarse_fused_window(steps, warmup, cpu_sample):
     dev = torch.device("cuda:0")
     W, hc = _bf(w_np, dev), _bf(hc_np, dev)
     ids, lp, rec = (torch.from_numpy(x).to(dev) for x in (ids_np, lp_np, rec_np))
-    ws = torch.empty(kld.kld_workspace_size(6, n, v, d), dtype=torch.uint8, device=dev)
-    ws_s = torch.empty(kld.kld_workspace_size(3, n, 0), dtype=torch.uint8, device=dev)
-    summ = torch.empty(8 + len(QUANTILES), dtype=torch.float64, device=dev)
-    kl = torch.empty(n, dtype=torch.float32, device=dev)
+    ws = [torch.empty(kld.kld_workspace_size(6, n, v, d), dtype=torch.uint8, device=dev)
+          for _ in range(2)]
+    ws_s = [torch.empty(kld.kld_workspace_size(3, n, 0), dtype=torch.uint8, device=dev)
+            for _ in range(2)]
+    summs = [torch.empty(8 + len(QUANTILES), dtype=torch.float64, device=dev) for _ in range(2)]
+    kls = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(2)]
 
     def step(i, ev):
-        kld.kld_coarse_fused(W, hc, ids, lp, rec, out=kl, ws=ws, events=ev[0] if ev else None)
-        kld.kld_summary(kl, quantiles=QUANTILES, ws=ws_s, out=summ)
+        k = i % 2
+        kld.kld_coarse_fused(W, hc, ids, lp, rec, out=kls[k], ws=ws[k],
+                             events=ev[0] if ev else None)
+        kld.kld_summary(kls[k], quantiles=QUANTILES, ws=ws_s[k], out=summs[k])
 
     elapsed, kernel_ms = _timeit(step, steps, warmup)
+    summ = summs[0]
     flops = 2.0 * n * d * v
     summary = kld.summary_dict(summ, QUANTILES)
     res = {
