@@ -13,7 +13,9 @@
 //
 //   paired_cluster_kernel   one block per cluster: its summed difference and
 //                           scored positions; one extra block: the overall
-//                           difference, wins, ties and a label check
+//                           difference, wins, ties and a check of the labels
+//                           and counts, whose failure turns every replicate
+//                           and percentile into NaN (a flag in the workspace)
 //   paired_replicate_kernel one wave per replicate: gather-sum over its draws
 //   paired_runsort_kernel   one block per run of 1,024 replicates: bitonic
 //                           sort of the run in LDS
@@ -52,7 +54,7 @@ __device__ __forceinline__ T block_sum(T x, T *red) {
 __global__ __launch_bounds__(PT) void paired_cluster_kernel(
     const double *__restrict__ sum_a, const double *__restrict__ sum_b,
     const int64_t *__restrict__ count, int64_t nctx, const int32_t *__restrict__ cluster,
-    int64_t nclust, longlong2 *__restrict__ clus,
+    int64_t nclust, longlong2 *__restrict__ clus, long long *__restrict__ flag,
     double *__restrict__ out) {
   __shared__ double rd[PT / 64];
   __shared__ long long ri[PT / 64];
@@ -126,6 +128,7 @@ __global__ __launch_bounds__(PT) void paired_cluster_kernel(
   ti = block_sum(ti, ri);
   bad = block_sum(bad, ri);
   if (threadIdx.x == 0) {
+    flag[0] = bad;   // read by the replicate and quantile kernels (later in stream order)
     out[0] = (bad || c == 0) ? __builtin_nan("") : d / (double)c;
     out[1] = (double)wa;
     out[2] = (double)wb;
@@ -136,7 +139,7 @@ __global__ __launch_bounds__(PT) void paired_cluster_kernel(
 constexpr int RW = 4;   // waves (replicates) per block
 
 __global__ __launch_bounds__(RW * 64) void paired_replicate_kernel(
-    const longlong2 *__restrict__ clus, int64_t nclust,
+    const longlong2 *__restrict__ clus, const long long *__restrict__ flag, int64_t nclust,
     const int32_t *__restrict__ draws, int64_t nrep, double *__restrict__ reps) {
   const int lane = threadIdx.x & 63;
   // the wave index made visibly uniform, so that the buffer resource lives
@@ -176,7 +179,9 @@ __global__ __launch_bounds__(RW * 64) void paired_replicate_kernel(
     den += __shfl_xor(den, m);
     bad |= __shfl_xor(bad, m);
   }
-  if (lane == 0) reps[r] = (bad || den == 0) ? __builtin_nan("") : num / (double)den;
+  // a context label outside [0, nclust) or a negative count invalidates every
+  // cluster sum: all replicates are NaN then
+  if (lane == 0) reps[r] = (bad || den == 0 || flag[0]) ? __builtin_nan("") : num / (double)den;
 }
 
 // Sorting the replicates: runs of RUN values are sorted one block each,
@@ -273,10 +278,11 @@ constexpr int QT = 1024;
 
 __global__ __launch_bounds__(QT) void paired_quantile_kernel(const double *__restrict__ reps,
                                                              const double *__restrict__ sorted,
+                                                             const long long *__restrict__ flag,
                                                              int64_t nrep, PairedQuantiles qs,
                                                              double *__restrict__ out) {
   __shared__ int any_nan;
-  if (threadIdx.x == 0) any_nan = 0;
+  if (threadIdx.x == 0) any_nan = flag[0] != 0;
   __syncthreads();
   int nan_here = 0;
   for (int64_t i = threadIdx.x; i < nrep; i += QT) nan_here |= reps[i] != reps[i];
@@ -296,10 +302,15 @@ __global__ __launch_bounds__(QT) void paired_quantile_kernel(const double *__res
 
 }  // namespace
 
+// Workspace: the input-check flag (16 bytes, keeping what follows 16-byte
+// aligned), per cluster its difference and count (16 bytes), the sorted runs
+// and the sorted replicates.
+constexpr size_t kFlagBytes = 16;
+
 size_t paired_workspace_bytes(int64_t nclust, int64_t nrep) {
   const int64_t c = nclust > 0 ? nclust : 0;
   const int64_t runs = nrep > 0 ? (nrep + RUN - 1) / RUN : 0;
-  return (size_t)c * (sizeof(double) + sizeof(int64_t)) +
+  return kFlagBytes + (size_t)c * (sizeof(double) + sizeof(int64_t)) +
          (size_t)(runs * RUN + (nrep > 0 ? nrep : 0)) * sizeof(double);
 }
 
@@ -307,17 +318,19 @@ hipError_t launch_paired_bootstrap(const double *sum_a, const double *sum_b, con
                                    int64_t nctx, const int32_t *cluster, int64_t nclust,
                                    const int32_t *draws, int64_t nrep, const PairedQuantiles &qs,
                                    double *reps, double *out, void *ws, hipStream_t stream) {
-  longlong2 *clus = static_cast<longlong2 *>(ws);   // per cluster: difference (f64 bits), count
+  long long *flag = static_cast<long long *>(ws);
+  longlong2 *clus = reinterpret_cast<longlong2 *>(static_cast<char *>(ws) + kFlagBytes);
+  // per cluster: difference (f64 bits), count
   double *runs = reinterpret_cast<double *>(clus + nclust);
   const int nruns = (int)((nrep + RUN - 1) / RUN);
   double *sorted = runs + (int64_t)nruns * RUN;
   hipLaunchKernelGGL(paired_cluster_kernel, dim3((unsigned)(nclust + 1)), dim3(PT), 0, stream,
-                     sum_a, sum_b, count, nctx, cluster, nclust, clus, out);
+                     sum_a, sum_b, count, nctx, cluster, nclust, clus, flag, out);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (nrep > 0) {
     hipLaunchKernelGGL(paired_replicate_kernel, dim3((unsigned)((nrep + RW - 1) / RW)),
-                       dim3(RW * 64), 0, stream, clus, nclust, draws, nrep, reps);
+                       dim3(RW * 64), 0, stream, clus, flag, nclust, draws, nrep, reps);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(paired_runsort_kernel, dim3((unsigned)nruns), dim3(RUN), 0, stream, reps,
                        nrep, runs);
@@ -326,8 +339,8 @@ hipError_t launch_paired_bootstrap(const double *sum_a, const double *sum_b, con
                        stream, runs, nrep, nruns, sorted);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(paired_quantile_kernel, dim3(1), dim3(QT), 0, stream, reps, sorted, nrep, qs,
-                     out);
+  hipLaunchKernelGGL(paired_quantile_kernel, dim3(1), dim3(QT), 0, stream, reps, sorted, flag, nrep,
+                     qs, out);
   return hipGetLastError();
 }
 

@@ -379,10 +379,12 @@ kld_status kld_window_summary(const float *kl, int64_t n, const int64_t *offsets
  *                (contexts with count 0 are in none), [4 + i] the type-7
  *                percentile of the replicates at quantiles[i].
  * ws           : kld_workspace_size(KLD_OP_PAIRED, nclust, nrep, 0, 0) bytes
- *                (per-cluster sums and two copies of the replicates).
- * A cluster label outside [0, nclust) or a negative count makes out[0] NaN;
- * a draw outside it makes that replicate NaN; any NaN replicate (or none)
- * makes every percentile NaN.  Sums run in a fixed order: results are
+ *                (an input-check flag, per-cluster sums and two copies of the
+ *                replicates).
+ * A cluster label outside [0, nclust) or a negative count makes out[0],
+ * every replicate and every percentile NaN (the cluster sums are not valid);
+ * a draw outside [0, nclust) makes that replicate NaN; any NaN replicate (or
+ * none) makes every percentile NaN.  Sums run in a fixed order: results are
  * bitwise reproducible.
  */
 kld_status kld_paired_bootstrap(const double *sum_a, const double *sum_b, const int64_t *count,

@@ -110,8 +110,17 @@ def test_edges():
 def test_bad_labels_and_draws_give_nan():
     s = np.arange(6, dtype=np.float64)
     cnt = np.full(6, 2)
-    out, reps = _gpu(s, s + 1, cnt, [0, 1, 2, 0, 1, 5], np.array([[0, 1, 2]], np.int32))
-    assert np.isnan(out[0])
+    # a label outside [0, nclust): the cluster sums are invalid, so the
+    # difference, every replicate and every percentile are NaN
+    out, reps = _gpu(s, s + 1, cnt, [0, 1, 2, 0, 1, 5], np.array([[0, 1, 2], [2, 2, 2]], np.int32))
+    assert np.isnan(out[0]) and np.all(np.isnan(reps)) and np.all(np.isnan(out[4:]))
+    # a negative count: the same
+    out, reps = _gpu(s, s + 1, [2, 2, -1, 2, 2, 2], [0, 1, 2, 0, 1, 2],
+                     np.array([[0, 1, 2], [1, 1, 0]], np.int32))
+    assert np.isnan(out[0]) and np.all(np.isnan(reps)) and np.all(np.isnan(out[4:]))
+    # valid inputs after invalid ones: finite again (every call rewrites the check)
+    out, reps = _gpu(s, s + 1, cnt, [0, 1, 2, 0, 1, 2], np.array([[0, 1, 2]], np.int32))
+    assert out[0] == -0.5 and reps[0] == -0.5 and np.all(np.isfinite(out[4:]))
     out, reps = _gpu(s, s + 1, cnt, [0, 1, 2, 0, 1, 2], np.array([[0, 1, 3], [0, 1, 2]], np.int32))
     assert np.isnan(reps[0]) and reps[1] == -0.5 and np.all(np.isnan(out[4:]))
 
