@@ -3,8 +3,8 @@
 // Each block owns one (row, vocabulary split) pair and streams both rows'
 // slices once, coalesced, 16 bytes per lane per load.  Every lane folds its
 // elements into an online RowState (kld_device.hpp), batch by batch: one
-// max per batch, one rebase when the max moves, then one exp2 per element
-// per side.  Lanes merge by butterfly, waves through LDS, and the block
+// max per batch, one rebase when the max moves, then one fma and one exp2
+// per element per side.  Lanes merge by butterfly, waves through LDS, and the block
 // writes one partial state; finalize_rows_kernel merges the splits (in f64) in a
 // fixed order and writes the per-position outputs.  HBM-bound: 2 v sizeof(T)
 // bytes per position are read once.
@@ -260,7 +260,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
   TopkShared<kSCap> &sh = sh_storage[0];
   __shared__ RowState waves[kWaves];
   __shared__ int done;   // waves that have finished (the last one merges)
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  // the wave index in a scalar register: the per-wave LDS bases become
+  // scalars and leave the vector registers to the streaming loop
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   // per side, uniform over the wave: value threshold, key threshold (0 = none)
   // and candidates in the wave's buffer
   float thr[2] = {kNegInf, kNegInf};
@@ -273,6 +276,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
     __syncthreads();
   }
 
+  // Inside the loop every element costs one fma before its exp2: its
+  // exponent is e = x L2E - o against the offset o = ref(m) L2E (f32), and
+  // t sums w (e_a - e_b), the log2-scaled difference against both offsets
+  // (exact arithmetic would give L2E ((a - ref_a) - (b - ref_b)) + (r_a - r_b),
+  // r = ref(m) L2E - o).  fold_offsets converts the sums back after the loop.
   float ma = kNegInf, sa = 0.f, t = 0.f, mb = kNegInf, sb = 0.f;
   int ia = kNoId, ib = kNoId;
 
@@ -392,14 +400,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
     };
     if (bma > ma) {   // new maximum: locate its lowest id in this batch, rebase the sums
       const int id = first_id(ca, bma);
-      const float f = rescale(ma, bma);
-      if (TWO && sa != 0.f) t = fmaf(-sa, bma - ref_of(ma), t);
+      const float o = bma * kL2E, oa = ref_of(ma) * kL2E;
+      const float f = ma == kNegInf ? 0.f : exp2_fast(oa - o);
+      if (TWO && sa != 0.f) t = fmaf(-sa, o - oa, t);
       t *= f; sa *= f; ma = bma; ia = id;
     }
     if (TWO && bmb > mb) {
       const int id = first_id(cb, bmb);
-      if (sa != 0.f) t = fmaf(sa, bmb - ref_of(mb), t);
-      sb *= rescale(mb, bmb); mb = bmb; ib = id;
+      const float o = bmb * kL2E, ob = ref_of(mb) * kL2E;
+      if (sa != 0.f) t = fmaf(sa, o - ob, t);
+      sb *= mb == kNegInf ? 0.f : exp2_fast(ob - o);
+      mb = bmb; ib = id;
     }
     if constexpr (TOPK) {
       {   // rounds 0, 1, 2, 3, 5, 7, 11, 15, 23, 31, ...: r + 1 = 2^k or 3 * 2^k
@@ -435,7 +446,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
         }
       }
     }
-    const float rfa = ref_of(ma), rfb = ref_of(mb);
+    const float oa = ref_of(ma) * kL2E, ob = ref_of(mb) * kL2E;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float xa[VEC], xb[VEC];
@@ -446,15 +457,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
       }
 #pragma unroll
       for (int j = 0; j < VEC; ++j) {
-        const float x = xa[j] - rfa;
-        const float w = exp2_fast(x * kL2E);
+        const float ea = fmaf(xa[j], kL2E, -oa);
+        const float w = exp2_fast(ea);
         sa += w;
         if (TWO) {
-          const float y = xb[j] - rfb;
-          // x - y is clamped below so that a -inf reference id (w = 0) adds
-          // exactly 0 even when the candidate id is -inf too.
-          t = fmaf(w, fmaxf(x - y, -kFltMax), t);
-          sb += exp2_fast(y * kL2E);
+          const float eb = fmaf(xb[j], kL2E, -ob);
+          // e_a - e_b is clamped below so that a -inf reference id (w = 0)
+          // adds exactly 0 even when the candidate id is -inf too.
+          t = fmaf(w, fmaxf(ea - eb, -kFltMax), t);
+          sb += exp2_fast(eb);
         }
       }
     }
@@ -548,6 +559,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
       }
       if (lane == 0) sh.lcount[side][wave] = n2;
     }
+  }
+  {   // fold_offsets: back to sums against ref(ma), ref(mb) and t in nats.
+      // The exact product ref(m) L2E is o + r (r = fma(ref, L2E, -o), exact
+      // and below half an ulp of o): every weight taken against o is 2^r too
+      // large, and e_a - e_b carries r_a - r_b besides L2E times the
+      // difference of the shifted logits.
+    const float oa = ref_of(ma) * kL2E, ob = ref_of(mb) * kL2E;
+    const float ra = fmaf(ref_of(ma), kL2E, -oa), rb = fmaf(ref_of(mb), kL2E, -ob);
+    const float ga = exp2_fast(-ra);
+    sa *= ga;
+    sb *= exp2_fast(-rb);
+    if (TWO && sa != 0.f) t = fmaf(t, ga, -(ra - rb) * sa) / kL2E;
   }
   RowState s;
   s.ma = ma; s.sa = sa; s.t = t; s.mb = mb; s.sb = sb; s.ia = ia; s.ib = ib;
