@@ -219,10 +219,10 @@ def _timeit(step, steps, warmup, n_ev=1):
     import torch
     evs = [[(TimingEvent(), TimingEvent()) for _ in range(n_ev)] for _ in range(steps)]
     ss = _streams()
-    for i in range(warmup):
+    for i in range(warmup):   # one at a time: warmup steps never overlap
         with torch.cuda.stream(ss[i % 2]):
             step(i, None)
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         if i > 0 and _hip().hipStreamWaitEvent(ss[i % 2].cuda_stream, evs[i - 1][-1][1].cuda_event,

@@ -108,6 +108,28 @@ def test_logits_edge_values():
     assert got["argmax_ref"][8] == 10
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+def test_logits_shifted_rows(bf16):
+    """Rows shifted by large opposite constants (|c| up to 300, a different
+    one per row and side): KL is invariant under such shifts, and the kernel's
+    exponents against rounded offsets must keep the per-position bar and the
+    mean bar there (a form that sums w (a - b) without offsets misses the
+    per-position bar by 50x on these rows)."""
+    need_gpu()
+    g = np.random.default_rng(5)
+    n, v = 48, 20_000
+    a = (3 * g.standard_normal((n, v))).astype(np.float32)
+    b = (a + 0.03 * g.standard_normal((n, v))).astype(np.float32)
+    ca = g.uniform(-300, 300, (n, 1)).astype(np.float32)
+    cb = g.uniform(-300, 300, (n, 1)).astype(np.float32)
+    a, b = (a + ca).astype(np.float32), (b + cb).astype(np.float32)
+    if bf16:
+        a, b = synth.f32_to_bf16_bits(a), synth.f32_to_bf16_bits(b)
+    got = _run(a, b, None, bf16)
+    want = _oracle(a, b, None, bf16)
+    _compare(got, want, f"shifted bf16={bf16}", strict_mean=True)
+
+
 def test_logits_target_out_of_range_gives_nan_nll():
     need_gpu()
     a, b = synth.logit_rows(synth.LOGITS_F32, range(3), 500)
