@@ -21,8 +21,10 @@
 // per-wave LDS buffer (ballot + mbcnt offsets, no atomics, no block barrier);
 // a wave whose buffer fills sorts it in registers, keeps its 64 best keys and
 // from then on also requires keys above the 64th.  At the end each wave drops
-// the entries below the final threshold, the wave that finishes last gathers
-// the four waves' survivors and cuts them to the 64 best; topk_merge_kernel
+// the entries below the final threshold; after a block barrier one wave per
+// side gathers the four waves' survivors and cuts them to the 64 best (the
+// two sides in parallel, beside a third wave that merges the row states);
+// topk_merge_kernel
 // (kld_topk.hip) merges the splits of a row and converts them to ids and fp16
 // log-probs.  On these inputs only a few hundred elements per row and side
 // pass the threshold, so the export costs little beyond the streaming pass.
@@ -259,7 +261,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
   __shared__ TopkShared<kSCap> sh_storage[1];
   TopkShared<kSCap> &sh = sh_storage[0];
   __shared__ RowState waves[kWaves];
-  __shared__ int done;   // waves that have finished (the last one merges)
   const int lane = threadIdx.x & 63;
   // the wave index in a scalar register: the per-wave LDS bases become
   // scalars and leave the vector registers to the streaming loop
@@ -272,7 +273,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
   int scnt[2] = {0, 0};   // vectors staged by the wave
   if constexpr (TOPK) {
     if (threadIdx.x < 2 * kWaves) (&sh.bound[0][0])[threadIdx.x] = kNegInf;
-    if (threadIdx.x == 0) done = 0;
     __syncthreads();
   }
 
@@ -577,45 +577,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
   s = wave_merge(s);
   if (lane == 0) waves[wave] = s;
 
-  // One wave merges the four waves' results, in wave order.  With top-k it
-  // is the wave that finishes last (the others leave without waiting);
-  // without, wave 0 after a barrier.
-  if constexpr (TOPK) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    int last = 0;
-    if (lane == 0) last = atomicAdd(&done, 1) == kWaves - 1;
-    if (__shfl(last, 0) == 0) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  } else {
-    __syncthreads();
-    if (wave != 0) return;
-  }
-  if (lane == 0) {
-    const volatile RowState *vw = waves;
-    RowState r;
-    r.ma = vw[0].ma; r.sa = vw[0].sa; r.t = vw[0].t; r.mb = vw[0].mb; r.sb = vw[0].sb;
-    r.ia = vw[0].ia; r.ib = vw[0].ib;
+  // After a block barrier the closing work is spread over the waves: with
+  // top-k, wave s < NS gathers side s's four lists and selects their 64 best
+  // while the next wave merges the four waves' row states (in wave order);
+  // without, wave 0 merges.  (A wave that left early would free nothing: the
+  // block's LDS stays allocated until its last wave ends.)
+  __syncthreads();
+  if (wave == (TOPK ? NS : 0)) {
+    if (lane == 0) {
+      RowState r = waves[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) {
-      RowState o;
-      o.ma = vw[w].ma; o.sa = vw[w].sa; o.t = vw[w].t; o.mb = vw[w].mb; o.sb = vw[w].sb;
-      o.ia = vw[w].ia; o.ib = vw[w].ib;
-      r = merge(r, o);
+      for (int w = 1; w < kWaves; ++w) r = merge(r, waves[w]);
+      part[row * splits + split] = r;
     }
-    part[row * splits + split] = r;
   }
   if constexpr (TOPK) {
-    // the four waves' lists (at most 256 entries) gathered into this wave's
-    // own candidate buffer, then cut to the range's 64 best
-#pragma unroll
-    for (int side = 0; side < NS; ++side) {
-      uint64_t *scr = sh.buf[side][wave];
+    if (wave < NS) {
+      const int side = wave;
+      uint64_t *scr = sh.buf[side][wave];   // this wave's own buffer, free now
       int nt = 0;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const int c = reinterpret_cast<const volatile int *>(sh.lcount[side])[w];
-        const volatile uint64_t *lst = reinterpret_cast<const volatile uint64_t *>(sh.stage[side][w]);
-        if (lane < c) scr[nt + lane] = lst[lane];
+        const int c = sh.lcount[side][w];
+        if (lane < c) scr[nt + lane] = reinterpret_cast<const uint64_t *>(sh.stage[side][w])[lane];
         nt += c;
       }
       const uint64_t k = wave_best64(lds<const uint64_t>(scr), nt);
