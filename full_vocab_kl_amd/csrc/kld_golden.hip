@@ -376,12 +376,28 @@ __device__ __forceinline__ void load_vecn(const T *__restrict__ row, int64_t pos
   }
 }
 
+// In-block state of coarse_partial_kernel, f32: maximum m, s = sum 2^((z -
+// m) log2e) over the range, w = the same over its unlisted ids.  Ranges are
+// at most 131,072 ids, so f32 sums keep ~1e-7 relative accuracy; the
+// finalize merges a row's ranges in f64.
+struct CoarseState {
+  float m, s, w;
+};
+
+__device__ __forceinline__ CoarseState coarse_merge(const CoarseState &a, const CoarseState &b) {
+  if (b.m == kNegInf) return a;
+  if (a.m == kNegInf) return b;
+  const float m = fmaxf(a.m, b.m);
+  const float fa = exp2_fast((a.m - m) * kL2E), fb = exp2_fast((b.m - m) * kL2E);
+  return CoarseState{m, fmaf(a.s, fa, b.s * fb), fmaf(a.w, fa, b.w * fb)};
+}
+
 template <typename T, int VEC, int U, bool ALIGNED>
 __global__ __launch_bounds__(GT) void coarse_partial_kernel(
     const T *__restrict__ cand, int64_t ld, int64_t v, int64_t chunk, int splits,
     const int32_t *__restrict__ ids, LseState *__restrict__ part) {
   __shared__ uint32_t listed[CMAXW];   // the record's ids in [lo, hi), bit (id - lo)
-  __shared__ LseState xw[GT / 64];
+  __shared__ CoarseState xw[GT / 64];
   const int64_t row = blockIdx.x / splits;
   const int split = (int)(blockIdx.x % splits);
   const int64_t lo = (int64_t)split * chunk;
@@ -400,54 +416,25 @@ __global__ __launch_bounds__(GT) void coarse_partial_kernel(
   __syncthreads();
 
   constexpr int64_t kStride = (int64_t)GT * VEC;
-  LseState st{kNegInf, 0.0, 0.0, 0.0};
+  CoarseState st{kNegInf, 0.f, 0.f};
   const int64_t rounds = (hi - lo + kStride * U - 1) / (kStride * U);
-  // Aligned rows: the whole vectors of [lo, hi) are read through a buffer
-  // resource (vectors past it read 0 and touch no memory), so a round's loads
-  // carry no branch and are all in flight together; elements past hi become
-  // -inf and a vector straddling hi is completed element by element.
-  const int len = (int)(hi - lo);   // a range spans at most 131,072 ids
-  const int nvec = len / VEC * VEC;
-  __amdgpu_buffer_rsrc_t rs;
-  if constexpr (ALIGNED)
-    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(r + lo), (short)0,
-                                           nvec * (int)sizeof(T), 0x00020000);
-  for (int64_t rd = 0; rd < rounds; ++rd) {
-    const int64_t base = lo + rd * kStride * U + (int64_t)threadIdx.x * VEC;
-    float x[U][VEC];
-    if constexpr (ALIGNED) {
-      typedef typename std::conditional<sizeof(T) == 4, f32x4, u32x4>::type Raw;
-      Raw q[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        q[u] = __builtin_bit_cast(Raw, __builtin_amdgcn_raw_buffer_load_b128(
-                   rs, (int)(base + u * kStride - lo) * (int)sizeof(T), 0, 2 /* streaming */));
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          if constexpr (sizeof(T) == 4) x[u][e] = q[u][e];
-          else x[u][e] = __uint_as_float((e & 1) ? (q[u][e >> 1] & 0xffff0000u) : (q[u][e >> 1] << 16));
-        }
-        const int64_t p = base + u * kStride;
-        if (p + VEC > hi) {   // the last vectors of the range only
-#pragma unroll
-          for (int e = 0; e < VEC; ++e)
-            x[u][e] = p + e < hi ? (p - lo >= nvec ? ld_f32(r, p + e) : x[u][e]) : kNegInf;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < U; ++u) load_vecn<T, VEC, false>(r, base + u * kStride, hi, x[u]);
-    }
+  // Fold one round's elements x (first at base) into the thread's state: the
+  // sum, and separately the sum over the ids the record does not list.
+  auto fold = [&](const float (&x)[U][VEC], int64_t base) __attribute__((always_inline)) {
     float bm = kNegInf;
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int e = 0; e < VEC; ++e) bm = fmaxf(bm, x[u][e]);
-    raise_max(st, bm);
-    float ps = 0.f, pw = 0.f;
+    // Inside the loop the sums are taken against the f32 offset m log2e, so
+    // an element costs one fma before its exp2; the offset's rounding is
+    // folded in after the loop.
+    if (bm > st.m) {   // new maximum: rebase the sums
+      const float f = st.m == kNegInf ? 0.f : exp2_fast(st.m * kL2E - bm * kL2E);
+      st.s *= f; st.w *= f; st.m = bm;
+    }
     if (st.m != kNegInf) {
+      const float om = st.m * kL2E;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         // offsets from lo are multiples of VEC, so the vector's flags sit in one word
@@ -455,17 +442,108 @@ __global__ __launch_bounds__(GT) void coarse_partial_kernel(
         const uint32_t flags = o < hi - lo ? listed[o >> 5] >> (o & 31) : 0u;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          const float w = exp2_fast((x[u][e] - st.m) * kL2E);
-          ps += w;
-          if (!((flags >> e) & 1u)) pw += w;
+          const float w = exp2_fast(fmaf(x[u][e], kL2E, -om));
+          st.s += w;
+          if (!((flags >> e) & 1u)) st.w += w;
         }
       }
     }
-    st.s += (double)ps;
-    st.w += (double)pw;
+  };
+  if constexpr (ALIGNED) {
+    // The whole vectors of [lo, hi) are read through a buffer resource
+    // (vectors past it read 0 and touch no memory), CD rounds ahead, so the
+    // steady loop loads without branches and keeps a round in flight while
+    // one is folded; in the last round elements past hi become -inf and a
+    // vector straddling hi is completed element by element.
+    typedef typename std::conditional<sizeof(T) == 4, f32x4, u32x4>::type Raw;
+    constexpr int CD = 2;   // rounds in flight
+    const int len = (int)(hi - lo);   // a range spans at most 131,072 ids
+    const int nvec = len / VEC * VEC;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T *>(r + lo), (short)0, nvec * (int)sizeof(T), 0x00020000);
+    Raw q[CD][U];
+    auto fetch = [&](int64_t rd, int sl) {
+      const int o0 = (int)(rd * kStride * U + (int64_t)threadIdx.x * VEC) * (int)sizeof(T);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        q[sl][u] = __builtin_bit_cast(Raw, __builtin_amdgcn_raw_buffer_load_b128(
+                       rs, o0 + u * (int)kStride * (int)sizeof(T), 0, 2 /* streaming */));
+    };
+    auto take = [&](const Raw (&c)[U], float (&x)[U][VEC]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          if constexpr (sizeof(T) == 4) x[u][e] = c[u][e];
+          else x[u][e] = __uint_as_float((e & 1) ? (c[u][e >> 1] & 0xffff0000u) : (c[u][e >> 1] << 16));
+        }
+    };
+#pragma unroll
+    for (int d = 0; d < CD; ++d) fetch(d, d);
+    int64_t rd = 0;
+    for (; rd + CD < rounds; rd += CD) {   // none of these rounds is the last
+#pragma unroll
+      for (int d = 0; d < CD; ++d) {
+        Raw c[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) c[u] = q[d][u];
+        fetch(rd + d + CD, d);
+        float x[U][VEC];
+        take(c, x);
+        fold(x, lo + (rd + d) * kStride * U + (int64_t)threadIdx.x * VEC);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < CD; ++d) {   // the 1 .. CD rounds left
+      if (rd + d < rounds) {
+        const int64_t base = lo + (rd + d) * kStride * U + (int64_t)threadIdx.x * VEC;
+        float x[U][VEC];
+        take(q[d], x);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t p = base + u * kStride;
+          if (p + VEC > hi) {   // the last vectors of the range only
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+              x[u][e] = p + e < hi ? (p - lo >= nvec ? ld_f32(r, p + e) : x[u][e]) : kNegInf;
+          }
+        }
+        fold(x, base);
+      }
+    }
+  } else {
+    for (int64_t rd = 0; rd < rounds; ++rd) {
+      const int64_t base = lo + rd * kStride * U + (int64_t)threadIdx.x * VEC;
+      float x[U][VEC];
+#pragma unroll
+      for (int u = 0; u < U; ++u) load_vecn<T, VEC, false>(r, base + u * kStride, hi, x[u]);
+      fold(x, base);
+    }
   }
-  const LseState tot = lse_block(st, xw);
-  if (threadIdx.x == 0) part[row * splits + split] = tot;
+  // Sums against m itself: the exact product m log2e is om + r (r =
+  // fma(m, log2e, -om), exact), so every weight above is 2^r too large.
+  if (st.m != kNegInf) {
+    const float g = exp2_fast(-fmaf(st.m, kL2E, -(st.m * kL2E)));
+    st.s *= g; st.w *= g;
+  }
+  // block merge in a fixed order: a butterfly within each wave, then the
+  // four waves in order
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    CoarseState q;
+    q.m = __shfl_xor(st.m, o);
+    q.s = __shfl_xor(st.s, o);
+    q.w = __shfl_xor(st.w, o);
+    st = (threadIdx.x & o) ? coarse_merge(q, st) : coarse_merge(st, q);
+  }
+  if ((threadIdx.x & 63) == 0) xw[threadIdx.x >> 6] = st;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    CoarseState r = xw[0];
+#pragma unroll
+    for (int w = 1; w < GT / 64; ++w) r = coarse_merge(r, xw[w]);
+    part[row * splits + split] = LseState{r.m, (double)r.s, 0.0, (double)r.w};
+  }
 }
 
 __global__ __launch_bounds__(GT) void coarse_finalize_kernel(
