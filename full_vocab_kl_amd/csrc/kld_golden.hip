@@ -33,12 +33,13 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int GT = 256;                  // threads per block
+constexpr int GT = 256;                  // threads per block (513-cell score)
+constexpr int XT = 512;                  // threads per block (golden export: one block per row)
 constexpr int GE = 8;                    // consecutive elements per thread and round
-constexpr int GROUND = GT * GE;          // elements per round
+constexpr int GROUND = XT * GE;          // elements per export round
 constexpr int GK = KLD_GOLDEN_TOPK;      // listed ids per record
-constexpr int GCAP = 4096;               // candidate keys per block
-static_assert(GCAP % GT == 0 && GCAP - GROUND >= GK, "buffer holds the kept keys plus a round");
+constexpr int GCAP = 8192;               // candidate keys per export block
+static_assert(GCAP % XT == 0 && GCAP - GROUND >= GK, "buffer holds the kept keys plus a round");
 
 __device__ __forceinline__ float ld_f32(const float *r, int64_t j) { return r[j]; }
 __device__ __forceinline__ float ld_f32(const uint16_t *r, int64_t j) { return bf16_to_f32(r[j]); }
@@ -89,7 +90,7 @@ __device__ __forceinline__ LseState lse_merge(const LseState &a, const LseState 
   return r;
 }
 
-// Block-wide merge (fixed butterfly, then the four waves in order); every
+// Block-wide merge (fixed butterfly, then the eight waves in order); every
 // thread gets the result.
 __device__ LseState lse_block(LseState st, LseState *xw) {
 #pragma unroll
@@ -106,7 +107,7 @@ __device__ LseState lse_block(LseState st, LseState *xw) {
   __syncthreads();
   LseState r = xw[0];
 #pragma unroll
-  for (int w = 1; w < GT / 64; ++w) r = lse_merge(r, xw[w]);
+  for (int w = 1; w < XT / 64; ++w) r = lse_merge(r, xw[w]);
   __syncthreads();
   return r;
 }
@@ -131,13 +132,13 @@ struct GoldenShared {
   uint64_t buf[GCAP];
   uint64_t top[GK];
   uint32_t hist[256];
-  LseState xw[GT / 64];
+  LseState xw[XT / 64];
   uint64_t thr;
   int cnt;
   int cut;                      // the buffer has been cut to its GK best
   int kept;                     // keys kept by a cut
-  int wcnt[GT / 64];            // per wave: keys at or above a trial prefix
-  uint32_t wthr[GT / 64];       // per wave: sampled threshold value
+  int wcnt[XT / 64];            // per wave: keys at or above a trial prefix
+  uint32_t wthr[XT / 64];       // per wave: sampled threshold value
   __align__(8) uint32_t sel[6];
 };
 
@@ -145,15 +146,15 @@ struct GoldenShared {
 // the GK-th the threshold; the mass of every dropped key is added to the
 // thread's unlisted sum (st.w), so the tail is summed directly in one pass.  The GK-th key is found bit by bit from the top:
 // a bit is kept if at least GK keys reach the prefix (each thread counts its
-// keys, a butterfly sums a wave's counts, LDS the four waves').  No
+// keys, a butterfly sums a wave's counts, LDS the eight waves').  No
 // histogram: keys that share their high bits would pile onto one bin.
 __device__ void golden_compact(GoldenShared &sh, LseState &st) {
-  uint64_t k[GCAP / GT];
+  uint64_t k[GCAP / XT];
   const int cnt = sh.cnt;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int q = 0; q < GCAP / GT; ++q) {
-    const int e = q * GT + (int)threadIdx.x;
+  for (int q = 0; q < GCAP / XT; ++q) {
+    const int e = q * XT + (int)threadIdx.x;
     k[q] = e < cnt ? sh.buf[e] : 0ull;
   }
   uint64_t t = 0;   // stays 0 when fewer than GK keys exist: all are kept
@@ -162,21 +163,21 @@ __device__ void golden_compact(GoldenShared &sh, LseState &st) {
       const uint64_t c = t | (1ull << b);
       int n = 0;
 #pragma unroll
-      for (int q = 0; q < GCAP / GT; ++q) n += k[q] >= c ? 1 : 0;
+      for (int q = 0; q < GCAP / XT; ++q) n += k[q] >= c ? 1 : 0;
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) n += __shfl_xor(n, o);
       if (lane == 0) sh.wcnt[wave] = n;
       __syncthreads();
       int tot = 0;
 #pragma unroll
-      for (int w = 0; w < GT / 64; ++w) tot += sh.wcnt[w];
+      for (int w = 0; w < XT / 64; ++w) tot += sh.wcnt[w];
       __syncthreads();
       if (tot >= GK) t = c;
     }
   }
   // the dropped keys' mass (each key is in one thread's slice)
 #pragma unroll
-  for (int q = 0; q < GCAP / GT; ++q) {
+  for (int q = 0; q < GCAP / XT; ++q) {
     if (k[q] != 0ull && k[q] < t) {
       const float x = key_value(k[q]);
       if (x != kNegInf) {   // (a -inf logit has no mass)
@@ -189,12 +190,12 @@ __device__ void golden_compact(GoldenShared &sh, LseState &st) {
   if (threadIdx.x == 0) sh.kept = 0;
   __syncthreads();
 #pragma unroll
-  for (int q = 0; q < GCAP / GT; ++q)
+  for (int q = 0; q < GCAP / XT; ++q)
     if (k[q] != 0ull && k[q] >= t) sh.top[atomicAdd(&sh.kept, 1)] = k[q];
   __syncthreads();
   const int kept = sh.kept;
-  for (int i = kept + (int)threadIdx.x; i < GK; i += GT) sh.top[i] = 0ull;
-  for (int i = (int)threadIdx.x; i < kept; i += GT) sh.buf[i] = sh.top[i];
+  for (int i = kept + (int)threadIdx.x; i < GK; i += XT) sh.top[i] = 0ull;
+  for (int i = (int)threadIdx.x; i < kept; i += XT) sh.buf[i] = sh.top[i];
   __syncthreads();
   if (threadIdx.x == 0) {
     sh.cnt = kept;
@@ -206,7 +207,7 @@ __device__ void golden_compact(GoldenShared &sh, LseState &st) {
 }
 
 template <typename T, bool ALIGNED>
-__global__ __launch_bounds__(GT) void golden_export_kernel(
+__global__ __launch_bounds__(XT) void golden_export_kernel(
     const T *__restrict__ logits, int64_t ld, int64_t v, const int32_t *__restrict__ target,
     int32_t *__restrict__ ids, float *__restrict__ lp, float *__restrict__ rec) {
   __shared__ GoldenShared sh;
@@ -216,14 +217,14 @@ __global__ __launch_bounds__(GT) void golden_export_kernel(
   // Starting threshold from a sample of the row: 16 evenly spread ids per
   // thread; each wave takes the value of the 5th best key of its 1,024 (a
   // bit search on the top 32 key bits, counts summed over the lanes) and the
-  // block the smallest of the four.  Keys below it are never appended, so
+  // block the smallest of the eight.  Keys below it are never appended, so
   // the buffer rarely needs cutting before the end.  If fewer than GK keys
   // reach it, the candidates are collected again from no threshold (below).
   {
-    uint64_t sk[GCAP / GT];
+    uint64_t sk[GCAP / XT];
 #pragma unroll
-    for (int q = 0; q < GCAP / GT; ++q) {
-      const int64_t p = ((int64_t)(q * GT + (int)threadIdx.x) * v) / GCAP;
+    for (int q = 0; q < GCAP / XT; ++q) {
+      const int64_t p = ((int64_t)(q * XT + (int)threadIdx.x) * v) / GCAP;
       const float x = ld_f32(r, p);
       sk[q] = x == x ? topk_key(x, (int)p) : 0ull;
     }
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(GT) void golden_export_kernel(
       const uint32_t c = pre | (1u << b);
       int cnt = 0;
 #pragma unroll
-      for (int q = 0; q < GCAP / GT; ++q) cnt += (uint32_t)(sk[q] >> 32) >= c ? 1 : 0;
+      for (int q = 0; q < GCAP / XT; ++q) cnt += (uint32_t)(sk[q] >> 32) >= c ? 1 : 0;
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o);
       if (cnt >= 5) pre = c;
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(GT) void golden_export_kernel(
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t m = sh.wthr[0];
-    for (int w = 1; w < GT / 64; ++w) m = sh.wthr[w] < m ? sh.wthr[w] : m;
+    for (int w = 1; w < XT / 64; ++w) m = sh.wthr[w] < m ? sh.wthr[w] : m;
     sh.thr = (uint64_t)m << 32;   // a key with that value and any id reaches it
     sh.cut = 0;
   }
@@ -331,11 +332,11 @@ __global__ __launch_bounds__(GT) void golden_export_kernel(
   // the GK best keys, sorted descending (zero keys -- fewer than GK valid
   // ids -- sort last)
   __syncthreads();
-  bitonic_desc<GT>(sh.top, GK);
+  bitonic_desc<XT>(sh.top, GK);
   const LseState tot = lse_block(st, sh.xw);
   const double ls = log(tot.s);
   const double lse = (double)tot.m + ls;
-  for (int i = (int)threadIdx.x; i < GK; i += GT) {
+  for (int i = (int)threadIdx.x; i < GK; i += XT) {
     const uint64_t key = sh.top[i];
     ids[row * GK + i] = key ? key_id(key) : 0;
     lp[row * GK + i] = key ? (float)((double)key_value(key) - lse) : kNegInf;
@@ -595,7 +596,7 @@ __global__ __launch_bounds__(GT) void coarse_finalize_kernel(
 hipError_t launch_golden_export(const void *logits, int dtype, int64_t n, int64_t v, int64_t ld,
                                 bool aligned, const int32_t *target, int32_t *ids, float *lp,
                                 float *rec, hipStream_t stream) {
-  const dim3 grid((unsigned)n), block(GT);
+  const dim3 grid((unsigned)n), block(XT);
   if (dtype == 0) {
     if (aligned)
       hipLaunchKernelGGL((golden_export_kernel<float, true>), grid, block, 0, stream,
