@@ -206,6 +206,46 @@ def _streams():
     return _STREAMS
 
 
+class _Chain:
+    """The launches of a step made of several calls (chunks, batches), spread
+    over the two streams: launch g runs on stream g % 2 and first waits for the
+    end of launch g - 1's dominant kernel, so the dominant kernels run one at
+    a time while a launch's closing kernels run beside the next launch's
+    dominant kernel -- within a step as across steps.  A launch's workspace
+    goes by g % 2 (launch g + 2, on the same stream, runs after launch g's
+    closing kernels).  One chain serves every step of a workload."""
+
+    def __init__(self):
+        self.g = 0
+        self.prev = None
+        self.spare = [(TimingEvent(), TimingEvent()) for _ in range(4)]   # untimed launches
+        self.tail = [TimingEvent() for _ in range(2)]
+
+    def launch(self, fn, ev=None):
+        """fn(parity, (start, stop)) issues one call with the event pair
+        around its dominant kernel, on the current stream."""
+        import torch
+        s = _streams()[self.g % 2]
+        if self.prev is not None and _hip().hipStreamWaitEvent(s.cuda_stream, self.prev, 0) != 0:
+            raise RuntimeError("hipStreamWaitEvent failed")
+        pair = ev if ev is not None else self.spare[self.g % len(self.spare)]
+        with torch.cuda.stream(s):
+            fn(self.g % 2, pair)
+        self.prev = pair[1].cuda_event
+        self.g += 1
+
+    def join(self):
+        """The stream of the last launch, after the other stream's work so
+        far: what closes a step (its summary) runs there."""
+        ss = _streams()
+        last, other = ss[(self.g - 1) % 2], ss[self.g % 2]
+        t = self.tail[self.g % 2]
+        if (_hip().hipEventRecord(t.cuda_event, other.cuda_stream) != 0 or
+                _hip().hipStreamWaitEvent(last.cuda_stream, t.cuda_event, 0) != 0):
+            raise RuntimeError("stream join failed")
+        return last
+
+
 def _timeit(step, steps, warmup, n_ev=1):
     """Run warmup untimed steps, then `steps` timed ones; step(i, evs) gets a
     list of n_ev (start, stop) event pairs for the dominant kernel's launches
@@ -505,15 +545,19 @@ def long_trace(steps, warmup, cpu_sample):
     views = [[{k: x[c * chunk:(c + 1) * chunk] for k, x in o.items()} for c in range(nchunk)]
              for o in outs]
 
+    chain = _Chain()   # chunk calls alternate streams: a chunk's closing kernels overlap the next
+
     def step(i, ev):
         k = i % 2
         for c in range(nchunk):
             sl = slice(c * chunk, (c + 1) * chunk)
-            kld.kld_fused_head(W, hr[sl], hc[sl], tg[sl], topk=True, ws=ws[k], out=views[k][c],
-                               events=ev[c] if ev else None)
+            chain.launch(lambda p, e: kld.kld_fused_head(W, hr[sl], hc[sl], tg[sl], topk=True,
+                                                         ws=ws[p], out=views[k][c], events=e),
+                         ev[c] if ev else None)
         o = outs[k]
-        kld.kld_summary(o["kl"], o["argmax_ref"], o["argmax_cand"], o["nll_ref"],
-                        o["nll_cand"], quantiles=QUANTILES, ws=ws_s[k], out=summs[k])
+        with torch.cuda.stream(chain.join()):
+            kld.kld_summary(o["kl"], o["argmax_ref"], o["argmax_cand"], o["nll_ref"],
+                            o["nll_cand"], quantiles=QUANTILES, ws=ws_s[k], out=summs[k])
 
     elapsed, kernel_ms = _timeit(step, steps, warmup, n_ev=nchunk)
     summ, out = summs[0], outs[0]
@@ -651,16 +695,21 @@ def bf16_topk_stream(steps, warmup, cpu_sample):
     tails = [torch.empty(total, dtype=torch.float32, device=dev) for _ in range(2)]
     views = [[{k: x[r0:r0 + nb] for k, x in o.items()} for r0, nb, _, _ in batches] for o in outs]
 
+    chain = _Chain()   # batch calls alternate streams: a batch's closing kernels overlap the next
+
     def step(i, ev):
         k = i % 2
         for j, (r0, nb, ra, rb) in enumerate(batches):
-            o = kld.kld_from_logits(ra, rb, None, topk=True, ws=ws[k], out=views[k][j],
-                                    events=ev[j] if ev else None)
-            kld.kld_topk_tail(o["ids_ref"], o["lp_ref"], o["ids_cand"], o["lp_cand"], v,
-                              out=tails[k][r0:r0 + nb])
+            def call(p, e):
+                o = kld.kld_from_logits(ra, rb, None, topk=True, ws=ws[p], out=views[k][j],
+                                        events=e)
+                kld.kld_topk_tail(o["ids_ref"], o["lp_ref"], o["ids_cand"], o["lp_cand"], v,
+                                  out=tails[k][r0:r0 + nb])
+            chain.launch(call, ev[j] if ev else None)
         o = outs[k]
-        kld.kld_summary(o["kl"], o["argmax_ref"], o["argmax_cand"], quantiles=QUANTILES,
-                        ws=ws_s[k], out=summs[k])   # no targets in this workload: no NLL
+        with torch.cuda.stream(chain.join()):
+            kld.kld_summary(o["kl"], o["argmax_ref"], o["argmax_cand"], quantiles=QUANTILES,
+                            ws=ws_s[k], out=summs[k])   # no targets in this workload: no NLL
 
     elapsed, kernel_ms = _timeit(step, steps, warmup, n_ev=len(batches))
     summ, out, tail = summs[0], outs[0], tails[0]
