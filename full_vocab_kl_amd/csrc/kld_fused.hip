@@ -116,16 +116,8 @@ __device__ __forceinline__ int logical_block(int b, int nb) {
 // scores, and the head streams once per group.  Within a group the XCD-aware
 // order above applies.  kGroupTiles is a multiple of 8, so every group starts
 // on XCD 0.  Returns (vocabulary tile, position tile).
-//
-// A call of one group (at most 16 position tiles, such as one 2047-position
-// window) takes each XCD's range in super-tiles of 8 head tiles x 4 position
-// tiles -- 32 blocks, one per CU of the XCD -- instead of 2 x 16: a round of
-// an XCD's blocks then reads 12 distinct tiles rather than 18, which cut the
-// window's L2 misses by a quarter and its time by 1.3 %; with several groups
-// the 2 x 16 order measured as fast or faster (1 % on 256 position tiles).
 constexpr int kGroupTiles = 16;
 static_assert(kGroupTiles % kXcds == 0, "groups start on XCD 0");
-constexpr int kSuperV = 8, kSuperP = 4;
 __device__ __forceinline__ int2 tile_of_block(int b, int npt, int nvt) {
   const int per = nvt * kGroupTiles;           // blocks of a full group
   const int ngroups = (npt + kGroupTiles - 1) / kGroupTiles;
@@ -133,14 +125,7 @@ __device__ __forceinline__ int2 tile_of_block(int b, int npt, int nvt) {
   if (g > ngroups - 1) g = ngroups - 1;
   const int gp = min(kGroupTiles, npt - g * kGroupTiles);   // position tiles of group g
   const int L = logical_block(b - g * per, nvt * gp);
-  if (ngroups > 1) return make_int2(L / gp, g * kGroupTiles + L % gp);
-  // rows of kSuperV head tiles (the last may be shorter), each row in
-  // column blocks of kSuperP position tiles (the last may be narrower)
-  const int row = L / (kSuperV * gp), v0 = row * kSuperV, rem = L - row * kSuperV * gp;
-  const int nv = min(kSuperV, nvt - v0);
-  const int col = rem / (nv * kSuperP), p0 = col * kSuperP, rem2 = rem - col * nv * kSuperP;
-  const int np = min(kSuperP, gp - p0);
-  return make_int2(v0 + rem2 / np, p0 + rem2 % np);
+  return make_int2(L / gp, g * kGroupTiles + L % gp);
 }
 
 // Buffer resource over `bytes` bytes at p (raw addressing, no stride): loads
