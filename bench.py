@@ -22,6 +22,7 @@ the ranked-next rows.
 Measurement helpers (no scoring): --copy-calibration (a plain 1 GiB device
 copy, for scaling the FETCH_SIZE / WRITE_SIZE counters), --gemm-calibration
 (the vendor library's bf16 GEMM at the head's shape, for comparison),
+--read-calibration (torch reductions and a copy over 4 GiB, for comparison),
 --record-traffic DIR (turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs into
 profiles/traffic.json) and --counter-table DIR (per-kernel averages of any
 rocprofv3 counter run).
@@ -59,6 +60,8 @@ def _args():
                    help="skip the secondary workloads")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (counter calibration)")
+    p.add_argument("--read-calibration", action="store_true",
+                   help="only time torch reductions and a copy over 4 GiB (comparison)")
     p.add_argument("--gemm-calibration", action="store_true",
                    help="only time the vendor bf16 GEMM at the head's shape (comparison)")
     p.add_argument("--record-traffic", metavar="DIR",
@@ -1054,6 +1057,34 @@ def gemm_calibration(reps=10):
     print(json.dumps({"gemm_calibration": res}), flush=True)
 
 
+def read_calibration(reps=10):
+    """Library streaming rates on the same chip, for comparison with the
+    logits passes: torch.sum and torch.amax over a resident 4 GiB f32 tensor
+    (read once) and torch's clone of it (read and write).  Not part of the
+    path."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = (4 << 30) // 4
+    x = torch.randn(n, device=dev)
+    res = []
+    for name, fn, moved in (("sum", lambda: x.sum(), 4 * n), ("amax", lambda: x.amax(), 4 * n),
+                            ("clone", lambda: x.clone(), 8 * n)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
+        gbs = moved / (ms * 1e-3) / 1e9
+        res.append({"op": f"torch.{name}, 4 GiB f32", "ms": round(ms, 4), "GB/s": round(gbs, 1),
+                    "frac_of_8000": round(gbs / PEAK_HBM_GBS, 4)})
+    print(json.dumps({"read_calibration": res}), flush=True)
+
+
 def _read_counter_csv(d):
     """Rows of every rocprofv3 counter_collection CSV under d."""
     import csv
@@ -1176,6 +1207,9 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.read_calibration:
+        read_calibration()
         return
     if args.gemm_calibration:
         gemm_calibration()
