@@ -17,17 +17,17 @@
 // least 64 elements of the block's range are known to reach: at rounds 0, 1,
 // 2, 3, 5, 7, 11, 15, ... every wave finds the 16th largest of its 64 lanes'
 // running maxima (distinct elements) and publishes it; the smallest of the
-// four waves' values is reached by 64 distinct elements.  Candidates are appended to a
-// per-wave LDS buffer (ballot + mbcnt offsets, no atomics, no block barrier);
-// a wave whose buffer fills sorts it in registers, keeps its 64 best keys and
-// from then on also requires keys above the 64th.  At the end each wave drops
-// the entries below the final threshold; after a block barrier one wave per
-// side gathers the four waves' survivors and cuts them to the 64 best (the
-// two sides in parallel, beside a third wave that merges the row states);
-// topk_merge_kernel
-// (kld_topk.hip) merges the splits of a row and converts them to ids and fp16
-// log-probs.  On these inputs only a few hundred elements per row and side
-// pass the threshold, so the export costs little beyond the streaming pass.
+// four waves' values is reached by 64 distinct elements.  Candidates are
+// appended to a per-wave LDS buffer (ballot + mbcnt offsets, no atomics, no
+// block barrier in the streaming loop); a wave whose buffer fills sorts it
+// in registers, keeps its 64 best keys and from then on also requires keys
+// above the 64th.  At the end each wave drops the entries below the final
+// threshold; after a block barrier one wave per side gathers the four waves'
+// survivors and cuts them to the 64 best (the two sides in parallel, beside
+// a third wave that merges the row states); topk_merge_kernel (kld_topk.hip)
+// merges the splits of a row and converts them to ids and fp16 log-probs.  On
+// these inputs only a few hundred elements per row and side pass the
+// threshold, so the export costs little beyond the streaming pass.
 #include "kld_device.hpp"
 #include "kld_launch.hpp"
 
