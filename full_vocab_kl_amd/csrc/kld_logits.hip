@@ -282,7 +282,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
   // (exact arithmetic would give L2E ((a - ref_a) - (b - ref_b)) + (r_a - r_b),
   // r = ref(m) L2E - o).  fold_offsets converts the sums back after the loop.
   float ma = kNegInf, sa = 0.f, t = 0.f, mb = kNegInf, sb = 0.f;
-  int ia = kNoId, ib = kNoId;
+  int ia = kNoId, ib = kNoId;   // argmax ids (top-k kernels: in the loop, the round of the maximum)
 
   constexpr int kStride = kThreads * VEC;
   constexpr int kRound = kStride * U;   // ids per round
@@ -398,15 +398,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
       const int k = __builtin_ctz(bits);
       return id0 + (k / VEC) * kStride + (k % VEC);
     };
-    if (bma > ma) {   // new maximum: locate its lowest id in this batch, rebase the sums
-      const int id = first_id(ca, bma);
+    // A new maximum rebases the sums.  The plain kernels locate its id in
+    // this batch at once; the top-k kernels, whose loop is VALU-bound, record
+    // the round instead and locate the id after the loop, so the many early
+    // rounds in which some lane's maximum rises cost the wave no search.
+    if (bma > ma) {
+      int id = r;
+      if constexpr (!TOPK) id = first_id(ca, bma);
       const float o = bma * kL2E, oa = ref_of(ma) * kL2E;
       const float f = ma == kNegInf ? 0.f : exp2_fast(oa - o);
       if (TWO && sa != 0.f) t = fmaf(-sa, o - oa, t);
       t *= f; sa *= f; ma = bma; ia = id;
     }
     if (TWO && bmb > mb) {
-      const int id = first_id(cb, bmb);
+      int id = r;
+      if constexpr (!TOPK) id = first_id(cb, bmb);
       const float o = bmb * kL2E, ob = ref_of(mb) * kL2E;
       if (sa != 0.f) t = fmaf(sa, o - ob, t);
       sb *= mb == kNegInf ? 0.f : exp2_fast(ob - o);
@@ -559,6 +565,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
       }
       if (lane == 0) sh.lcount[side][wave] = n2;
     }
+  }
+  if constexpr (TOPK) {
+      // locate: each side's argmax is the lowest id holding its maximum in
+      // the round where the maximum last rose (ia, ib hold that round, kNoId
+      // while a side has seen only -inf): that round's vectors are read again
+      // -- as the loop read them, ids past hi as -inf -- and the lowest
+      // element equal to the maximum is taken (one bit per element, then the
+      // lowest set bit).
+    auto locate = [&](const T *rowp, int rr, float m) -> int {
+      static_assert(U * VEC <= 32, "one bit per element of a round");
+      const int id0 = (int)lo + rr * kRound + tofs;
+      uint32_t bits = 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const Raw c = load_raw<T, VEC, ALIGNED>(rowp, (int64_t)id0 + u * kStride, hi);
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) bits |= (elem(c, j) == m ? 1u : 0u) << (u * VEC + j);
+      }
+      const int k = __builtin_ctz(bits);
+      return id0 + (k / VEC) * kStride + (k % VEC);
+    };
+    if (ia != kNoId) ia = locate(ra, ia, ma);
+    if (TWO && ib != kNoId) ib = locate(rb, ib, mb);
   }
   {   // fold_offsets: back to sums against ref(ma), ref(mb) and t in nats.
       // The exact product ref(m) L2E is o + r (r = fma(ref, L2E, -o), exact
