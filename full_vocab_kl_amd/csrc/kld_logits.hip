@@ -572,7 +572,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
       // while a side has seen only -inf): that round's vectors are read again
       // -- as the loop read them, ids past hi as -inf -- and the lowest
       // element equal to the maximum is taken (one bit per element, then the
-      // lowest set bit).
+      // lowest set bit).  Only lanes that hold the wave's maximum can supply
+      // the merged argmax, so only they read (a lane's read fetches a whole
+      // cache line, which all 64 lanes would pay for); the others drop their
+      // id, which the merge never takes from a smaller maximum.
     auto locate = [&](const T *rowp, int rr, float m) -> int {
       static_assert(U * VEC <= 32, "one bit per element of a round");
       const int id0 = (int)lo + rr * kRound + tofs;
@@ -586,8 +589,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
       const int k = __builtin_ctz(bits);
       return id0 + (k / VEC) * kStride + (k % VEC);
     };
-    if (ia != kNoId) ia = locate(ra, ia, ma);
-    if (TWO && ib != kNoId) ib = locate(rb, ib, mb);
+    float wa = ma, wb = mb;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      wa = fmaxf(wa, __shfl_xor(wa, o));
+      if (TWO) wb = fmaxf(wb, __shfl_xor(wb, o));
+    }
+    if (ia != kNoId) ia = ma == wa ? locate(ra, ia, ma) : kNoId;
+    if (TWO && ib != kNoId) ib = mb == wb ? locate(rb, ib, mb) : kNoId;
   }
   {   // fold_offsets: back to sums against ref(ma), ref(mb) and t in nats.
       // The exact product ref(m) L2E is o + r (r = fma(ref, L2E, -o), exact
