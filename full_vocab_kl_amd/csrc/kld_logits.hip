@@ -111,6 +111,12 @@ struct TopkShared {
 __device__ __forceinline__ float uniform_f(float x) {
   return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
 }
+// Maximum over the wave's 64 lanes (no NaN among them), in a scalar register.
+__device__ __forceinline__ float wave_max_uniform(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return uniform_f(x);
+}
 __device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(x >> 32));
@@ -281,8 +287,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
   // t sums w (e_a - e_b), the log2-scaled difference against both offsets
   // (exact arithmetic would give L2E ((a - ref_a) - (b - ref_b)) + (r_a - r_b),
   // r = ref(m) L2E - o).  fold_offsets converts the sums back after the loop.
+  // The maxima ma, mb (so the offsets) are the wave's in the plain kernels
+  // and the lane's in the top-k kernels, whose bounds need the lanes' own.
   float ma = kNegInf, sa = 0.f, t = 0.f, mb = kNegInf, sb = 0.f;
-  int ia = kNoId, ib = kNoId;   // argmax ids (top-k kernels: in the loop, the round of the maximum)
+  // argmax ids; in the top-k loop, the round in which the lane's maximum rose
+  int ia = kNoId, ib = kNoId;
 
   constexpr int kStride = kThreads * VEC;
   constexpr int kRound = kStride * U;   // ids per round
@@ -336,18 +345,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
   auto update = [&]() __attribute__((always_inline)) {
     float b16[2];
     wave_16th_bound2(ma, mb, b16[0], b16[1]);   // (mb unused with one side)
-    // no fence: another wave may read an older (smaller) value, which is
-    // still valid, and a fence here would also wait for this wave's
-    // prefetched row loads
+    // Relaxed workgroup-scope atomics on LDS addresses: plain LDS reads and
+    // writes with no fence (another wave may read an older, smaller value,
+    // which is still valid).  Volatile accesses would keep generic addresses
+    // and become flat operations, whose wait also drains this wave's
+    // prefetched row loads.
 #pragma unroll
     for (int side = 0; side < NS; ++side)
-      if (lane == 0) reinterpret_cast<volatile float *>(sh.bound[side])[wave] = b16[side];
+      if (lane == 0)
+        __hip_atomic_store(lds(&sh.bound[side][wave]), b16[side], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
 #pragma unroll
     for (int side = 0; side < NS; ++side) {
-      const volatile float *bd = sh.bound[side];
-      float b = bd[0];
+      const Lds<float> bd = lds(sh.bound[side]);
+      float b = __hip_atomic_load(bd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) b = fminf(b, bd[w]);
+      for (int w = 1; w < kWaves; ++w)
+        b = fminf(b, __hip_atomic_load(bd + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
       thr[side] = uniform_f(fmaxf(thr[side], b));
     }
   };
@@ -398,25 +412,51 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TOPK &
       const int k = __builtin_ctz(bits);
       return id0 + (k / VEC) * kStride + (k % VEC);
     };
-    // A new maximum rebases the sums.  The plain kernels locate its id in
-    // this batch at once; the top-k kernels, whose loop is VALU-bound, record
-    // the round instead and locate the id after the loop, so the many early
-    // rounds in which some lane's maximum rises cost the wave no search.
-    if (bma > ma) {
-      int id = r;
-      if constexpr (!TOPK) id = first_id(ca, bma);
-      const float o = bma * kL2E, oa = ref_of(ma) * kL2E;
-      const float f = ma == kNegInf ? 0.f : exp2_fast(oa - o);
-      if (TWO && sa != 0.f) t = fmaf(-sa, o - oa, t);
-      t *= f; sa *= f; ma = bma; ia = id;
-    }
-    if (TWO && bmb > mb) {
-      int id = r;
-      if constexpr (!TOPK) id = first_id(cb, bmb);
-      const float o = bmb * kL2E, ob = ref_of(mb) * kL2E;
-      if (sa != 0.f) t = fmaf(sa, o - ob, t);
-      sb *= mb == kNegInf ? 0.f : exp2_fast(ob - o);
-      mb = bmb; ib = id;
+    if constexpr (!TOPK) {
+      // Plain kernels: the sums are taken against the wave's maximum, so a
+      // round costs one compare and a ballot per side, and the rebase and
+      // the argmax search run only when the wave's maximum rises (a handful
+      // of times per row for typical logits; with a maximum per lane some
+      // lane's rose in nearly every round).  Lanes that hold the new maximum
+      // locate its lowest id in this batch; the others drop theirs, which
+      // the merge never takes from a smaller maximum.  Later rounds that
+      // only equal the maximum hold larger ids and change nothing.
+      if (__ballot(bma > ma)) {
+        const float m = wave_max_uniform(bma);
+        const float o = m * kL2E, oa = ref_of(ma) * kL2E;
+        const float f = ma == kNegInf ? 0.f : exp2_fast(oa - o);
+        if (TWO && sa != 0.f) t = fmaf(-sa, o - oa, t);
+        t *= f; sa *= f;
+        ia = bma == m ? first_id(ca, m) : kNoId;
+        ma = m;
+      }
+      if (TWO && __ballot(bmb > mb)) {
+        const float m = wave_max_uniform(bmb);
+        const float o = m * kL2E, ob = ref_of(mb) * kL2E;
+        if (sa != 0.f) t = fmaf(sa, o - ob, t);
+        sb *= mb == kNegInf ? 0.f : exp2_fast(ob - o);
+        ib = bmb == m ? first_id(cb, m) : kNoId;
+        mb = m;
+      }
+    } else {
+      // Top-k kernels: the lane's own maximum (the bound needs them).  A
+      // rise rebases the lane's sums and records the round; the id is
+      // located after the loop, so the many early rounds in which some
+      // lane's maximum rises cost the wave no per-element search.  (Measured:
+      // the wave's maximum here, with the lanes' kept beside it for the
+      // bound, was slower -- this kernel sits at its register limit.)
+      if (bma > ma) {
+        const float o = bma * kL2E, oa = ref_of(ma) * kL2E;
+        const float f = ma == kNegInf ? 0.f : exp2_fast(oa - o);
+        if (TWO && sa != 0.f) t = fmaf(-sa, o - oa, t);
+        t *= f; sa *= f; ma = bma; ia = r;
+      }
+      if (TWO && bmb > mb) {
+        const float o = bmb * kL2E, ob = ref_of(mb) * kL2E;
+        if (sa != 0.f) t = fmaf(sa, o - ob, t);
+        sb *= mb == kNegInf ? 0.f : exp2_fast(ob - o);
+        mb = bmb; ib = r;
+      }
     }
     if constexpr (TOPK) {
       {   // rounds 0, 1, 2, 3, 5, 7, 11, 15, 23, 31, ...: r + 1 = 2^k or 3 * 2^k
