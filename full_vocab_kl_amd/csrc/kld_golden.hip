@@ -549,29 +549,66 @@ __global__ __launch_bounds__(GT) void coarse_partial_kernel(
   }
 }
 
-__global__ __launch_bounds__(GT) void coarse_finalize_kernel(
-    const LseState *__restrict__ part, int splits, int64_t n, const void *__restrict__ cand,
-    int dtype, int64_t ld, int64_t v, const int32_t *__restrict__ ids,
+template <typename T>
+__global__ __launch_bounds__(64) void coarse_finalize_kernel(
+    const LseState *__restrict__ part, int splits, int64_t n, const T *__restrict__ cand,
+    int64_t ld, int64_t v, const int32_t *__restrict__ ids,
     const float *__restrict__ lp, const float *__restrict__ rec, float *__restrict__ kl) {
-  const int64_t row = (int64_t)blockIdx.x * (GT / 64) + (threadIdx.x >> 6);
+  // One wave per row.  Every load is issued before arithmetic waits on one:
+  // the listed ids and log-probabilities (GK / 64 per lane), the row's
+  // partial states (one per lane, 64 at a time) and the candidate's logits
+  // at the listed ids; then the states are merged in split order (lane i's
+  // state broadcast in turn) and the ids summed in list order per lane.
+  constexpr int PER = GK / 64;
+  static_assert(GK % 64 == 0, "whole waves of listed ids");
+  const int64_t row = blockIdx.x;
   const int lane = threadIdx.x & 63;
   if (row >= n) return;
-  LseState tot = part[row * splits];
-  for (int i = 1; i < splits; ++i) tot = lse_merge(tot, part[row * splits + i]);
+  int32_t id[PER];
+  float l[PER], z[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    id[j] = ids[row * GK + lane + 64 * j];
+    l[j] = lp[row * GK + lane + 64 * j];
+  }
+  LseState mine{kNegInf, 0.0, 0.0, 0.0};
+  if (lane < splits) mine = part[row * splits + lane];
+  // (an id outside [0, v) reads id 0 instead, so that no load sits behind
+  // a branch; such an id makes the row NaN below)
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int64_t c = id[j] >= 0 && (int64_t)id[j] < v ? id[j] : 0;
+    if constexpr (sizeof(T) == 4) z[j] = cand[row * ld + c];
+    else z[j] = bf16_to_f32(cand[row * ld + c]);
+  }
+  LseState tot = mine;
+  for (int base = 0; base < splits; base += 64) {
+    if (base > 0) {
+      mine = LseState{kNegInf, 0.0, 0.0, 0.0};
+      if (base + lane < splits) mine = part[row * splits + base + lane];
+    }
+    const int cnt = splits - base < 64 ? splits - base : 64;
+    for (int i = 0; i < cnt; ++i) {
+      LseState q;
+      q.m = __shfl(mine.m, i);
+      q.s = __shfl(mine.s, i);
+      q.u = __shfl(mine.u, i);
+      q.w = __shfl(mine.w, i);
+      tot = base == 0 && i == 0 ? q : lse_merge(tot, q);   // split 0, then in order
+    }
+  }
   const double lse = (double)tot.m + log(tot.s);
   const double q_t = tot.w / tot.s;
   double acc = 0.0;
   int flags = 0;   // 1: an id outside [0, v); 2: p > 0 against q = 0
-  for (int i = lane; i < GK; i += 64) {
-    const int32_t id = ids[row * GK + i];
-    if (id < 0 || (int64_t)id >= v) { flags |= 1; continue; }
-    const double l = (double)lp[row * GK + i];
-    const double p = exp(l);
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    if (id[j] < 0 || (int64_t)id[j] >= v) { flags |= 1; continue; }
+    const double lj = (double)l[j];
+    const double p = exp(lj);
     if (p == 0.0) continue;
-    const float z = dtype == 0 ? reinterpret_cast<const float *>(cand)[row * ld + id]
-                               : bf16_to_f32(reinterpret_cast<const uint16_t *>(cand)[row * ld + id]);
-    if (z == kNegInf) { flags |= 2; continue; }
-    acc += p * (l - ((double)z - lse));
+    if (z[j] == kNegInf) { flags |= 2; continue; }
+    acc += p * (lj - ((double)z[j] - lse));
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -657,8 +694,12 @@ hipError_t launch_coarse_kl(const void *cand, int dtype, int64_t n, int64_t v, i
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(coarse_finalize_kernel, dim3((unsigned)((n + 3) / 4)), block, 0, stream, part,
-                     g.splits, n, cand, dtype, ld, v, ids, lp, rec, kl);
+  if (dtype == 0)
+    hipLaunchKernelGGL(coarse_finalize_kernel<float>, dim3((unsigned)n), dim3(64), 0, stream, part,
+                       g.splits, n, (const float *)cand, ld, v, ids, lp, rec, kl);
+  else
+    hipLaunchKernelGGL(coarse_finalize_kernel<uint16_t>, dim3((unsigned)n), dim3(64), 0, stream,
+                       part, g.splits, n, (const uint16_t *)cand, ld, v, ids, lp, rec, kl);
   return hipGetLastError();
 }
 
