@@ -406,6 +406,31 @@ __global__ __launch_bounds__(GT) void coarse_partial_kernel(
   const int64_t lo = (int64_t)split * chunk;
   const int64_t hi = lo + chunk < v ? lo + chunk : v;
   const T *r = cand + row * ld;
+  constexpr int64_t kStride = (int64_t)GT * VEC;
+  // Aligned rows: the whole vectors of [lo, hi) are read through a buffer
+  // resource (vectors past it read 0 and touch no memory), CD rounds ahead,
+  // so the steady loop loads without branches and keeps a round in flight
+  // while one is folded.  The first CD rounds are requested before the
+  // bitmap is built, so their latency overlaps it.
+  typedef typename std::conditional<sizeof(T) == 4, f32x4, u32x4>::type Raw;
+  constexpr int CD = 2;   // rounds in flight
+  const int len = (int)(hi - lo);   // a range spans at most 131,072 ids
+  const int nvec = len / VEC * VEC;
+  __amdgpu_buffer_rsrc_t rs;
+  Raw q[CD][U];
+  auto fetch = [&](int64_t rd, int sl) {
+    const int o0 = (int)(rd * kStride * U + (int64_t)threadIdx.x * VEC) * (int)sizeof(T);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      q[sl][u] = __builtin_bit_cast(Raw, __builtin_amdgcn_raw_buffer_load_b128(
+                     rs, o0 + u * (int)kStride * (int)sizeof(T), 0, 2 /* streaming */));
+  };
+  if constexpr (ALIGNED) {
+    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(r + lo), (short)0,
+                                           nvec * (int)sizeof(T), 0x00020000);
+#pragma unroll
+    for (int d = 0; d < CD; ++d) fetch(d, d);
+  }
   const int nw = (int)((hi - lo + 31) >> 5);   // bitmap words of this range
   for (int w = (int)threadIdx.x; w < nw; w += GT) listed[w] = 0u;
   __syncthreads();
@@ -418,7 +443,6 @@ __global__ __launch_bounds__(GT) void coarse_partial_kernel(
   }
   __syncthreads();
 
-  constexpr int64_t kStride = (int64_t)GT * VEC;
   CoarseState st{kNegInf, 0.f, 0.f};
   const int64_t rounds = (hi - lo + kStride * U - 1) / (kStride * U);
   // Fold one round's elements x (first at base) into the thread's state: the
@@ -453,25 +477,8 @@ __global__ __launch_bounds__(GT) void coarse_partial_kernel(
     }
   };
   if constexpr (ALIGNED) {
-    // The whole vectors of [lo, hi) are read through a buffer resource
-    // (vectors past it read 0 and touch no memory), CD rounds ahead, so the
-    // steady loop loads without branches and keeps a round in flight while
-    // one is folded; in the last round elements past hi become -inf and a
-    // vector straddling hi is completed element by element.
-    typedef typename std::conditional<sizeof(T) == 4, f32x4, u32x4>::type Raw;
-    constexpr int CD = 2;   // rounds in flight
-    const int len = (int)(hi - lo);   // a range spans at most 131,072 ids
-    const int nvec = len / VEC * VEC;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<T *>(r + lo), (short)0, nvec * (int)sizeof(T), 0x00020000);
-    Raw q[CD][U];
-    auto fetch = [&](int64_t rd, int sl) {
-      const int o0 = (int)(rd * kStride * U + (int64_t)threadIdx.x * VEC) * (int)sizeof(T);
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        q[sl][u] = __builtin_bit_cast(Raw, __builtin_amdgcn_raw_buffer_load_b128(
-                       rs, o0 + u * (int)kStride * (int)sizeof(T), 0, 2 /* streaming */));
-    };
+    // In the last round elements past hi become -inf and a vector straddling
+    // hi is completed element by element.
     auto take = [&](const Raw (&c)[U], float (&x)[U][VEC]) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -481,8 +488,6 @@ __global__ __launch_bounds__(GT) void coarse_partial_kernel(
           else x[u][e] = __uint_as_float((e & 1) ? (c[u][e >> 1] & 0xffff0000u) : (c[u][e >> 1] << 16));
         }
     };
-#pragma unroll
-    for (int d = 0; d < CD; ++d) fetch(d, d);
     int64_t rd = 0;
     for (; rd + CD < rounds; rd += CD) {   // none of these rounds is the last
 #pragma unroll
@@ -679,10 +684,10 @@ hipError_t launch_coarse_kl(const void *cand, int dtype, int64_t n, int64_t v, i
   const dim3 grid((unsigned)(n * g.splits)), block(GT);
   if (dtype == 0) {
     if (aligned)
-      hipLaunchKernelGGL((coarse_partial_kernel<float, 4, 4, true>), grid, block, 0, stream,
+      hipLaunchKernelGGL((coarse_partial_kernel<float, 4, 2, true>), grid, block, 0, stream,
                          (const float *)cand, ld, v, g.chunk, g.splits, ids, part);
     else
-      hipLaunchKernelGGL((coarse_partial_kernel<float, 4, 4, false>), grid, block, 0, stream,
+      hipLaunchKernelGGL((coarse_partial_kernel<float, 4, 2, false>), grid, block, 0, stream,
                          (const float *)cand, ld, v, g.chunk, g.splits, ids, part);
   } else {
     if (aligned)
