@@ -9,8 +9,10 @@
 // 512 are sorted by a block bitonic network and written with their f32
 // log-probs.  The probability of every id outside the 512 is summed directly
 // in the same pass -- ids below the threshold as they stream by, candidates
-// as cuts drop them -- so a tiny tail mass keeps its relative accuracy
-// instead of coming out of 1 - sum of the listed probabilities.
+// as cuts drop them (exactly, in integer bins per f32 exponent, so that the
+// order in which threads appended candidates cannot change the bits) -- so a
+// tiny tail mass keeps its relative accuracy instead of coming out of 1 - sum
+// of the listed probabilities.
 //
 // coarse_partial_kernel + coarse_finalize_kernel: a candidate row is split
 // into ranges of at most 131,072 ids, one block each.  A block sets the
@@ -131,26 +133,30 @@ __device__ __forceinline__ void raise_max(LseState &st, float bm) {
 struct GoldenShared {
   uint64_t buf[GCAP];
   uint64_t top[GK];
-  uint32_t hist[256];
+  unsigned long long dbin[128];   // a cut's dropped mass: mantissa sums per f32 exponent
   LseState xw[XT / 64];
+  double dd;                    // mass of the keys dropped by cuts, relative to dref
+  float dref;                   // (a key value; -inf while nothing was dropped)
   uint64_t thr;
-  int cnt;
-  int cut;                      // the buffer has been cut to its GK best
+  int rc[3];                    // per round (mod 3): keys the round appended
   int kept;                     // keys kept by a cut
   int wcnt[XT / 64];            // per wave: keys at or above a trial prefix
   uint32_t wthr[XT / 64];       // per wave: sampled threshold value
-  __align__(8) uint32_t sel[6];
 };
 
+
 // Cut the candidate buffer to its GK best keys (distinct; 0 = none) and make
-// the GK-th the threshold; the mass of every dropped key is added to the
-// thread's unlisted sum (st.w), so the tail is summed directly in one pass.  The GK-th key is found bit by bit from the top:
+// the GK-th the threshold; the mass of every dropped key is added to sh.dd,
+// so the tail is summed directly in one pass.  Which thread holds which key
+// depends on the order of the appends, so the dropped mass is summed in a way
+// that order cannot change: each key's weight is taken against the value of
+// the GK-th key (an f32 exp2, at most 1), its mantissa added to the integer
+// bin of its exponent (exact), and the bins summed in a fixed order.  The GK-th key is found bit by bit from the top:
 // a bit is kept if at least GK keys reach the prefix (each thread counts its
 // keys, a butterfly sums a wave's counts, LDS the eight waves').  No
 // histogram: keys that share their high bits would pile onto one bin.
-__device__ void golden_compact(GoldenShared &sh, LseState &st) {
+__device__ int golden_compact(GoldenShared &sh, const int cnt) {
   uint64_t k[GCAP / XT];
-  const int cnt = sh.cnt;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int q = 0; q < GCAP / XT; ++q) {
@@ -176,15 +182,48 @@ __device__ void golden_compact(GoldenShared &sh, LseState &st) {
     }
   }
   // the dropped keys' mass (each key is in one thread's slice)
+  if (t != 0ull) {
+    const float ref = key_value(t);
 #pragma unroll
-  for (int q = 0; q < GCAP / XT; ++q) {
-    if (k[q] != 0ull && k[q] < t) {
-      const float x = key_value(k[q]);
-      if (x != kNegInf) {   // (a -inf logit has no mass)
-        raise_max(st, x);
-        st.w += (double)exp2_fast((x - st.m) * kL2E);   // as the streaming loop weighs it
+    for (int q = 0; q < GCAP / XT; ++q) {
+      if (k[q] != 0ull && k[q] < t) {
+        const float x = key_value(k[q]);
+        if (x != kNegInf) {   // (a -inf logit has no mass)
+          const uint32_t b = __float_as_uint(exp2_fast((x - ref) * kL2E));
+          const uint32_t e = b >> 23;   // at most 127: the weight is at most 1
+          // (a NaN weight, from +inf against +inf, is left out: such a row's
+          // log-sum-exp is +inf and its records NaN anyway)
+          if (b != 0u && e < 128u)
+            atomicAdd(&sh.dbin[e], (unsigned long long)((b & 0x7fffffu) | (e ? 0x800000u : 0u)));
+        }
       }
     }
+    __syncthreads();
+    // bin e holds mantissa sums worth 2^(e - 150) (2^-149 for e = 0); wave 0
+    // sums them by a fixed butterfly and thread 0 adds the sum to sh.dd
+    if (wave == 0) {
+      double sum = 0.0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int e = lane + 64 * h;
+        sum += ldexp((double)sh.dbin[e], e ? e - 150 : -149);
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+      if (lane == 0 && sum > 0.0) {   // (ref is then finite)
+        if (sh.dref == kNegInf) {
+          sh.dd = sum;
+          sh.dref = ref;
+        } else if (ref <= sh.dref) {
+          sh.dd += sum * exp((double)ref - (double)sh.dref);
+        } else {   // a later cut's threshold is higher: rebase to it
+          sh.dd = sh.dd * exp((double)sh.dref - (double)ref) + sum;
+          sh.dref = ref;
+        }
+      }
+    }
+    __syncthreads();   // wave 0 has read the bins
+    if (threadIdx.x < 128) sh.dbin[threadIdx.x] = 0ull;
   }
   // the kept keys (exactly GK when t > 0) in any order, then zeros
   if (threadIdx.x == 0) sh.kept = 0;
@@ -198,12 +237,24 @@ __device__ void golden_compact(GoldenShared &sh, LseState &st) {
   for (int i = (int)threadIdx.x; i < kept; i += XT) sh.buf[i] = sh.top[i];
   __syncthreads();
   if (threadIdx.x == 0) {
-    sh.cnt = kept;
     // GK keys at or above t exist, so no other key below t can be among
     // the GK best (keys are distinct)
     if (t != 0ull) sh.thr = t;
   }
   __syncthreads();
+  return kept;
+}
+
+// Appends of a round go to cnt + (the round's own counter), cnt being the
+// keys in the buffer before the round: the same in every thread, which adds
+// the round's count after the round's barrier.  Three counters in turn: a
+// thread already in the next round appends to another one, so no thread
+// reads a count that is still growing, and every thread takes the same
+// decision to cut the buffer.  Thread 0 clears the counter of round rd + 1
+// during round rd, before its barrier (it was last read before the barrier
+// of round rd - 1).
+__device__ __forceinline__ void golden_append(GoldenShared &sh, uint64_t key, int cnt, int slot) {
+  sh.buf[cnt + atomicAdd(&sh.rc[slot], 1)] = key;
 }
 
 template <typename T, bool ALIGNED>
@@ -240,18 +291,21 @@ __global__ __launch_bounds__(XT) void golden_export_kernel(
     }
     if (lane == 0) sh.wthr[wave] = pre;
   }
-  if (threadIdx.x == 0) sh.cnt = 0;
+  if (threadIdx.x == 0) { sh.rc[0] = sh.rc[1] = sh.rc[2] = 0; sh.dd = 0.0; sh.dref = kNegInf; }
+  if (threadIdx.x < 128) sh.dbin[threadIdx.x] = 0ull;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t m = sh.wthr[0];
     for (int w = 1; w < XT / 64; ++w) m = sh.wthr[w] < m ? sh.wthr[w] : m;
     sh.thr = (uint64_t)m << 32;   // a key with that value and any id reaches it
-    sh.cut = 0;
   }
   __syncthreads();
   const uint64_t thr0 = sh.thr;
 
   LseState st{kNegInf, 0.0, 0.0, 0.0};
+  int cnt = 0;        // keys in the buffer (the same in every thread)
+  bool cut = false;   // the buffer has been cut to its GK best
+  int slot = 0;       // this round's counter
   const int64_t rounds = (v + GROUND - 1) / GROUND;
   // each round's elements are loaded one round ahead, so the loads are in
   // flight while the previous round is processed (and waits at its barrier)
@@ -287,27 +341,34 @@ __global__ __launch_bounds__(XT) void golden_export_kernel(
     for (int e = 0; e < GE; ++e) {
       if (pos + e < v && x[e] == x[e]) {
         const uint64_t key = topk_key(x[e], (int)(pos + e));
-        if (key > th) sh.buf[atomicAdd(&sh.cnt, 1)] = key;
+        if (key > th) golden_append(sh, key, cnt, slot);
         else pw += w[e];
       }
     }
     st.s += (double)ps;
     st.u += (double)pu;
     st.w += (double)pw;
+    const int next = slot == 2 ? 0 : slot + 1;
+    if (threadIdx.x == 0) sh.rc[next] = 0;
     __syncthreads();
-    if (sh.cnt > GCAP - GROUND) {
-      golden_compact(sh, st);
-      if (threadIdx.x == 0) sh.cut = 1;
-      __syncthreads();
+    cnt += sh.rc[slot];
+    slot = next;
+    if (cnt > GCAP - GROUND) {   // no room for another round: cut
+      cnt = golden_compact(sh, cnt);
+      cut = true;
     }
   }
   // Fewer than GK keys reached the sampled threshold and no cut raised it:
   // the GK best may include keys below it, so collect the candidates (and
   // the tail) again from no threshold; the other sums are complete.
-  if (thr0 != 0ull && sh.cut == 0 && sh.cnt < GK) {
+  if (thr0 != 0ull && !cut && cnt < GK) {
     __syncthreads();
-    if (threadIdx.x == 0) { sh.cnt = 0; sh.thr = 0ull; }
+    if (threadIdx.x == 0) {
+      sh.rc[0] = sh.rc[1] = sh.rc[2] = 0; sh.thr = 0ull; sh.dd = 0.0; sh.dref = kNegInf;
+    }
     st.w = 0.0;
+    cnt = 0;
+    slot = 0;
     __syncthreads();
     for (int64_t rd = 0; rd < rounds; ++rd) {
       const int64_t pos = rd * GROUND + (int64_t)threadIdx.x * GE;
@@ -319,16 +380,20 @@ __global__ __launch_bounds__(XT) void golden_export_kernel(
       for (int e = 0; e < GE; ++e) {
         if (pos + e < v && x[e] == x[e]) {
           const uint64_t key = topk_key(x[e], (int)(pos + e));
-          if (key > th) sh.buf[atomicAdd(&sh.cnt, 1)] = key;
+          if (key > th) golden_append(sh, key, cnt, slot);
           else if (st.m != kNegInf) pw += exp2_fast((x[e] - st.m) * kL2E);
         }
       }
       st.w += (double)pw;
+      const int next = slot == 2 ? 0 : slot + 1;
+      if (threadIdx.x == 0) sh.rc[next] = 0;
       __syncthreads();
-      if (sh.cnt > GCAP - GROUND) golden_compact(sh, st);
+      cnt += sh.rc[slot];
+      slot = next;
+      if (cnt > GCAP - GROUND) cnt = golden_compact(sh, cnt);
     }
   }
-  golden_compact(sh, st);
+  golden_compact(sh, cnt);
   // the GK best keys, sorted descending (zero keys -- fewer than GK valid
   // ids -- sort last)
   __syncthreads();
@@ -341,8 +406,12 @@ __global__ __launch_bounds__(XT) void golden_export_kernel(
     ids[row * GK + i] = key ? key_id(key) : 0;
     lp[row * GK + i] = key ? (float)((double)key_value(key) - lse) : kNegInf;
   }
-  const double tail = tot.w / tot.s;   // every id outside the GK listed ones, summed directly
   if (threadIdx.x == 0) {
+    // every id outside the GK listed ones, summed directly: the ids below the
+    // threshold as they streamed by, and the keys the cuts dropped
+    double w = tot.w;
+    if (sh.dd > 0.0) w += sh.dd * exp((double)sh.dref - (double)tot.m);
+    const double tail = w / tot.s;
     float nll = __builtin_nanf("");
     if (target) {
       const int32_t tg = target[row];

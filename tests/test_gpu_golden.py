@@ -90,6 +90,34 @@ def test_golden_export_adversarial():
     assert np.isnan(got["rec"][3, 0])
 
 
+def test_golden_export_repeatable():
+    """Repeated exports of the same rows are bitwise identical: 192 f32 rows
+    of the 512-row logits workload at V = 248,320 and the all-equal row
+    (every id a candidate, so the buffer is cut several times), each exported
+    four times.  (The candidate buffer fills in whatever order the threads
+    append, so the mass of the keys a cut drops must be summed in a way that
+    order cannot change.)"""
+    need_gpu()
+    n, v = 192, synth.VOCAB
+    a, _ = synth.logit_rows(synth.LOGITS_F32, range(n), v)
+    a = np.concatenate([a, np.full((1, v), 1.5, np.float32)])
+    t = synth.targets(synth.LOGITS_F32, range(n + 1), v)
+    da, dt = to_dev(a, False), to_dev(t)
+    first = None
+    for rep in range(4):
+        print(f"golden repeat {rep}", flush=True)
+        out = kld.kld_golden_export(da, dt)
+        torch.cuda.synchronize()
+        got = {k: x.cpu().numpy() for k, x in out.items()}
+        if first is None:
+            first = got
+            continue
+        for k in first:
+            same = first[k].view(np.uint8).reshape(n + 1, -1) == got[k].view(np.uint8).reshape(n + 1, -1)
+            rows = np.flatnonzero(~same.all(axis=1))
+            assert rows.size == 0, f"repeat {rep}: {k} differs in rows {rows[:8]}"
+
+
 def test_golden_export_full_vocab_sampled():
     """Eight f32 rows of the 512-row logits workload at V = 248,320; three
     seeded rows against the oracle."""
