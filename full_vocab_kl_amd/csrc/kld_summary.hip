@@ -215,6 +215,11 @@ __global__ __launch_bounds__(SMALL_T) void summary_small_kernel(
   }
   if (lane == 0) wpart[wave] = s;
   if (tid < nranks) { pre[tid] = 0; rk[tid] = ranks.rank[tid]; }
+  // Pass 0 reads other threads' entries of pre (a run of equal prefixes
+  // shares one histogram).  Without a barrier nothing orders their stores
+  // before those reads: the compiler may even move the read of pre[tid - 1]
+  // above this thread's own store to pre[tid], a different address.
+  __syncthreads();
 
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
