@@ -94,10 +94,37 @@ TRAFFIC_KERNELS = {
 KERNEL_SOURCES = {key: src for key, _, src in TRAFFIC_KERNELS.values()}
 
 
+def _code_text(src):
+    """The source with comments removed and whitespace collapsed, so that a
+    comment edit leaves a kernel's recorded traffic valid (string and
+    character literals are kept as written)."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def _sha(path):
+    """sha256 of a kernel source's code (_code_text)."""
     import hashlib
-    with open(os.path.join(ROOT, path), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    with open(os.path.join(ROOT, path), encoding="utf-8") as f:
+        return hashlib.sha256(_code_text(f.read()).encode()).hexdigest()
 
 
 def _traffic(kernel_key):
@@ -1128,7 +1155,9 @@ def record_traffic(d):
         rec = {"kernels": {}}
     rec["note"] = ("HBM-side bytes per launch of each workload's dominant kernel: FETCH_SIZE and "
                    "WRITE_SIZE (rocprofv3 --pmc, one counter per run, the workload run on its "
-                   "own) scaled by the same counters on a plain copy of known size.")
+                   "own) scaled by the same counters on a plain copy of known size. "
+                   "source_sha256: of the kernel source with comments removed and whitespace "
+                   "collapsed.")
     for wl, (key, part, src) in TRAFFIC_KERNELS.items():
         f = _per_dispatch(_read_counter_csv(os.path.join(d, wl, "pmc_FETCH_SIZE")), "FETCH_SIZE",
                           part)

@@ -3,11 +3,15 @@
 // Each block owns one (row, vocabulary split) pair and streams both rows'
 // slices once, coalesced, 16 bytes per lane per load.  Every lane folds its
 // elements into an online RowState (kld_device.hpp), batch by batch: one max
-// per batch, one rebase when the max moves, then one fma and one exp2 per
-// element per side.  Lanes merge by butterfly, waves through LDS, and the
-// block writes one partial state; finalize_rows_kernel merges the splits (in
-// f64) in a fixed order and writes the per-position outputs.  HBM-bound:
-// 2 v sizeof(T) bytes per position are read once.
+// per batch, a rebase when the maximum moves, then one fma and one exp2 per
+// element per side.  The plain kernels take the wave's maximum as the offset,
+// so the rebase and the argmax search run only when the wave's maximum rises;
+// the top-k kernels keep each lane's own maximum, which their threshold
+// needs, and locate the argmax id after the loop.  Lanes merge by butterfly,
+// waves through LDS, and the block writes one partial state;
+// finalize_rows_kernel merges the splits (in f64) in a fixed order and writes
+// the per-position outputs.  HBM-bound: 2 v sizeof(T) bytes per position are
+// read once.
 //
 // Top-64 export ("Qwopus3.8-27B-Coder-Flash: quality-eval reference",
 // "Files": top-64 ids and fp16 log-probs, sorted) rides the same pass.  Each
