@@ -535,12 +535,24 @@ __global__ __launch_bounds__(GT) void coarse_partial_kernel(
       for (int u = 0; u < U; ++u) {
         // offsets from lo are multiples of VEC, so the vector's flags sit in one word
         const int64_t o = base + u * kStride - lo;
-        const uint32_t flags = o < hi - lo ? listed[o >> 5] >> (o & 31) : 0u;
+        const uint32_t flags =
+            (o < hi - lo ? listed[o >> 5] >> (o & 31) : 0u) & ((1u << VEC) - 1u);
+        // the vector's sum goes to both sums unless it holds a listed id (a
+        // few hundred of a row's vectors): then its unlisted elements only
+        float w[VEC], ws = 0.f;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          const float w = exp2_fast(fmaf(x[u][e], kL2E, -om));
-          st.s += w;
-          if (!((flags >> e) & 1u)) st.w += w;
+          w[e] = exp2_fast(fmaf(x[u][e], kL2E, -om));
+          ws += w[e];
+        }
+        st.s += ws;
+        if (flags == 0u) {
+          st.w += ws;
+        } else {
+          float wu = 0.f;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) wu += (flags >> e) & 1u ? 0.f : w[e];
+          st.w += wu;
         }
       }
     }
