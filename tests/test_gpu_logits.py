@@ -130,6 +130,45 @@ def test_logits_shifted_rows(bf16):
     _compare(got, want, f"shifted bf16={bf16}", strict_mean=True)
 
 
+@pytest.mark.parametrize("topk", [False, True])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_argmax_ties_across_lanes_rounds_and_splits(bf16, topk):
+    """Equal maxima planted at ids that fall in different lanes, rounds,
+    waves and vocabulary splits of full-vocabulary rows: the argmax is the
+    lowest of them on each side (reading R1), both from the plain kernels
+    (maxima per wave, the search when the wave's maximum rises) and from the
+    top-k kernels (maxima per lane, the id located after the loop)."""
+    need_gpu()
+    n, v = 7, synth.VOCAB
+    a, b = synth.logit_rows(synth.LOGITS_F32, range(n), v)
+    a[6] = np.linspace(-4.0, 4.0, v, dtype=np.float32)   # the maximum rises all along the row
+    m = float(np.ceil(max(a.max(), b.max()))) + 8.0       # an integer: exact in bf16 too
+    plants = [[150000, 70000, 200000],                    # different splits
+              [5, 6, 1029],                               # one vector, then another lane
+              [v - 1, 124160],                            # the last id and a split boundary
+              [4, 4100, 8196, 12292],                     # one lane, later rounds
+              [99999, 100000, 1000, 63000],
+              [0, v - 1],
+              [248000, 100]]                              # on the rising row
+    for r, ids in enumerate(plants):
+        a[r, ids] = m
+        b[r, sorted(ids)[1:]] = m                         # the candidate's lowest is the second
+    if bf16:
+        a, b = synth.f32_to_bf16_bits(a), synth.f32_to_bf16_bits(b)
+    da, db = to_dev(a, bf16), to_dev(b, bf16)
+    out = kld.kld_from_logits(da, db, None, topk=topk)
+    torch.cuda.synchronize()
+    got = {k: x.cpu().numpy() for k, x in out.items()}
+    want = _oracle(a, b, None, bf16)
+    for r, ids in enumerate(plants):
+        lo = sorted(ids)
+        assert got["argmax_ref"][r] == lo[0], (r, got["argmax_ref"][r], lo)
+        assert got["argmax_cand"][r] == lo[1], (r, got["argmax_cand"][r], lo)
+    assert np.array_equal(got["argmax_ref"], want["argmax_ref"])
+    assert np.array_equal(got["argmax_cand"], want["argmax_cand"])
+    assert_kl_close(got["kl"], want["kl"], f"ties bf16={bf16} topk={topk}")
+
+
 def test_logits_target_out_of_range_gives_nan_nll():
     need_gpu()
     a, b = synth.logit_rows(synth.LOGITS_F32, range(3), 500)

@@ -48,6 +48,8 @@ def _check_rows(a, b, bf16, where, pad=0):
     for s in ("ref", "cand"):
         assert np.array_equal(got[f"ids_{s}"], want[f"ids_{s}"]), f"{where}: ids {s}"
         assert_lp_close(got[f"lp_{s}"].view(np.uint16), want[f"lp_{s}"], f"{where} {s}")
+        # the top-k kernels locate the argmax after their loop
+        assert np.array_equal(got[f"argmax_{s}"], want[f"argmax_{s}"]), f"{where}: argmax {s}"
     assert_kl_close(got["kl"], want["kl"], where)
     return got
 
