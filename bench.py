@@ -453,7 +453,7 @@ def fused_window(steps, warmup, cpu_sample):
         res["parity"] = _fused_parity(got, want, z, v)
         res["cpu_baseline"] = {
             "value": len(rows) / dt, "unit": "positions/s", "cores": _cores(), "kind": "oracle",
-            "sample": f"{len(rows)} seeded positions of the 2047-position window: head logits "
+            "sample": f"{len(rows)} of the 2047 positions of the window: head logits "
                       f"in f64 for both sides over all 248,320 ids (one BLAS product), then KL, "
                       f"argmax, NLL, top-64 and tail KLD per row on {_cores()} threads, and the "
                       f"summary; {dt:.1f} s"}
@@ -1030,7 +1030,7 @@ FUNCS = {"fused_window": fused_window, "logits_f32": logits_f32,
          "long_trace": long_trace, "golden_f32": golden_f32, "windows_paired": windows_paired,
          "coarse_fused_window": coarse_fused_window}
 # default oracle sample per workload when it runs on its own / as a secondary entry
-CPU_SAMPLE = {"fused_window": (512, None), "logits_f32": (512, 512),
+CPU_SAMPLE = {"fused_window": (2047, None), "logits_f32": (512, 512),
               "bf16_topk_stream": (1024, 1024), "fused_batch": (256, 256), "long_trace": (256, 256),
               "golden_f32": (64, 0), "windows_paired": (10_000, 0), "coarse_fused_window": (64, 0)}
 SECONDARY_STEPS = {"long_trace": 3, "fused_batch": 3, "bf16_topk_stream": 5}
