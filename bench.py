@@ -1031,7 +1031,7 @@ FUNCS = {"fused_window": fused_window, "logits_f32": logits_f32,
          "coarse_fused_window": coarse_fused_window}
 # default oracle sample per workload when it runs on its own / as a secondary entry
 CPU_SAMPLE = {"fused_window": (2047, None), "logits_f32": (512, 512),
-              "bf16_topk_stream": (1024, 1024), "fused_batch": (256, 256), "long_trace": (256, 256),
+              "bf16_topk_stream": (2048, 2048), "fused_batch": (768, 768), "long_trace": (768, 768),
               "golden_f32": (64, 0), "windows_paired": (10_000, 0), "coarse_fused_window": (64, 0)}
 SECONDARY_STEPS = {"long_trace": 3, "fused_batch": 3, "bf16_topk_stream": 5}
 
