@@ -243,9 +243,11 @@ class _Chain:
     a time while a launch's closing kernels run beside the next launch's
     dominant kernel -- within a step as across steps.  A launch's workspace
     goes by g % 2 (launch g + 2, on the same stream, runs after launch g's
-    closing kernels).  One chain serves every step of a workload."""
+    closing kernels).  One chain serves every step of a workload.  serial:
+    every launch on the first stream, one after the other."""
 
-    def __init__(self):
+    def __init__(self, serial=False):
+        self.serial = serial
         self.g = 0
         self.prev = None
         self.spare = [(TimingEvent(), TimingEvent()) for _ in range(4)]   # untimed launches
@@ -255,8 +257,9 @@ class _Chain:
         """fn(parity, (start, stop)) issues one call with the event pair
         around its dominant kernel, on the current stream."""
         import torch
-        s = _streams()[self.g % 2]
-        if self.prev is not None and _hip().hipStreamWaitEvent(s.cuda_stream, self.prev, 0) != 0:
+        s = _streams()[0 if self.serial else self.g % 2]
+        if (not self.serial and self.prev is not None and
+                _hip().hipStreamWaitEvent(s.cuda_stream, self.prev, 0) != 0):
             raise RuntimeError("hipStreamWaitEvent failed")
         pair = ev if ev is not None else self.spare[self.g % len(self.spare)]
         with torch.cuda.stream(s):
@@ -268,6 +271,8 @@ class _Chain:
         """The stream of the last launch, after the other stream's work so
         far: what closes a step (its summary) runs there."""
         ss = _streams()
+        if self.serial:
+            return ss[0]
         last, other = ss[(self.g - 1) % 2], ss[self.g % 2]
         t = self.tail[self.g % 2]
         if (_hip().hipEventRecord(t.cuda_event, other.cuda_stream) != 0 or
@@ -276,7 +281,7 @@ class _Chain:
         return last
 
 
-def _timeit(step, steps, warmup, n_ev=1):
+def _timeit(step, steps, warmup, n_ev=1, serial=False):
     """Run warmup untimed steps, then `steps` timed ones; step(i, evs) gets a
     list of n_ev (start, stop) event pairs for the dominant kernel's launches
     (None during warmup).  Step i runs on stream i % 2 and must use buffers
@@ -285,20 +290,22 @@ def _timeit(step, steps, warmup, n_ev=1):
     a time (each event pair brackets one launch) while one step's small
     closing kernels (finalize, top-64 select, tail KLD, summary) overlap the
     next step's dominant kernel, as a scorer fed batch after batch would run
-    them.  Returns (elapsed seconds, mean dominant-kernel ms per launch)."""
+    them.  serial: every step on the first stream, one after the other.
+    Returns (elapsed seconds, mean dominant-kernel ms per launch)."""
     import torch
     evs = [[(TimingEvent(), TimingEvent()) for _ in range(n_ev)] for _ in range(steps)]
     ss = _streams()
     for i in range(warmup):   # one at a time: warmup steps never overlap
-        with torch.cuda.stream(ss[i % 2]):
+        with torch.cuda.stream(ss[0 if serial else i % 2]):
             step(i, None)
         torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        if i > 0 and _hip().hipStreamWaitEvent(ss[i % 2].cuda_stream, evs[i - 1][-1][1].cuda_event,
-                                                0) != 0:
+        if (not serial and i > 0 and
+                _hip().hipStreamWaitEvent(ss[i % 2].cuda_stream, evs[i - 1][-1][1].cuda_event,
+                                          0) != 0):
             raise RuntimeError("hipStreamWaitEvent failed")
-        with torch.cuda.stream(ss[i % 2]):
+        with torch.cuda.stream(ss[0 if serial else i % 2]):
             step(i, evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -725,7 +732,11 @@ def bf16_topk_stream(steps, warmup, cpu_sample):
     tails = [torch.empty(total, dtype=torch.float32, device=dev) for _ in range(2)]
     views = [[{k: x[r0:r0 + nb] for k, x in o.items()} for r0, nb, _, _ in batches] for o in outs]
 
-    chain = _Chain()   # batch calls alternate streams: a batch's closing kernels overlap the next
+    # The batches run back to back on one stream: beside the next batch's pass,
+    # a batch's closing kernels (merge, tail KLD, finalize; ~0.04 ms) had
+    # slowed that pass by more than their own time (0.69 against 0.665 ms per
+    # pass, 5.63 against 5.54-5.58 ms per stream, interleaved on one box).
+    chain = _Chain(serial=True)
 
     def step(i, ev):
         k = i % 2
@@ -741,7 +752,7 @@ def bf16_topk_stream(steps, warmup, cpu_sample):
             kld.kld_summary(o["kl"], o["argmax_ref"], o["argmax_cand"], quantiles=QUANTILES,
                             ws=ws_s[k], out=summs[k])   # no targets in this workload: no NLL
 
-    elapsed, kernel_ms = _timeit(step, steps, warmup, n_ev=len(batches))
+    elapsed, kernel_ms = _timeit(step, steps, warmup, n_ev=len(batches), serial=True)
     summ, out, tail = summs[0], outs[0], tails[0]
     nbytes = 4.0 * bsz * v
     mean_ms = kernel_ms
